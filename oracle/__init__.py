@@ -1,0 +1,17 @@
+"""CPU oracle for the fused attention forward (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import anything from this package.  It shares no code with
+the HIP path: it is the plain definition of the operator, in float64 numpy,
+against which the GPU kernels are checked.
+"""
+from .attention import (attention_head, attn_fwd, attn_fwd_blocksparse, merge_states,
+                        output_stage, scores_stage, softmax_stage, token_mask_block_sparse,
+                        token_mask_dense)
+from .blockmask import canonical_blockmask
+
+__all__ = [
+    "attention_head", "attn_fwd", "attn_fwd_blocksparse", "merge_states", "output_stage",
+    "scores_stage", "softmax_stage", "token_mask_block_sparse", "token_mask_dense",
+    "canonical_blockmask",
+]

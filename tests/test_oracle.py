@@ -1,0 +1,464 @@
+"""Pins for the float64 CPU oracle: worked numbers printed on the pages,
+closed forms, invariants, a library special case and brute force.
+
+Each pin is chosen so that a plausible mistake in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, a double-counted duplicate)
+fails at least one of them; ``test_planted_mistakes_are_caught`` plants such
+mistakes in a copy of the oracle and checks exactly that.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle import attention as A
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _head(q, k, v, scale, allowed):
+    return A.attention_head(q, k, v, scale, allowed)
+
+
+# ---------------------------------------------------------------------------
+# worked numbers from the pages
+# ---------------------------------------------------------------------------
+
+def test_three_logit_merge_worked_example():
+    g = _golden()["three_logit_merge"]
+    logits = g["tile1_logits"] + g["tile2_logits"]
+    values = g["tile1_values"] + g["tile2_values"]
+    n = len(logits)
+    # one query, d = 1: q = 1, k_j = logit_j, scale = 1 gives S_0j = logit_j
+    q = np.ones((n, 1))
+    k = np.array(logits)[:, None]
+    v = np.array(values)[:, None]
+    allowed = np.ones((1, n), dtype=bool)
+    o, lse = A.attention_head(q, k, v, 1.0, allowed, rows=np.array([0]))
+    # closed form of the page's statement: weights e^(s - 1001) of the three logits
+    w = [math.exp(s - 1001.0) for s in logits]
+    o_ref = sum(wi * vi for wi, vi in zip(w, values)) / sum(w)
+    lse_ref = 1001.0 + math.log(sum(w))
+    assert o[0, 0] == pytest.approx(o_ref, rel=1e-15, abs=1e-13)
+    assert lse[0] == pytest.approx(lse_ref, rel=1e-15, abs=1e-12)
+    assert o_ref == pytest.approx(7.501988792539335, rel=1e-14)
+    assert lse_ref == pytest.approx(1001.4076059644444, rel=1e-14)
+    # the first tile alone is the page's intermediate state m = 1000,
+    # l = 1 + e^-1, A = 2 + 4 e^-1
+    a1 = np.array([[True, True, False]])
+    o1, lse1 = A.attention_head(q, k, v, 1.0, a1, rows=np.array([0]))
+    assert lse1[0] == pytest.approx(1000.0 + math.log(1 + math.exp(-1)), abs=1e-12)
+    assert o1[0, 0] == pytest.approx((2 + 4 * math.exp(-1)) / (1 + math.exp(-1)), rel=1e-15)
+    # merging it with the second tile (m = 1001, l = 1, A = 10) by the page's rule
+    a2 = np.array([[False, False, True]])
+    o2, lse2 = A.attention_head(q, k, v, 1.0, a2, rows=np.array([0]))
+    m, l, acc = oracle.merge_states(lse1, np.ones(1), o1, lse2, np.ones(1), o2)
+    assert m[0] == 1001.0
+    assert (acc[0, 0] / l[0]) == pytest.approx(o_ref, rel=1e-14)
+    assert (m[0] + math.log(l[0])) == pytest.approx(lse_ref, abs=1e-12)
+
+
+def test_drop_and_renormalize_worked_example():
+    g = _golden()["drop_and_renormalize"]
+    n = len(g["logits"])
+    q = np.zeros((n, 1))            # every logit is 0
+    k = np.zeros((n, 1))
+    v = np.array(g["values"])[:, None]
+    dense_allowed = np.ones((1, n), dtype=bool)
+    o, _ = A.attention_head(q, k, v, 1.0, dense_allowed, rows=np.array([0]))
+    assert o[0, 0] == pytest.approx(g["dense_output"], rel=1e-15)
+    # the same selection expressed as block-sparse metadata, b = 1
+    rows = [[0, 1], [0, 1, 2], [0, 1, 2]]
+    rp, col = workloads.lists_to_csr(rows)
+    qq, kk, vv = (x[None, None] for x in (q, k, v))
+    o_s, lse_s = oracle.attn_fwd_blocksparse(qq, kk, vv, 1.0, False, 1, rp, col, 1)
+    assert o_s[0, 0, 0, 0] == pytest.approx(g["selected_output"], rel=1e-15)
+    assert lse_s[0, 0, 0] == pytest.approx(math.log(2.0), rel=1e-15)
+    assert o_s[0, 0, 1, 0] == pytest.approx(g["dense_output"], rel=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# closed forms and special cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [1, 8, 64])
+def test_single_key_gives_its_value(d):
+    q, k, v = (_rand((1, 1, 1, d), s) for s in (1, 2, 3))
+    scale = 0.37
+    o, lse = oracle.attn_fwd(q, k, v, scale, causal=False)
+    np.testing.assert_allclose(o[0, 0, 0], v[0, 0, 0], rtol=1e-15, atol=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(scale * float(q[0, 0, 0] @ k[0, 0, 0]), rel=1e-14, abs=1e-15)
+
+
+def test_causal_row_zero_sees_only_itself():
+    q, k, v = (_rand((2, 3, 40, 16), s) for s in (4, 5, 6))
+    o, lse = oracle.attn_fwd(q, k, v, 0.25, causal=True)
+    np.testing.assert_allclose(o[:, :, 0], v[:, :, 0], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lse[:, :, 0], 0.25 * np.einsum("bhd,bhd->bh", q[:, :, 0], k[:, :, 0]),
+                               rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_allowed_values(causal):
+    N, d = 37, 8
+    q = _rand((1, 1, N, d), 7)
+    k = np.broadcast_to(_rand((1, 1, 1, d), 8), (1, 1, N, d)).copy()
+    v = _rand((1, 1, N, d), 9)
+    scale = 0.5
+    o, lse = oracle.attn_fwd(q, k, v, scale, causal=causal)
+    for i in range(N):
+        n_i = i + 1 if causal else N
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, :n_i].mean(axis=0), rtol=1e-12, atol=1e-13)
+        assert lse[0, 0, i] == pytest.approx(scale * float(q[0, 0, i] @ k[0, 0, 0]) + math.log(n_i),
+                                             rel=1e-13, abs=1e-13)
+
+
+def test_identical_keys_block_sparse_counts_duplicates_once():
+    N, d, b = 50, 4, 8            # 7 blocks, the last one partial (2 keys)
+    nqb = -(-N // b)
+    q = _rand((1, 1, N, d), 10)
+    k = np.broadcast_to(_rand((1, 1, 1, d), 11), (1, 1, N, d)).copy()
+    v = _rand((1, 1, N, d), 12)
+    rows = [[6, 0, 0, 3, 3, 3], [], [2, 2], [1, 6], [0, 4, 4, 1], [5], [6, 6, 0]]
+    assert len(rows) == nqb
+    rp, col = workloads.lists_to_csr(rows)
+    o, lse = oracle.attn_fwd_blocksparse(q, k, v, 1.0, False, b, rp, col, 1)
+    for i in range(N):
+        blocks = sorted(set(rows[i // b]))
+        keys = [j for kb in blocks for j in range(kb * b, min(N, kb * b + b))]
+        if not keys:
+            assert np.all(o[0, 0, i] == 0.0) and lse[0, 0, i] == -np.inf
+            continue
+        np.testing.assert_allclose(o[0, 0, i], v[0, 0, keys].mean(axis=0), rtol=1e-12, atol=1e-13)
+        assert lse[0, 0, i] == pytest.approx(float(q[0, 0, i] @ k[0, 0, 0]) + math.log(len(keys)), abs=1e-12)
+
+
+def test_empty_rows_give_zero_and_minus_inf():
+    N, d, b = 24, 4, 8
+    q, k, v = (_rand((1, 2, N, d), s) for s in (13, 14, 15))
+    rp, col = workloads.lists_to_csr([[1], [], [2, 0]])
+    o, lse = oracle.attn_fwd_blocksparse(q, k, v, 0.5, True, b, rp, col, 1)
+    # row block 0 lists only a future block, block 1 lists nothing
+    assert np.all(o[:, :, :16] == 0.0)
+    assert np.all(lse[:, :, :16] == -np.inf)
+    assert np.all(np.isfinite(lse[:, :, 16:]))
+
+
+def test_library_special_case_sdpa_float64():
+    """torch's scaled_dot_product_attention (math path, float64, CPU) with the
+    same boolean mask, on rows that have at least one allowed key."""
+    N, d, b = 48, 16, 8
+    q, k, v = (_rand((2, 2, N, d), s) for s in (16, 17, 18))
+    scale = 0.3
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd(q, k, v, scale, causal)
+        mask = torch.ones(N, N, dtype=torch.bool)
+        if causal:
+            mask = torch.tril(mask)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=scale)
+        np.testing.assert_allclose(o, ref.numpy(), rtol=1e-12, atol=1e-12)
+        s = scale * torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2).contiguous()
+        s = s.masked_fill(~mask, -math.inf)
+        np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-13, atol=1e-12)
+    # block-sparse: the boolean mask built directly from (query block, key block) membership
+    rows = [[0, 5], [1], [2, 2, 0], [3, 1], [], [4, 5, 0]]
+    rp, col = workloads.lists_to_csr(rows)
+    o, lse = oracle.attn_fwd_blocksparse(q, k, v, scale, False, b, rp, col, 1)
+    mask = torch.zeros(N, N, dtype=torch.bool)
+    for qb, r in enumerate(rows):
+        for kb in r:
+            mask[qb * b:(qb + 1) * b, kb * b:(kb + 1) * b] = True
+    live = mask.any(dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=mask, scale=scale)
+    np.testing.assert_allclose(o[:, :, live.numpy()], ref.numpy()[:, :, live.numpy()], rtol=1e-12, atol=1e-12)
+
+
+def test_scalar_brute_force_tiny():
+    """Pure-Python triple loop over (i, j, c) on a tiny ragged case."""
+    N, d, b = 7, 3, 3
+    q, k, v = (_rand((1, 1, N, d), s) for s in (19, 20, 21))
+    rows = [[2, 0], [1, 1], [0, 2]]
+    rp, col = workloads.lists_to_csr(rows)
+    scale = 0.8
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_blocksparse(q, k, v, scale, causal, b, rp, col, 1)
+        for i in range(N):
+            keys = [j for j in range(N) if (j // b) in rows[i // b] and (not causal or j <= i)]
+            s = [scale * sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(d)) for j in keys]
+            if not s:
+                assert lse[0, 0, i] == -math.inf and all(o[0, 0, i] == 0)
+                continue
+            m = max(s)
+            z = sum(math.exp(x - m) for x in s)
+            assert lse[0, 0, i] == pytest.approx(m + math.log(z), abs=1e-13)
+            for c in range(d):
+                ref = sum(math.exp(x - m) * v[0, 0, j, c] for x, j in zip(s, keys)) / z
+                assert o[0, 0, i, c] == pytest.approx(ref, abs=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+def test_key_permutation_invariance():
+    q, k, v = (_rand((1, 2, 33, 8), s) for s in (22, 23, 24))
+    perm = np.random.default_rng(25).permutation(33)
+    o1, l1 = oracle.attn_fwd(q, k, v, 0.4, False)
+    o2, l2 = oracle.attn_fwd(q, k[:, :, perm], v[:, :, perm], 0.4, False)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,b", [(64, 16), (53, 8)])
+def test_all_active_block_mask_equals_dense(causal, N, b):
+    q, k, v = (_rand((1, 3, N, 8), s) for s in (26, 27, 28))
+    nqb = -(-N // b)
+    rows = [list(range(nqb))[::-1] for _ in range(nqb)]   # reversed order: unsorted input
+    rp, col = workloads.lists_to_csr(rows)
+    o_d, l_d = oracle.attn_fwd(q, k, v, 0.5, causal)
+    o_s, l_s = oracle.attn_fwd_blocksparse(q, k, v, 0.5, causal, b, rp, col, 1)
+    np.testing.assert_array_equal(o_d, o_s)
+    np.testing.assert_array_equal(l_d, l_s)
+
+
+def test_two_block_merge_equals_full_softmax():
+    N, d = 40, 8
+    q, k, v = (_rand((N, d), s) for s in (29, 30, 31))
+    rows = np.arange(N)
+    split = np.zeros(N, dtype=bool)
+    split[np.random.default_rng(32).permutation(N)[:17]] = True     # I: 17 keys, J: the rest
+    full = np.ones((N, N), dtype=bool)
+    o, lse = A.attention_head(q, k, v, 0.6, full, rows)
+    oi, li = A.attention_head(q, k, v, 0.6, np.broadcast_to(split, (N, N)), rows)
+    oj, lj = A.attention_head(q, k, v, 0.6, np.broadcast_to(~split, (N, N)), rows)
+    m, l, acc = oracle.merge_states(li, np.ones(N), oi, lj, np.ones(N), oj)
+    np.testing.assert_allclose(acc / l[:, None], o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(m + np.log(l), lse, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(np.logaddexp(li, lj), lse, rtol=1e-13, atol=1e-13)
+    # order does not matter: J then I
+    m2, l2, acc2 = oracle.merge_states(lj, np.ones(N), oj, li, np.ones(N), oi)
+    np.testing.assert_allclose(acc2 / l2[:, None], o, rtol=1e-12, atol=1e-13)
+
+
+def test_row_identities():
+    """sum_j exp(S_ij - LSE_i) = 1 on allowed pairs, and P = exp(S - LSE)."""
+    N, d = 30, 6
+    q, k = _rand((N, d), 33), _rand((N, d), 34)
+    allowed = token = A.token_mask_dense(N, True, np.arange(N))
+    s = A.scores_stage(q, k, 0.9, allowed)
+    p, lse = A.softmax_stage(s)
+    np.testing.assert_allclose(np.exp(s - lse[:, None]).sum(axis=1), np.ones(N), rtol=1e-14)
+    np.testing.assert_allclose(p, np.where(token, np.exp(s - lse[:, None]), 0.0), rtol=1e-13, atol=1e-16)
+    assert np.all(p[~token] == 0.0)
+
+
+def test_sparse_dense_decomposition_identity():
+    """o = lambda o_E + (1 - lambda) o_U with lambda = Z_E / Z_A: links the
+    sparse (selected set E) and dense outputs; the error of drop-and-renormalize
+    is (1 - lambda)(o_E - o_U)."""
+    N, d, b = 48, 8, 8
+    nqb = N // b
+    q, k, v = (_rand((1, 1, N, d), s) for s in (35, 36, 37))
+    rng = workloads.SplitMix64(38)
+    e_rows = [sorted({rng.below(nqb) for _ in range(3)}) for _ in range(nqb)]
+    u_rows = [[kb for kb in range(nqb) if kb not in r] for r in e_rows]
+    o_a, l_a = oracle.attn_fwd(q, k, v, 0.7, False)
+    rp, col = workloads.lists_to_csr(e_rows)
+    o_e, l_e = oracle.attn_fwd_blocksparse(q, k, v, 0.7, False, b, rp, col, 1)
+    rp, col = workloads.lists_to_csr(u_rows)
+    o_u, l_u = oracle.attn_fwd_blocksparse(q, k, v, 0.7, False, b, rp, col, 1)
+    lam = np.exp(l_e - l_a)[..., None]
+    np.testing.assert_allclose(lam * o_e + (1 - lam) * o_u, o_a, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(o_e - o_a, (1 - lam) * (o_e - o_u), rtol=1e-11, atol=1e-13)
+
+
+def test_sampled_rows_match_full_rows():
+    q, k, v = (_rand((1, 2, 300, 8), s) for s in (39, 40, 41))
+    rows = workloads.sample_rows(300, 20, 42)
+    o, lse = oracle.attn_fwd(q, k, v, 0.3, True)
+    os_, ls_ = oracle.attn_fwd(q, k, v, 0.3, True, rows=rows, row_chunk=7)
+    for bh in range(2):
+        np.testing.assert_allclose(os_[bh], o[0, bh, rows], rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(ls_[bh], lse[0, bh, rows], rtol=1e-14, atol=1e-15)
+
+
+def test_out_of_range_block_entry_raises():
+    q = k = v = np.zeros((1, 1, 16, 2))
+    rp, col = workloads.lists_to_csr([[0], [2]])
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_blocksparse(q, k, v, 1.0, False, 8, rp, col, 1)
+    with pytest.raises(ValueError):
+        oracle.canonical_blockmask(rp, col, 1, 16, 8, False)
+
+
+# ---------------------------------------------------------------------------
+# canonical metadata: brute force from logical token pairs
+# ---------------------------------------------------------------------------
+
+def _brute_canonical(rows, N, b, causal):
+    """Canonical tiles characterised from the logical mask alone: a tile is
+    executed iff it holds at least one allowed pair; it needs the triangular
+    mask iff it holds a listed pair with j > i under causal; it is partial iff
+    it holds a key index >= N."""
+    nqb = -(-N // b)
+    out = []
+    for qb in range(nqb):
+        listed = set(rows[qb])
+        ents = []
+        for kb in range(nqb):
+            pairs = [(i, j) for i in range(qb * b, min(N, qb * b + b)) for j in range(kb * b, kb * b + b)]
+            allowed = [(i, j) for i, j in pairs if kb in listed and j < N and (not causal or j <= i)]
+            if not allowed:
+                continue
+            f = 0
+            padded = [(i, j) for i in range(qb * b, qb * b + b) for j in range(kb * b, kb * b + b)]
+            if causal and any(j > i for i, j in padded):
+                f |= 1
+            if any(j >= N for _, j in pairs):
+                f |= 2
+            ents.append((kb, f))
+        out.append(ents)
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_canonical_blockmask_brute_force(causal):
+    rng = workloads.SplitMix64(43 + causal)
+    for trial in range(40):
+        b = [1, 2, 4, 8][rng.below(4)]
+        N = 1 + rng.below(40)
+        nqb = -(-N // b)
+        meta_heads = 1 + rng.below(3)
+        rows = workloads.random_lists(meta_heads * nqb, nqb, rng, max_len=6, empty_prob_per_mille=150)
+        rp, col = workloads.lists_to_csr(rows)
+        c = oracle.canonical_blockmask(rp, col, meta_heads, N, b, causal)
+        pos = 0
+        for h in range(meta_heads):
+            brute = _brute_canonical(rows[h * nqb:(h + 1) * nqb], N, b, causal)
+            cnt_allowed = 0
+            for qb, ents in enumerate(brute):
+                lo, hi = c["row_ptr"][h * nqb + qb], c["row_ptr"][h * nqb + qb + 1]
+                assert lo == pos and hi - lo == len(ents)
+                assert list(c["col"][lo:hi]) == [kb for kb, _ in ents]
+                assert list(c["flags"][lo:hi]) == [f for _, f in ents]
+                pos = hi
+                for i in range(qb * b, min(N, qb * b + b)):
+                    cnt_allowed += sum(1 for j in range(N)
+                                       if (j // b) in set(rows[h * nqb + qb]) and (not causal or j <= i))
+            assert c["allowed_pairs"][h] == cnt_allowed
+            assert c["executed_tile_pairs"][h] == sum(len(e) for e in brute)
+        assert c["nnz"] == len(c["col"]) == pos
+
+
+@pytest.mark.parametrize("N,b", [(256, 64), (300, 64), (16300, 128)])
+def test_allowed_pair_closed_forms(N, b):
+    nqb = -(-N // b)
+    full = [list(range(nqb)) for _ in range(nqb)]
+    rp, col = workloads.lists_to_csr(full)
+    c = oracle.canonical_blockmask(rp, col, 1, N, b, True)
+    assert c["allowed_pairs"][0] == N * (N + 1) // 2
+    assert c["executed_tile_pairs"][0] == nqb * (nqb + 1) // 2
+    c = oracle.canonical_blockmask(rp, col, 1, N, b, False)
+    assert c["allowed_pairs"][0] == N * N
+    assert c["executed_tile_pairs"][0] == nqb * nqb
+
+
+def test_local_global_random_pattern_properties():
+    cfg = workloads.CONFIGS["c4"]
+    rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
+    nqb = -(-cfg.N // cfg.block)
+    assert len(rows) == nqb == 128
+    empties = [qb for qb, r in enumerate(rows) if not r]
+    assert len(empties) == 4 and nqb - 1 not in empties
+    assert any(len(r) != len(set(r)) for r in rows)              # duplicates present
+    assert any(r != sorted(r) for r in rows)                     # unordered present
+    # the realised pattern is reproducible from the seed
+    assert rows == workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
+    rp, col = workloads.lists_to_csr(rows)
+    c = oracle.canonical_blockmask(rp, col, 1, cfg.N, cfg.block, True)
+    # closed form of the pair count: per canonical tile, rows x valid keys,
+    # the diagonal tile a triangle, the partial last block 16300 - 127*128 = 44 wide
+    tail = cfg.N - (nqb - 1) * cfg.block
+    total = 0
+    for qb in range(nqb):
+        nrows = cfg.block if qb < nqb - 1 else tail
+        for kb in c["col"][c["row_ptr"][qb]:c["row_ptr"][qb + 1]]:
+            if kb == qb:
+                total += nrows * (nrows + 1) // 2
+            else:
+                total += nrows * cfg.block
+    assert c["allowed_pairs"][0] == total
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin above
+# ---------------------------------------------------------------------------
+
+def _mutants():
+    def no_scale(q_rows, k, scale, allowed):
+        s = q_rows @ k.T
+        s[~allowed] = -np.inf
+        return s
+
+    def transposed(q_rows, k, scale, allowed):
+        s = scale * (k[: q_rows.shape[0]] @ q_rows.T) if q_rows.shape[0] == k.shape[0] else scale * (q_rows @ k.T)
+        s[~allowed] = -np.inf
+        return s
+
+    def lse_without_max(s):
+        p, lse = A.softmax_stage.__wrapped__(s) if hasattr(A.softmax_stage, "__wrapped__") else ORIG_SOFTMAX(s)
+        m = np.max(s, axis=1)
+        return p, np.where(np.isfinite(m), lse - m, lse)
+
+    def strict_causal(N, causal, rows):
+        j = np.arange(N)
+        allowed = np.ones((len(rows), N), dtype=bool)
+        if causal:
+            allowed &= j[None, :] < np.asarray(rows)[:, None]
+        return allowed
+
+    return {"no_scale": ("scores_stage", no_scale), "transposed": ("scores_stage", transposed),
+            "lse_without_max": ("softmax_stage", lse_without_max),
+            "strict_causal": ("token_mask_dense", strict_causal)}
+
+
+ORIG_SOFTMAX = A.softmax_stage
+
+PIN_TESTS = [test_three_logit_merge_worked_example, test_single_key_gives_its_value,
+             test_causal_row_zero_sees_only_itself, test_identical_keys_give_mean_of_allowed_values,
+             test_library_special_case_sdpa_float64, test_scalar_brute_force_tiny]
+
+
+@pytest.mark.parametrize("name", sorted(_mutants()))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    attr, fn = _mutants()[name]
+    monkeypatch.setattr(A, attr, fn)
+    caught = 0
+    for t in PIN_TESTS:
+        try:
+            if t is test_single_key_gives_its_value:
+                t(8)
+            elif t is test_identical_keys_give_mean_of_allowed_values:
+                t(True)
+            else:
+                t()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"planted mistake {name} passed every pin"
