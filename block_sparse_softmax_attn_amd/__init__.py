@@ -1,0 +1,158 @@
+"""Fused softmax-attention forward (dense, causal, block-sparse) for AMD MI355X.
+
+Thin Python layer over the C ABI of ``libbsattn.so``: it checks tensors,
+passes raw device pointers and the current HIP stream, and returns the
+outputs.  PyTorch only provides device memory and streams; the arithmetic runs
+in the gfx950 kernels.
+
+    o, lse = attn_fwd(q, k, v, scale=None, causal=False)
+    meta   = blockmask_build(raw_row_ptr, raw_col, meta_heads, N, block, causal)
+    o, lse = attn_fwd_blocksparse(q, k, v, meta, causal=True)
+
+Operator ("Exact Blocks, Rings, and Sparsity", sections 1, 2 and 5;
+"block-sparse attention patterns"): O = softmax(scale * Q K^T) V over the
+allowed pairs, LSE = log-sum-exp of the scaled logits (natural log); rows with
+no allowed key give O = 0 and LSE = -inf.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN_FLAG_PARTIAL, ATTN_OK,
+                   AttnError, LIB_PATH, check, lib, status_string)
+
+__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "BlockMask", "AttnError", "LIB_PATH",
+           "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: bfloat16 or float32")
+
+
+def _check_qkv(q, k, v):
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or len({q.device, k.device, v.device}) != 1:
+        raise ValueError("q, k, v must live on one GPU")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+
+
+def _outputs(q, out, lse):
+    import torch
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), device=q.device, dtype=torch.float32)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must match q in shape, dtype, device and be contiguous")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    return out, lse
+
+
+def _stream(dev):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, lse=None):
+    """Dense or causal attention forward; returns (O in q's dtype, LSE fp32 [B,H,N])."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)), _stream(q.device))
+    check("attn_fwd", st)
+    return out, lse
+
+
+@dataclasses.dataclass
+class BlockMask:
+    """Canonical block-sparse metadata (host arrays) and its pair counts."""
+    N: int
+    block: int
+    causal: bool
+    meta_heads: int
+    row_ptr: np.ndarray              # int32 [meta_heads * nqb + 1]
+    col: np.ndarray                  # int32 [nnz]
+    flags: np.ndarray                # uint8 [nnz]
+    allowed_pairs: np.ndarray        # int64 [meta_heads]
+    executed_tile_pairs: np.ndarray  # int64 [meta_heads]
+    _device: dict = dataclasses.field(default_factory=dict, repr=False)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.col.size)
+
+    def to_device(self, device):
+        """Device copies (row_ptr, col, flags), cached per device."""
+        import torch
+        key = str(device)
+        if key not in self._device:
+            col = self.col if self.col.size else np.zeros(1, np.int32)
+            flags = self.flags if self.flags.size else np.zeros(1, np.uint8)
+            self._device[key] = tuple(torch.from_numpy(np.ascontiguousarray(x)).to(device)
+                                      for x in (self.row_ptr, col, flags))
+        return self._device[key]
+
+
+def blockmask_build(raw_row_ptr, raw_col, meta_heads: int, N: int, block: int, causal: bool) -> BlockMask:
+    """Canonicalise raw per-query-block key-block lists (host, in the library)."""
+    rp = np.ascontiguousarray(np.asarray(raw_row_ptr, dtype=np.int32))
+    rc = np.ascontiguousarray(np.asarray(raw_col, dtype=np.int32))
+    nqb = -(-int(N) // int(block)) if block > 0 else 0
+    if rp.shape != (int(meta_heads) * nqb + 1,):
+        raise ValueError("raw_row_ptr must hold meta_heads * ceil(N / block) + 1 offsets")
+    cap = max(int(rc.size), 1)
+    row_ptr = np.zeros(rp.size, dtype=np.int32)
+    col = np.zeros(cap, dtype=np.int32)
+    flags = np.zeros(cap, dtype=np.uint8)
+    nnz = np.zeros(1, dtype=np.int64)
+    allowed = np.zeros(max(int(meta_heads), 1), dtype=np.int64)
+    executed = np.zeros(max(int(meta_heads), 1), dtype=np.int64)
+    ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.attn_blockmask_build(ptr(rp), ptr(rc) if rc.size else None, int(meta_heads), int(N), int(block),
+                                  int(bool(causal)), ptr(row_ptr), ptr(col), ptr(flags), cap, ptr(nnz),
+                                  ptr(allowed), ptr(executed))
+    check("attn_blockmask_build", st)
+    n = int(nnz[0])
+    return BlockMask(int(N), int(block), bool(causal), int(meta_heads), row_ptr, col[:n].copy(),
+                     flags[:n].copy(), allowed[:meta_heads].copy(), executed[:meta_heads].copy())
+
+
+def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None, causal: Optional[bool] = None,
+                         out=None, lse=None):
+    """Block-sparse attention forward, renormalised over the allowed pairs."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    if mask.N != N:
+        raise ValueError(f"mask was built for N={mask.N}, inputs have N={N}")
+    causal = mask.causal if causal is None else bool(causal)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    row_ptr, col, flags = mask.to_device(q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                      B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(causal), mask.block,
+                                      row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz,
+                                      mask.meta_heads, _stream(q.device))
+    check("attn_fwd_blocksparse", st)
+    return out, lse

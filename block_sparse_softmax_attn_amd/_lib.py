@@ -1,0 +1,60 @@
+"""ctypes binding of ``libbsattn.so`` (the C ABI in ``include/bsattn.h``).
+
+Argument marshalling only: every step of the attention forward runs in the HIP
+kernels behind the C ABI.  Importing this module fails loudly when the library
+has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
+
+ATTN_OK = 0
+ATTN_EINVAL = -1
+ATTN_EUNSUPPORTED = -2
+ATTN_ECAPACITY = -3
+ATTN_EHIP = -4
+ATTN_F32 = 0
+ATTN_BF16 = 1
+ATTN_FLAG_DIAGONAL = 1
+ATTN_FLAG_PARTIAL = 2
+
+EXPORTED = ("attn_status_string", "attn_fwd", "attn_blockmask_build", "attn_fwd_blocksparse")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status} ({text})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m block_sparse_softmax_attn_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.attn_blockmask_build.restype = i32
+    lib.attn_blockmask_build.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
+    lib.attn_fwd_blocksparse.restype = i32
+    lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
+                                         vp, vp, vp, i64, i64, vp]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.attn_status_string(int(status)).decode()
+
+
+def check(fn: str, status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(fn, status, status_string(status))

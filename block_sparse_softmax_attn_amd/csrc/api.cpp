@@ -1,0 +1,96 @@
+// C ABI of the attention forward: argument validation and kernel dispatch.
+// Every check happens before any launch; nothing here allocates device memory.
+#include <cmath>
+#include <cstdint>
+
+#include "bsattn.h"
+#include "fwd_common.h"
+
+namespace {
+
+constexpr int64_t kMaxN = int64_t(1) << 30;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                 int64_t N, int64_t d, int dtype, float scale, int causal) {
+    if (!q || !k || !v || !o || !lse) return ATTN_EINVAL;
+    if (B < 1 || H < 1 || N < 1 || d < 1) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+    if (N > kMaxN || H > INT32_MAX) return ATTN_EINVAL;
+    // element count and grid size must fit the kernels' 64-bit offsets and 32-bit grid
+    if (B > (int64_t(1) << 62) / H) return ATTN_EINVAL;
+    const int64_t bh = B * H;
+    if (bh > (int64_t(1) << 62) / (N * d)) return ATTN_EINVAL;
+    const int64_t tiles = ((N + 63) / 64) * bh;
+    if (tiles > INT32_MAX) return ATTN_EINVAL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+bsattn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                          int64_t H, int64_t N, int64_t d, float scale, int causal) {
+    bsattn::FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.BH = B * H;
+    a.H = static_cast<int>(H);
+    a.N = static_cast<int>(N);
+    a.d = static_cast<int>(d);
+    a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a.causal = causal;
+    return a;
+}
+
+int run(const bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, hipStream_t stream) {
+    hipError_t e = dtype == ATTN_BF16 ? bsattn::launch_fwd_bf16(a, mode, stream)
+                                      : bsattn::launch_fwd_f32(a, mode, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+extern "C" const char* attn_status_string(int status) {
+    switch (status) {
+        case ATTN_OK: return "ok";
+        case ATTN_EINVAL: return "invalid argument";
+        case ATTN_EUNSUPPORTED: return "unsupported configuration";
+        case ATTN_ECAPACITY: return "output capacity too small";
+        case ATTN_EHIP: return "HIP runtime error at launch";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                        int64_t N, int64_t d, int dtype, float scale, int causal, hipStream_t stream) {
+    const int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    const bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, stream);
+}
+
+extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                    int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
+                                    int64_t block, const int32_t* row_ptr, const int32_t* col,
+                                    const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
+    const int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
+    if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
+    if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
+    if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
+    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    a.row_ptr = row_ptr;
+    a.col = col;
+    a.flags = flags;
+    a.nnz = nnz;
+    a.meta_heads = static_cast<int>(meta_heads);
+    a.block = static_cast<int>(block);
+    return run(a, dtype, bsattn::Mode::kSparse, stream);
+}

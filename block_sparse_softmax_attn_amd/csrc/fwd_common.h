@@ -1,0 +1,48 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 forward kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsattn {
+
+// Everything a forward launch needs; built and validated by the host layer.
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    int64_t BH;          // B * H
+    int H;
+    int N;
+    int d;
+    float scale_log2;    // scale * log2(e): logits are handled in base-2 units
+    int causal;
+    // block-sparse schedule (sparse launches only)
+    const int32_t* row_ptr;
+    const int32_t* col;
+    const uint8_t* flags;
+    int64_t nnz;
+    int meta_heads;
+    int block;
+};
+
+enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2 };
+
+// Launchers: return hipSuccess or the launch error.
+hipError_t launch_fwd_bf16(const FwdArgs& a, Mode mode, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, Mode mode, hipStream_t stream);
+
+// Workgroup index -> (tile order index) so that consecutive tile indices land
+// on the same XCD: the dispatcher hands workgroup i to XCD i % 8, so XCD x
+// receives the contiguous range [x*T/8, (x+1)*T/8) of the tile order and the
+// query tiles of one head share that XCD's L2 while they stream its K/V.
+__device__ __forceinline__ int64_t xcd_tile_order(int64_t wg, int64_t total) {
+    constexpr int kXcds = 8;
+    const int64_t per = total / kXcds;
+    if (wg >= per * kXcds) return wg;  // ragged tail keeps its own index
+    return (wg % kXcds) * per + wg / kXcds;
+}
+
+}  // namespace bsattn

@@ -1,0 +1,147 @@
+/*
+ * bsattn.h - C ABI of the fused softmax-attention forward for AMD MI355X (gfx950).
+ *
+ * The library computes, for every (batch b, head h) and query row i,
+ *
+ *     O_i   = sum_j softmax_j(scale * q_i . k_j) v_j      over the allowed keys j
+ *     LSE_i = ln sum_j exp(scale * q_i . k_j)             (natural log, fp32)
+ *
+ * without writing the N x N score or probability matrix to HBM: one
+ * workgroup owns a query tile, streams key/value tiles past it and folds each
+ * score tile into a running online-softmax state (max m, denominator l,
+ * unnormalised accumulator A).  Sources of the operator:
+ *   - "Exact Blocks, Rings, and Sparsity", section 1 (S = QK^T, P = softmax,
+ *     O = PV), section 2 (online softmax state, merge invariant, saved LSE)
+ *     and section 5 (block-sparse schedule over the active key-block set C_a);
+ *   - "FlashAttention: Fast and Memory Efficient Exact Attention with IO
+ *     Awareness" (notes), sections 5.1-5.2 (online softmax statistics,
+ *     forward tiling) and 5.6 (block-sparse FlashAttention);
+ *   - "block-sparse attention patterns", "Count active blocks and acknowledge
+ *     the changed operator" (renormalisation over the sparse domain,
+ *     triangular mask inside diagonal blocks, partial blocks, duplicates).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense and contiguous: Q, K, V, O are [B, H, N, d] with row
+ *     stride d; LSE is [B, H, N] fp32.  Q, K, V, O have the same dtype.
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *     aligned to 16 bytes.  The caller owns every buffer; the library never
+ *     allocates device memory and keeps no pointer after a call returns.
+ *   - Calls are asynchronous on `stream` (0 = the null stream): the inputs
+ *     must stay alive and unmodified until the stream has run the work.
+ *   - Allowed pairs: causal keeps j <= i.  A query row with no allowed key
+ *     gets O = 0 and LSE = -inf.
+ *   - Status codes: every function returns ATTN_OK or a negative code, and
+ *     validates all arguments before any launch (nothing is launched on
+ *     error).  No C++ exception crosses this interface.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    ATTN_OK = 0,
+    ATTN_EINVAL = -1,       /* null pointer, bad size, bad flag, misaligned pointer, malformed metadata */
+    ATTN_EUNSUPPORTED = -2, /* valid request outside what the kernels implement (d, dtype, block size) */
+    ATTN_ECAPACITY = -3,    /* caller-provided output buffer too small */
+    ATTN_EHIP = -4          /* the HIP runtime reported an error at launch */
+};
+
+enum { ATTN_F32 = 0, ATTN_BF16 = 1 };
+
+/* Bits of the per-entry flags of canonical block-sparse metadata. */
+enum {
+    ATTN_FLAG_DIAGONAL = 1, /* causal and the tile straddles the diagonal: triangular element mask */
+    ATTN_FLAG_PARTIAL = 2   /* key block is the last one and N % block != 0: keys j >= N are masked */
+};
+
+/* Static text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/*
+ * attn_fwd - dense or causal attention forward.
+ *   q, k, v : device, [B,H,N,d] of `dtype` (ATTN_BF16 or ATTN_F32), read only.
+ *   o       : device, [B,H,N,d] of `dtype`, written (O in the input dtype).
+ *   lse     : device, [B,H,N] fp32, written; natural-log log-sum-exp of the
+ *             scaled logits over the allowed keys.
+ *   B, H, N : >= 1; d in {64, 128}.
+ *   scale   : finite and > 0 (e.g. 1/sqrt(d)); logits are scale * q.k.
+ *   causal  : 0 or 1 (1 keeps j <= i; tiles wholly in the future are skipped,
+ *             the diagonal tile gets the triangular element mask).
+ * Source: "Exact Blocks, Rings, and Sparsity", section 2, forward kernel
+ * ("What the forward kernel keeps on chip"): the host wrapper takes q, k, v
+ * and a causal flag and returns O and the per-row LSE.
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
+             hipStream_t stream);
+
+/*
+ * attn_blockmask_build - HOST-side canonicaliser of block-sparse metadata.
+ *   raw_row_ptr : host, int32 [meta_heads * nqb + 1], nqb = ceil(N / block);
+ *                 CSR offsets into raw_col: starts at 0, non-decreasing.
+ *   raw_col     : host, int32 [raw_row_ptr[last]]; key-block indices per
+ *                 query block, any order, repeats allowed, rows may be empty,
+ *                 and under causal may name future blocks.  An index outside
+ *                 [0, nqb) is an error (ATTN_EINVAL).
+ *   meta_heads  : number of independent patterns (1: shared by every (b,h);
+ *                 H: one per head, the same for every batch).
+ *   N, block    : sequence length >= 1 and block size b >= 1.
+ *   causal      : 0 or 1.
+ * Outputs (host buffers owned by the caller):
+ *   row_ptr [meta_heads*nqb + 1], col [capacity], flags [capacity]: canonical
+ *     CSR: each row strictly increasing and unique; future blocks dropped when
+ *     causal; flags per entry use ATTN_FLAG_*.
+ *   capacity          : entries available in col/flags; raw nnz always suffices.
+ *   nnz               : entries written (or needed, with ATTN_ECAPACITY).
+ *   allowed_pairs     : [meta_heads] logical (i, j) pairs with i, j < N allowed
+ *                       by each pattern, per (b, h).
+ *   executed_tile_pairs : [meta_heads] block x block tiles executed per (b, h).
+ * Source: "Exact Blocks, Rings, and Sparsity", section 5, "Why the sparse
+ * unit is usually a block" (active set C_a per query tile); "block-sparse
+ * attention patterns" (duplicates count once, partial blocks, report logical
+ * allowed pairs next to executed tile work).
+ * Errors: ATTN_EINVAL, ATTN_ECAPACITY (row_ptr, nnz and the counts are still
+ * written; col/flags are not).
+ */
+int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* raw_col,
+                         int64_t meta_heads, int64_t N, int64_t block, int causal,
+                         int32_t* row_ptr, int32_t* col, uint8_t* flags, int64_t capacity,
+                         int64_t* nnz, int64_t* allowed_pairs, int64_t* executed_tile_pairs);
+
+/*
+ * attn_fwd_blocksparse - block-sparse attention forward, renormalised over
+ * the allowed pairs (drop-and-renormalize).
+ *   q, k, v, o, lse, B, H, N, d, dtype, scale, causal: as for attn_fwd.
+ *   block      : b in {64, 128}: query and key block size of the metadata.
+ *   row_ptr    : DEVICE int32 [meta_heads * nqb + 1], canonical CSR offsets.
+ *   col, flags : DEVICE int32 / uint8 [nnz]: canonical entries and their
+ *                ATTN_FLAG_* bits, as written by attn_blockmask_build (sorted,
+ *                unique: a duplicated entry would be counted twice).
+ *   nnz        : number of entries in col/flags; offsets are clamped to it and
+ *                entries outside [0, nqb) are skipped, so malformed metadata
+ *                cannot make the kernel read out of bounds.
+ *   meta_heads : 1 (one pattern for every (b,h)) or H (pattern h for head h).
+ * Source: "Exact Blocks, Rings, and Sparsity", section 5 (the outer loop runs
+ * over b in C_a; skipped tiles skip their loads and both products) and
+ * section 6 (drop-and-renormalize); "block-sparse attention patterns"
+ * (triangular element mask inside diagonal blocks, empty rows).
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ */
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
+                         int causal, int64_t block,
+                         const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
+                         int64_t nnz, int64_t meta_heads, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

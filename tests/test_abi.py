@@ -1,0 +1,140 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the
+header declares, validates arguments before any launch, and its host-side
+metadata builder matches the oracle's canonicaliser bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+
+@pytest.fixture(scope="module")
+def m():
+    import block_sparse_softmax_attn_amd as m
+    return m
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(m):
+    from block_sparse_softmax_attn_amd import _lib
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.EXPORTED)
+    raw = ctypes.CDLL(m.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), f"{name} not exported"
+
+
+def test_status_strings(m):
+    from block_sparse_softmax_attn_amd import _lib
+    for code in (0, -1, -2, -3, -4):
+        assert m.status_string(code) and m.status_string(code) != "unknown status"
+    assert m.status_string(12345) == "unknown status"
+
+
+FAKE = 1 << 20   # 16-aligned, never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(q=0), -1),
+    (dict(B=0), -1), (dict(H=-1), -1), (dict(N=0), -1),
+    (dict(d=96), -2), (dict(d=256), -2), (dict(dtype=7), -2),
+    (dict(scale=0.0), -1), (dict(scale=-1.0), -1), (dict(scale=float("nan")), -1), (dict(scale=float("inf")), -1),
+    (dict(causal=2), -1),
+    (dict(q=FAKE + 2), -1),
+    (dict(N=1 << 31), -1),
+])
+def test_attn_fwd_rejects_bad_arguments(m, args, expect):
+    from block_sparse_softmax_attn_amd._lib import lib
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, dtype=1, scale=0.125, causal=0)
+    a.update(args)
+    st = lib.attn_fwd(a["q"] or None, a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["dtype"], ctypes.c_float(a["scale"]), a["causal"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(block=32), -2), (dict(block=0), -2),
+    (dict(meta_heads=3), -1), (dict(row_ptr=0), -1), (dict(nnz=-1), -1), (dict(nnz=4, col=0), -1),
+    (dict(d=80), -2),
+])
+def test_attn_fwd_blocksparse_rejects_bad_arguments(m, args, expect):
+    from block_sparse_softmax_attn_amd._lib import lib
+    a = dict(d=64, block=128, row_ptr=FAKE, col=FAKE, flags=FAKE, nnz=4, meta_heads=1)
+    a.update(args)
+    st = lib.attn_fwd_blocksparse(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, a["d"], 1, ctypes.c_float(0.1), 1,
+                                  a["block"], a["row_ptr"] or None, a["col"] or None, a["flags"], a["nnz"],
+                                  a["meta_heads"], None)
+    assert st == expect
+
+
+def _check_builder(m, rows, meta_heads, N, block, causal):
+    rp, col = workloads.lists_to_csr(rows)
+    got = m.blockmask_build(rp, col, meta_heads, N, block, causal)
+    ref = oracle.canonical_blockmask(rp, col, meta_heads, N, block, causal)
+    assert np.array_equal(got.row_ptr, ref["row_ptr"]) and got.row_ptr.dtype == np.int32
+    assert np.array_equal(got.col, ref["col"]) and got.col.dtype == np.int32
+    assert np.array_equal(got.flags, ref["flags"]) and got.flags.dtype == np.uint8
+    assert got.nnz == int(ref["nnz"])
+    assert np.array_equal(got.allowed_pairs, ref["allowed_pairs"])
+    assert np.array_equal(got.executed_tile_pairs, ref["executed_tile_pairs"])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_builder_matches_oracle_random(m, causal):
+    rng = workloads.SplitMix64(101 + causal)
+    for _ in range(60):
+        block = [1, 3, 8, 64, 128][rng.below(5)]
+        N = 1 + rng.below(1500)
+        nqb = -(-N // block)
+        if nqb > 200:
+            continue
+        mh = 1 + rng.below(3)
+        rows = workloads.random_lists(mh * nqb, nqb, rng, max_len=min(3 * nqb, 40), empty_prob_per_mille=120)
+        _check_builder(m, rows, mh, N, block, causal)
+
+
+def test_builder_matches_oracle_on_sparse_workload(m):
+    cfg = workloads.CONFIGS["c4"]
+    rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
+    _check_builder(m, rows, 1, cfg.N, cfg.block, True)
+    _check_builder(m, rows, 1, cfg.N, cfg.block, False)
+
+
+def test_builder_errors(m):
+    from block_sparse_softmax_attn_amd import AttnError
+    rp, col = workloads.lists_to_csr([[0], [3]])
+    with pytest.raises(AttnError) as e:
+        m.blockmask_build(rp, col, 1, 16, 8, False)          # block 3 out of range for 2 blocks
+    assert e.value.status == -1
+    rp, col = workloads.lists_to_csr([[0], [-1]])
+    with pytest.raises(AttnError):
+        m.blockmask_build(rp, col, 1, 16, 8, False)
+    bad_rp = np.array([0, 2, 1], dtype=np.int32)              # decreasing offsets
+    with pytest.raises(AttnError):
+        m.blockmask_build(bad_rp, np.array([0, 1], np.int32), 1, 16, 8, False)
+
+
+def test_builder_capacity_error(m):
+    from block_sparse_softmax_attn_amd._lib import lib, ATTN_ECAPACITY
+    rp, col = workloads.lists_to_csr([[1, 0], [1, 1, 0]])
+    out_rp = np.zeros(3, np.int32)
+    out_col = np.zeros(2, np.int32)
+    out_fl = np.zeros(2, np.uint8)
+    nnz = np.zeros(1, np.int64)
+    al = np.zeros(1, np.int64)
+    ex = np.zeros(1, np.int64)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    st = lib.attn_blockmask_build(p(rp), p(col), 1, 16, 8, 0, p(out_rp), p(out_col), p(out_fl), 2, p(nnz), p(al), p(ex))
+    assert st == ATTN_ECAPACITY and nnz[0] == 4 and list(out_rp) == [0, 2, 4] and al[0] == 256 and ex[0] == 4

@@ -1,0 +1,222 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the float64
+oracle on the same seeded inputs, element by element.
+
+Small shapes are compared in full (several tiles, ragged tails, edge cases);
+the five named workloads run at full size in the bench's launch configuration
+and are compared on seeded samples of query rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity_utils import compare, inputs, to64
+
+pytestmark = pytest.mark.gpu
+
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    import block_sparse_softmax_attn_amd as m
+    return m
+
+
+def _dense_case(lib, B, H, N, d, dtype, causal, seed, scale=None):
+    q, k, v = inputs(B, H, N, d, dtype, seed)
+    scale = float(np.float32(1.0 / math.sqrt(d))) if scale is None else scale
+    o, lse = lib.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, causal)
+    return compare(to64(o), to64(lse), o_ref, lse_ref, dtype, f"dense B{B} H{H} N{N} d{d} {dtype} causal={causal}")
+
+
+SMALL = [
+    (1, 1, 1, 64), (1, 2, 17, 64), (2, 1, 64, 128), (1, 3, 100, 128), (1, 2, 129, 64),
+    (2, 2, 300, 128), (1, 1, 1000, 64), (1, 2, 513, 128),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B{}H{}N{}d{}".format(*s))
+def test_dense_small(lib, shape, causal, dtype):
+    B, H, N, d = shape
+    print(f"case dense {shape} causal={causal} {dtype}", flush=True)
+    _dense_case(lib, B, H, N, d, dtype, causal, seed=1000 + N + d + causal)
+
+
+def test_c1_full(lib):
+    cfg = workloads.CONFIGS["c1"]
+    print("case c1", flush=True)
+    _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.seed, cfg.scale)
+
+
+def test_c2_full(lib):
+    cfg = workloads.CONFIGS["c2"]
+    print("case c2", flush=True)
+    _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.seed, cfg.scale)
+
+
+def _sampled_dense(lib, cfg, rows_per_head=None):
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    o, lse = lib.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=cfg.scale, causal=cfg.causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    n = rows_per_head or cfg.sample_rows
+    rows_fn = lambda b, h: workloads.sample_rows(cfg.N, n, cfg.seed * 1000 + h)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, cfg.scale, cfg.causal, rows=rows_fn)
+    worst = (0.0, 0.0)
+    i = 0
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            r = rows_fn(b, h)
+            do, dl = compare(to64(o[b, h, r]), to64(lse[b, h, r]), o_ref[i], lse_ref[i], cfg.dtype,
+                             f"{cfg.name} b{b} h{h}")
+            worst = (max(worst[0], do), max(worst[1], dl))
+            i += 1
+    print(f"{cfg.name}: max|dO| {worst[0]:.3e} max|dLSE| {worst[1]:.3e}", flush=True)
+
+
+def test_c3_sampled(lib):
+    print("case c3", flush=True)
+    _sampled_dense(lib, workloads.CONFIGS["c3"], rows_per_head=256)
+
+
+def test_c5_sampled(lib):
+    print("case c5", flush=True)
+    _sampled_dense(lib, workloads.CONFIGS["c5"])
+
+
+# ---------------------------------------------------------------------------
+# block-sparse
+# ---------------------------------------------------------------------------
+
+def _sparse_case(lib, B, H, N, d, dtype, causal, block, rows, meta_heads, seed, sample=None):
+    q, k, v = inputs(B, H, N, d, dtype, seed)
+    rp, col = workloads.lists_to_csr(rows)
+    mask = lib.blockmask_build(rp, col, meta_heads, N, block, causal)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = lib.attn_fwd_blocksparse(q.cuda(), k.cuda(), v.cuda(), mask, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    label = f"sparse B{B} H{H} N{N} d{d} {dtype} causal={causal} b={block} mh={meta_heads}"
+    if sample is None:
+        o_ref, lse_ref = oracle.attn_fwd_blocksparse(q, k, v, scale, causal, block, rp, col, meta_heads)
+        return compare(to64(o), to64(lse), o_ref, lse_ref, dtype, label)
+    rows_fn = lambda b, h: sample(h)
+    o_ref, lse_ref = oracle.attn_fwd_blocksparse(q, k, v, scale, causal, block, rp, col, meta_heads, rows=rows_fn)
+    i = 0
+    for b in range(B):
+        for h in range(H):
+            r = sample(h)
+            compare(to64(o[b, h, r]), to64(lse[b, h, r]), o_ref[i], lse_ref[i], dtype, f"{label} b{b} h{h}")
+            i += 1
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [64, 128])
+@pytest.mark.parametrize("N,d,meta", [(300, 64, 1), (517, 128, 2), (1024, 128, 1), (64, 64, 2)])
+def test_sparse_random_lists(lib, N, d, meta, block, causal, dtype):
+    B, H = 1, 2
+    nqb = -(-N // block)
+    rng = workloads.SplitMix64(7 * N + block + causal)
+    mh = 1 if meta == 1 else H
+    rows = workloads.random_lists(mh * nqb, nqb, rng, max_len=2 * nqb + 1, empty_prob_per_mille=150)
+    print(f"case sparse N{N} d{d} b{block} causal={causal} {dtype} mh={mh}", flush=True)
+    _sparse_case(lib, B, H, N, d, dtype, causal, block, rows, mh, seed=N + d)
+
+
+def test_c4_sampled(lib):
+    cfg = workloads.CONFIGS["c4"]
+    rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
+    print("case c4", flush=True)
+
+    def sample(h):
+        r = set(workloads.sample_rows(cfg.N, 384, cfg.seed * 1000 + h).tolist())
+        # rows of every empty query block and of the partial last block
+        for qb, lst in enumerate(rows):
+            if not lst:
+                r.update((qb * cfg.block, qb * cfg.block + 77))
+        r.update(range(cfg.N - 44, cfg.N, 5))
+        return np.array(sorted(r))
+
+    _sparse_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.block, rows, 1, cfg.seed, sample)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("block", [64, 128])
+def test_all_active_mask_equals_dense_bitwise(lib, causal, block):
+    B, H, N, d = 1, 3, 700, 128
+    q, k, v = (t.cuda() for t in inputs(B, H, N, d, "bf16", 77))
+    nqb = -(-N // block)
+    rp, col = workloads.lists_to_csr([list(range(nqb))[::-1] + [0] for _ in range(nqb)])
+    mask = lib.blockmask_build(rp, col, 1, N, block, causal)
+    o_s, l_s = lib.attn_fwd_blocksparse(q, k, v, mask, causal=causal)
+    o_d, l_d = lib.attn_fwd(q, k, v, causal=causal)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d) and torch.equal(l_s, l_d)
+
+
+def test_shuffled_duplicated_lists_give_identical_output(lib):
+    B, H, N, d, block = 1, 2, 640, 128, 128
+    nqb = N // block
+    q, k, v = (t.cuda() for t in inputs(B, H, N, d, "bf16", 78))
+    rng = workloads.SplitMix64(79)
+    base = [sorted({rng.below(nqb) for _ in range(3)}) for _ in range(nqb)]
+    shuffled = []
+    for r in base:
+        r2 = r + r[:1]
+        r2 = [r2[(i * 7 + 3) % len(r2)] for i in range(len(r2))] if r2 else []
+        shuffled.append(r2 + r2[:2])
+    outs = []
+    for rows in (base, shuffled):
+        rp, col = workloads.lists_to_csr(rows)
+        mask = lib.blockmask_build(rp, col, 1, N, block, True)
+        outs.append(lib.attn_fwd_blocksparse(q, k, v, mask, causal=True))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_run_to_run_bitwise_determinism(lib):
+    q, k, v = (t.cuda() for t in inputs(2, 4, 1111, 128, "bf16", 80))
+    a = lib.attn_fwd(q, k, v, causal=True)
+    b = lib.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_outputs_not_written_past_n(lib):
+    """Guard band: O and LSE views inside larger buffers; the canaries after
+    the last row must survive."""
+    B, H, N, d = 1, 2, 200, 64
+    q, k, v = (t.cuda() for t in inputs(B, H, N, d, "bf16", 81))
+    big_o = torch.full((B * H * N * d + 4096,), 7.0, device="cuda", dtype=torch.bfloat16)
+    big_l = torch.full((B * H * N + 1024,), 7.0, device="cuda", dtype=torch.float32)
+    o = big_o[:B * H * N * d].view(B, H, N, d)
+    lse = big_l[:B * H * N].view(B, H, N)
+    lib.attn_fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(big_o[B * H * N * d:] == 7.0) and torch.all(big_l[B * H * N:] == 7.0)
+
+
+def test_single_key_gives_its_value_on_gpu(lib):
+    q, k, v = (t.cuda() for t in inputs(2, 3, 1, 128, "bf16", 82))
+    o, lse = lib.attn_fwd(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
+    ref = (q.float() * k.float()).sum(-1) * float(np.float32(1 / math.sqrt(128)))
+    assert torch.allclose(lse, ref, atol=1e-3, rtol=0)
+
+
+def test_causal_row_zero_equals_v0(lib):
+    q, k, v = (t.cuda() for t in inputs(1, 4, 333, 64, "bf16", 83))
+    o, _ = lib.attn_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0], v[:, :, 0])
