@@ -1,0 +1,221 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one call of the hot path (host validation + launch + the fused
+kernel) over one batch of synthetic N(0,1) bf16 input already resident in
+HBM.  The default workload is the dense non-causal d=128 case (B=1 H=32
+N=8192), the one the throughput target is stated on.  Prints ONE JSON line:
+
+  value    allowed-pair TFLOP/s over the K timed steps (4*d flops per allowed
+           query-key pair: the QK^T and PV contractions), wall clock between
+           two device synchronisations;
+  roofline the fused kernel against the bf16 MFMA peak: achieved = flops per
+           launch / mean launch duration (HIP events on the launch stream);
+           traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE and
+           WRITE_SIZE counters (calibrated on a plain copy), read from
+           profiles/ and reported only while the kernel source is unchanged;
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same
+           workload (whole heads, about 10 s), on this host's cores.
+
+Other flags: --no-cpu-baseline, --copy-calibration (a plain device copy of
+known size, run under rocprofv3 --pmc to calibrate the byte counters).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz, dense
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_softmax_attn_amd", "csrc", "fwd_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_{workload}_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def allowed_pairs_dense(cfg) -> int:
+    per_head = cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.N
+    return cfg.B * cfg.H * per_head
+
+
+def read_traffic(workload: str):
+    path = TRAFFIC_FILE.format(workload=workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None   # counters were taken on another version of the kernel
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(cfg, q, k, v, budget_s: float = 10.0):
+    """The oracle as it stands, on whole heads of the same inputs, until the
+    time budget is spent (at least one head)."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    done_heads, flops, t_total = 0, 0, 0.0
+    H = cfg.H
+    for h in range(H):
+        qh, kh, vh = (t[:, h:h + 1].to("cpu") for t in (q, k, v))
+        t0 = time.perf_counter()
+        oracle.attn_fwd(qh, kh, vh, cfg.scale, cfg.causal)
+        t_total += time.perf_counter() - t0
+        done_heads += 1
+        per_head = cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.N
+        flops += 4 * cfg.d * per_head * cfg.B
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done_heads} of {cfg.B * H} (batch, head) pairs of {cfg.name}, every query row, "
+                  f"float64 numpy three-stage oracle, {t_total:.1f} s",
+    }
+
+
+def copy_calibration(nbytes: int = 1 << 30):
+    """A plain device-to-device copy of known size (torch's copy kernel)."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "dispatches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported by this build "
+              "(the attention forward is measured on one MI355X; sharding is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import torch
+    import block_sparse_softmax_attn_amd as attn
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = workloads.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    q, k, v = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
+               .to(torch.bfloat16).contiguous() for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
+
+    if cfg.sparse:
+        rp, col = workloads.config_block_lists(cfg)
+        t0 = time.perf_counter()
+        mask = attn.blockmask_build(rp, col, 1, cfg.N, cfg.block, cfg.causal)
+        build_ms = (time.perf_counter() - t0) * 1e3
+        pairs = int(mask.allowed_pairs[0]) * cfg.B * cfg.H
+        executed = int(mask.executed_tile_pairs[0]) * cfg.B * cfg.H * cfg.block * cfg.block
+        mask.to_device(dev)
+        step = lambda: attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
+    else:
+        build_ms = None
+        pairs = allowed_pairs_dense(cfg)
+        executed = None
+        step = lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
+    flops = 4 * cfg.d * pairs
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    mean_launch_ms = sum(launch_ms) / len(launch_ms)
+
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention fwd TFLOP/s (allowed pairs) + % of bf16 MFMA peak, 1xMI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": cfg.description,
+            "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "causal": cfg.causal,
+            "block_sparse": cfg.sparse, "scale": cfg.scale, "seed": cfg.seed,
+            "allowed_pairs": pairs, "flops_per_step": flops,
+            "flop_count": "4*d per allowed (query, key) pair",
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": read_traffic(args.workload),
+            "kernel": "fwd_bf16_kernel",
+            "mean_launch_ms": round(mean_launch_ms, 5),
+        },
+    }
+    if executed is not None:
+        rec["config"]["executed_tile_flops_per_step"] = 4 * cfg.d * executed
+        rec["config"]["executed_tile_tflops"] = round(4 * cfg.d * executed * args.steps / wall / 1e12, 3)
+        rec["config"]["blockmask_build_ms_host"] = round(build_ms, 3)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
