@@ -176,7 +176,7 @@ def main():
     value = flops * args.steps / wall / 1e12
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
     rec = {
-        "metric": "attention fwd TFLOP/s (allowed pairs) + % of bf16 MFMA peak, 1xMI355X",
+        "metric": "attention fwd TFLOP/s (allowed pairs) + % of bf16 MFMA peak, 1\u00d7MI355X",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
