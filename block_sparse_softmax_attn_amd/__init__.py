@@ -24,9 +24,9 @@ from typing import Optional
 import numpy as np
 
 from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN_FLAG_PARTIAL, ATTN_OK,
-                   AttnError, LIB_PATH, check, lib, status_string)
+                   AttnError, LIB_PATH, check, get as _get_lib, status_string)
 
-__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "BlockMask", "AttnError", "LIB_PATH",
+__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "BlockMask", "AttnError", "LIB_PATH",
            "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
 
 
@@ -64,21 +64,48 @@ def _outputs(q, out, lse):
     return out, lse
 
 
+def workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
+    """Device workspace (bytes) the forward needs for these sizes."""
+    code = dtype if isinstance(dtype, int) else (ATTN_BF16 if str(dtype).endswith("bfloat16") else ATTN_F32)
+    n = int(_get_lib().attn_fwd_workspace_bytes(int(B), int(H), int(N), int(d), code))
+    if n < 0:
+        raise ValueError("sizes or dtype not supported")
+    return n
+
+
+def _workspace(q, workspace):
+    import torch
+    B, H, N, d = q.shape
+    need = workspace_bytes(B, H, N, d, _dtype_code(q))
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on q's device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
 def _stream(dev):
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, lse=None):
-    """Dense or causal attention forward; returns (O in q's dtype, LSE fp32 [B,H,N])."""
+def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, lse=None, workspace=None):
+    """Dense or causal attention forward; returns (O in q's dtype, LSE fp32 [B,H,N]).
+
+    ``workspace``: optional device buffer of at least ``workspace_bytes(...)``
+    bytes (allocated per call from torch's caching allocator when omitted)."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
+    ws, ws_bytes = _workspace(q, workspace)
     with torch.cuda.device(q.device):
-        st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)), _stream(q.device))
+        st = _get_lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
+                          ws.data_ptr() if ws is not None else None, ws_bytes, _stream(q.device))
     check("attn_fwd", st)
     return out, lse
 
@@ -128,7 +155,7 @@ def blockmask_build(raw_row_ptr, raw_col, meta_heads: int, N: int, block: int, c
     allowed = np.zeros(max(int(meta_heads), 1), dtype=np.int64)
     executed = np.zeros(max(int(meta_heads), 1), dtype=np.int64)
     ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
-    st = lib.attn_blockmask_build(ptr(rp), ptr(rc) if rc.size else None, int(meta_heads), int(N), int(block),
+    st = _get_lib().attn_blockmask_build(ptr(rp), ptr(rc) if rc.size else None, int(meta_heads), int(N), int(block),
                                   int(bool(causal)), ptr(row_ptr), ptr(col), ptr(flags), cap, ptr(nnz),
                                   ptr(allowed), ptr(executed))
     check("attn_blockmask_build", st)
@@ -138,7 +165,7 @@ def blockmask_build(raw_row_ptr, raw_col, meta_heads: int, N: int, block: int, c
 
 
 def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None, causal: Optional[bool] = None,
-                         out=None, lse=None):
+                         out=None, lse=None, workspace=None):
     """Block-sparse attention forward, renormalised over the allowed pairs."""
     import torch
     _check_qkv(q, k, v)
@@ -149,10 +176,12 @@ def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
     row_ptr, col, flags = mask.to_device(q.device)
+    ws, ws_bytes = _workspace(q, workspace)
     with torch.cuda.device(q.device):
-        st = lib.attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        st = _get_lib().attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                       B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(causal), mask.block,
                                       row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz,
-                                      mask.meta_heads, _stream(q.device))
+                                      mask.meta_heads, ws.data_ptr() if ws is not None else None, ws_bytes,
+                                      _stream(q.device))
     check("attn_fwd_blocksparse", st)
     return out, lse

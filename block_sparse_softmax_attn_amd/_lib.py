@@ -1,8 +1,8 @@
 """ctypes binding of ``libbsattn.so`` (the C ABI in ``include/bsattn.h``).
 
 Argument marshalling only: every step of the attention forward runs in the HIP
-kernels behind the C ABI.  Importing this module fails loudly when the library
-has not been built: there is no fallback path.
+kernels behind the C ABI.  The library is loaded on first use; if it has not
+been built, that use raises ImportError: there is no fallback path.
 """
 from __future__ import annotations
 
@@ -21,7 +21,8 @@ ATTN_BF16 = 1
 ATTN_FLAG_DIAGONAL = 1
 ATTN_FLAG_PARTIAL = 2
 
-EXPORTED = ("attn_status_string", "attn_fwd", "attn_blockmask_build", "attn_fwd_blocksparse")
+EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_blockmask_build",
+            "attn_fwd_blocksparse")
 
 
 class AttnError(RuntimeError):
@@ -38,21 +39,31 @@ def _load() -> ctypes.CDLL:
     i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i32]
+    lib.attn_fwd_workspace_bytes.restype = i64
+    lib.attn_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
     lib.attn_blockmask_build.restype = i32
     lib.attn_blockmask_build.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
     lib.attn_fwd_blocksparse.restype = i32
     lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
-                                         vp, vp, vp, i64, i64, vp]
+                                         vp, vp, vp, i64, i64, vp, i64, vp]
     return lib
 
 
-lib = _load()
+_LIB = None
+
+
+def get() -> ctypes.CDLL:
+    """The loaded library (loaded once; raises ImportError if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = _load()
+    return _LIB
 
 
 def status_string(status: int) -> str:
-    return lib.attn_status_string(int(status)).decode()
+    return get().attn_status_string(int(status)).decode()
 
 
 def check(fn: str, status: int) -> None:

@@ -48,9 +48,30 @@ bsattn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, 
     return a;
 }
 
-int run(const bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, hipStream_t stream) {
-    hipError_t e = dtype == ATTN_BF16 ? bsattn::launch_fwd_bf16(a, mode, stream)
-                                      : bsattn::launch_fwd_f32(a, mode, stream);
+int64_t workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (dtype != ATTN_BF16) return 0;
+    return B * H * d * bsattn::vt_padded_keys(N) * 2;
+}
+
+int check_workspace(void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    const int64_t need = workspace_bytes(B, H, N, d, dtype);
+    if (need == 0) return ATTN_OK;
+    if (ws_bytes < need) return ATTN_ECAPACITY;
+    if (!ws || !aligned16(ws)) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+// bf16: V^T into the workspace, then the fused kernel, both on `stream`.
+int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, hipStream_t stream) {
+    hipError_t e;
+    if (dtype == ATTN_BF16) {
+        a.vt = ws;
+        a.npad = static_cast<int>(bsattn::vt_padded_keys(a.N));
+        e = bsattn::launch_v_transpose(a, stream);
+        if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, mode, stream);
+    } else {
+        e = bsattn::launch_fwd_f32(a, mode, stream);
+    }
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
@@ -67,24 +88,37 @@ extern "C" const char* attn_status_string(int status) {
     }
 }
 
+extern "C" int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128)) return -1;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return -1;
+    if (B > (int64_t(1) << 62) / H || B * H > (int64_t(1) << 62) / (2 * d * bsattn::vt_padded_keys(N))) return -1;
+    return workspace_bytes(B, H, N, d, dtype);
+}
+
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                        int64_t N, int64_t d, int dtype, float scale, int causal, hipStream_t stream) {
-    const int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
+                        int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
+                        int64_t workspace_bytes_given, hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
-    const bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
-    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, stream);
+    st = check_workspace(workspace, workspace_bytes_given, B, H, N, d, dtype);
+    if (st != ATTN_OK) return st;
+    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, workspace, stream);
 }
 
 extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                     int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
                                     int64_t block, const int32_t* row_ptr, const int32_t* col,
-                                    const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
-    const int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
+                                    const uint8_t* flags, int64_t nnz, int64_t meta_heads, void* workspace,
+                                    int64_t workspace_bytes_given, hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
     if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
     if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
+    st = check_workspace(workspace, workspace_bytes_given, B, H, N, d, dtype);
+    if (st != ATTN_OK) return st;
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
     a.row_ptr = row_ptr;
     a.col = col;
@@ -92,5 +126,5 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
     a.nnz = nnz;
     a.meta_heads = static_cast<int>(meta_heads);
     a.block = static_cast<int>(block);
-    return run(a, dtype, bsattn::Mode::kSparse, stream);
+    return run(a, dtype, bsattn::Mode::kSparse, workspace, stream);
 }

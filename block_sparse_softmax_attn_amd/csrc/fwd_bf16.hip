@@ -9,22 +9,25 @@
 // LSE = m + ln l.
 //
 // gfx950 mapping (ours, not the pages'):
-//   * 4 waves x 32 query rows (BM = 128); each wave computes S^T = K Q^T with
+//   * NW waves x 32 query rows.  Each wave computes S^T = K Q^T with
 //     v_mfma_f32_32x32x16_bf16, so a lane holds 16 scores of ONE query row per
 //     32-key block: the row max and row sum stay inside the lane plus one
 //     exchange with lane l^32 (v_permlane32_swap), no LDS reductions.
-//   * The S^T accumulator converts in place to the B operand of O^T += V^T P^T;
-//     the key order inside each 16-key step is permuted to match, and V is
-//     stored transposed and permuted in LDS so its A operand is one
-//     ds_read_b128 per lane.
+//   * The S^T accumulator converts in place to the B operand of O^T += V^T P^T.
+//     The key order inside each 16-key MFMA step is permuted to the keys a lane
+//     already holds; V^T is prepared once per call in that order (a transpose
+//     pass into a workspace), so both K and V^T tiles are plain 16-byte rows.
+//   * K and V^T tiles go from global memory straight into LDS
+//     (global_load_lds_dwordx4: no VGPR staging, no LDS store instructions),
+//     NSTAGE tiles in flight, 16-byte chunks XOR-swizzled per row so the
+//     fragment reads (one ds_read_b128 per lane) are bank-conflict free.
 //   * Logits are handled in base-2 units (scale * log2 e folded into one FMA
 //     before v_exp_f32).  The running max is only raised when a row's new max
 //     exceeds it by more than 8 (a factor 256): exact, since A and l share the
 //     stale max, and it removes almost every rescale of the accumulator.
-//   * K/V tiles are double-buffered in LDS; the next tile's global loads are
-//     in flight while the current tile is computed.
-//   * Causal: key tiles wholly in the future are never visited; the diagonal
-//     tiles get the element mask.  Block-sparse: the tile loop runs over the
+//   * Causal: key tiles wholly in the future are never visited, a wave skips
+//     the tiles that lie past all of its rows, and only tiles that cross the
+//     diagonal get the element mask.  Block-sparse: the tile loop runs over the
 //     canonical list of active key blocks of the query block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -35,37 +38,64 @@ namespace bsattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 64;                 // keys per tile step
 constexpr float kSlack = 8.0f;         // lazy-rescale headroom, base-2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D, int NW>
+template <int D, int NW, int NS>
 struct Geo {
-    static constexpr int NT = 64 * NW;             // threads per workgroup
-    static constexpr int BM = 32 * NW;             // query rows per workgroup
-    static constexpr int KS = D + 8;               // K row stride in LDS (bf16)
-    static constexpr int VS = BN + 8;              // V^T row stride in LDS (bf16)
-    static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = D * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int K_CHUNKS = BN * D / 8;    // 16-byte chunks of a K tile
-    static constexpr int K_PER_T = K_CHUNKS / NT;
-    static constexpr int V_PAIRS = (BN / 4) * (D / 8);   // (4 keys x 8 dims) pieces of a V tile
-    static constexpr int V_PER_T = (V_PAIRS + NT - 1) / NT;
-    static_assert(K_CHUNKS % NT == 0, "K tile must split evenly");
+    static constexpr int NT = 64 * NW;               // threads per workgroup
+    static constexpr int BM = 32 * NW;               // query rows per workgroup
+    static constexpr int K_BYTES = BN * D * 2;       // K tile: BN rows of D bf16
+    static constexpr int V_BYTES = D * BN * 2;       // V^T tile: D rows of BN bf16
+    static constexpr int K_PER_W = K_BYTES / 1024 / NW;   // 1 KiB direct-to-LDS loads per wave
+    static constexpr int V_PER_W = V_BYTES / 1024 / NW;
+    static constexpr int PER_W = K_PER_W + V_PER_W;
+    static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "tile must split over waves");
+    static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
+    static_assert((NS - 2) * PER_W < 64, "vmcnt range");
 };
 
-// Position of key o (0..15) of a 16-key step inside the V^T LDS row: keys
-// {4h..4h+3, 8+4h..8+4h+3} (the ones lane half h holds in its S^T registers)
-// become the contiguous slots 8h..8h+7.
-__device__ __forceinline__ int vt_pos_of_quad(int kq) {
-    // first key of quad kq (keys 4kq..4kq+3) within a BN-key tile
-    return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+// 16 bytes per lane from global memory straight into LDS: lane i writes
+// lds + 16 i; lds must be the same for the whole wave (it goes to M0).  Issued
+// as inline asm so the compiler does not make every later LDS read wait for
+// every load in flight (it cannot tell the stage buffers apart); completion is
+// tracked by hand with wait_vmcnt before the barrier that publishes a tile.
+// Nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const unsigned lds_addr =
+        __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "s"(lds_addr) : "memory");
+#endif
 }
+
+// s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier without a memory fence: the direct-to-LDS data was waited
+// for explicitly; the empty asm keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Row r, logical 16-byte chunk c -> physical chunk.  Sixteen consecutive rows
+// read at one logical chunk land in 16 distinct slots of a 256-byte bank window.
+template <int D>
+__device__ __forceinline__ int k_swz(int r, int c) {
+    return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+__device__ __forceinline__ int v_swz(int d, int c) { return c ^ ((d >> 1) & 7); }   // V^T rows are 128 bytes
 
 __device__ __forceinline__ float xor32_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -77,76 +107,25 @@ __device__ __forceinline__ float xor32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Tile descriptor: first key of the 64-key tile and what to mask in it.
+// One 64-key tile of the schedule.
 struct TileDesc {
-    int kb0;
-    int causal_mask;   // element mask j <= i needed somewhere in the tile
-    int skip;          // no valid key at all (compute skipped, loads clamped)
+    int kb0;       // first key
+    int nlim;      // keys j >= nlim are masked (N; 0 for an invalid metadata entry)
+    int causal;    // element mask j <= i applies
+    int masked;    // any element mask needed (uniform over the workgroup)
 };
 
-template <int D, int NW>
-__device__ __forceinline__ void load_tile(const __bf16* __restrict__ Kh, const __bf16* __restrict__ Vh, int kb0,
-                                          int N, int tid, u32x4 (&kreg)[Geo<D, NW>::K_PER_T],
-                                          u32x4 (&vreg)[Geo<D, NW>::V_PER_T][4]) {
-    using G = Geo<D, NW>;
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int u = 0; u < G::K_PER_T; ++u) {
-        const int c = tid + u * G::NT;
-        const int row = c / CPR, ch = c % CPR;
-        const int key = min(kb0 + row, N - 1);
-        kreg[u] = *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + ch * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < G::V_PER_T; ++u) {
-        const int pr = tid + u * G::NT;
-        if (pr < G::V_PAIRS) {
-            const int kq = pr % (BN / 4), dq = pr / (BN / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = min(kb0 + 4 * kq + r, N - 1);
-                vreg[u][r] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + dq * 8);
-            }
-        }
-    }
-}
-
-template <int D, int NW>
-__device__ __forceinline__ void store_tile(__bf16* sK, __bf16* sV, int tid, const u32x4 (&kreg)[Geo<D, NW>::K_PER_T],
-                                           const u32x4 (&vreg)[Geo<D, NW>::V_PER_T][4]) {
-    using G = Geo<D, NW>;
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int u = 0; u < G::K_PER_T; ++u) {
-        const int c = tid + u * G::NT;
-        const int row = c / CPR, ch = c % CPR;
-        *reinterpret_cast<u32x4*>(sK + row * G::KS + ch * 8) = kreg[u];
-    }
-#pragma unroll
-    for (int u = 0; u < G::V_PER_T; ++u) {
-        const int pr = tid + u * G::NT;
-        if (pr < G::V_PAIRS) {
-            const int kq = pr % (BN / 4), dq = pr / (BN / 4);
-            const int pos = vt_pos_of_quad(kq);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1;
-                const int sh = (e & 1) * 16;
-                const unsigned a0 = (vreg[u][0][w] >> sh) & 0xffffu, a1 = (vreg[u][1][w] >> sh) & 0xffffu;
-                const unsigned a2 = (vreg[u][2][w] >> sh) & 0xffffu, a3 = (vreg[u][3][w] >> sh) & 0xffffu;
-                u32x2 pk;
-                pk[0] = a0 | (a1 << 16);
-                pk[1] = a2 | (a3 << 16);
-                *reinterpret_cast<u32x2*>(sV + (dq * 8 + e) * G::VS + pos) = pk;
-            }
-        }
-    }
-}
-
-template <int D, int NW, int MODE>
+template <int D, int NW, int NS, int MODE>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
-    using G = Geo<D, NW>;
-    __shared__ __attribute__((aligned(16))) __bf16 smem[2 * G::STAGE];
+    using G = Geo<D, NW, NS>;
+    // One array per stage: distinct objects let the compiler see that a tile in
+    // flight never aliases the tile being read.
+    constexpr int KB2 = NS > 2 ? G::K_BYTES : 16, KB3 = NS > 3 ? G::K_BYTES : 16;
+    constexpr int VB2 = NS > 2 ? G::V_BYTES : 16, VB3 = NS > 3 ? G::V_BYTES : 16;
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[G::K_BYTES], sK1[G::K_BYTES], sK2[KB2], sK3[KB3];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::V_BYTES], sV1[G::V_BYTES], sV2[VB2], sV3[VB3];
+    unsigned char* const kbuf[4] = {sK0, sK1, sK2, sK3};
+    unsigned char* const vbuf[4] = {sV0, sV1, sV2, sV3};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -160,16 +139,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     if (MODE != (int)Mode::kDense) qt = nqt - 1 - qt;   // heaviest query tiles first
     const int q0 = qt * G::BM;
     const int q0w = q0 + 32 * w;
+    const int qi = q0w + l32;  // this lane's query row
 
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
     const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
-    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
+    const __bf16* Vth = static_cast<const __bf16*>(a.vt) + bh * (int64_t)a.npad * D;
 
-    // Tile schedule.
-    int ntiles = 0;
-    int e0 = 0;
-    int subs = 1;
-    int nqb_meta = 0;
+    // ---- tile schedule ----
+    int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0;
     if (MODE == (int)Mode::kDense) {
         ntiles = (N + BN - 1) / BN;
     } else if (MODE == (int)Mode::kCausal) {
@@ -178,97 +155,121 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         subs = a.block / BN;
         nqb_meta = (N + a.block - 1) / a.block;
         const int h = (int)(bh % a.H);
-        const int mh = a.meta_heads == 1 ? 0 : h;
-        const int r = mh * nqb_meta + qt;            // BM == block for sparse launches
+        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + qt;   // BM == block for sparse launches
         int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
         lo = (int)min<int64_t>(max(lo, 0), a.nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);
         e0 = lo;
         ntiles = (hi_ - lo) * subs;
     }
-
     auto describe = [&](int it) -> TileDesc {
         TileDesc t;
         if (MODE == (int)Mode::kSparse) {
             const int e = e0 + it / subs;
-            const int sub = it % subs;
             const int kb = a.col[e];
-            const int f = a.flags[e];
             const bool valid = kb >= 0 && kb < nqb_meta;
-            t.kb0 = valid ? kb * a.block + sub * BN : 0;
+            t.kb0 = valid ? kb * a.block + (it % subs) * BN : 0;
+            t.nlim = valid ? N : 0;
             // the flag comes from canonical metadata; the geometric test keeps a
             // causal launch correct even for lists that were not pruned
-            t.causal_mask = ((f & 1) != 0) || (a.causal && t.kb0 + BN - 1 > q0);
-            t.skip = !valid || t.kb0 >= N;
+            t.causal = ((a.flags[e] & 1) != 0) || (a.causal && t.kb0 + BN - 1 > q0);
         } else {
             t.kb0 = it * BN;
-            t.causal_mask = (MODE == (int)Mode::kCausal) && (t.kb0 + BN - 1 > q0);
-            t.skip = 0;
+            t.nlim = N;
+            t.causal = (MODE == (int)Mode::kCausal) && (t.kb0 + BN - 1 > q0);
         }
+        t.masked = t.causal || (t.kb0 + BN > t.nlim);
         return t;
     };
 
-    // Query fragments (B operand of S^T = K Q^T): lane holds dims 16s+8hi..+7 of row q0w+l32.
-    bf16x8 qf[D / 16];
-    {
-        const int qrow = min(q0w + l32, N - 1);
+    // Source offsets of this wave's direct-to-LDS loads: lane i of load g fills
+    // bytes [1024 g + 16 i, +16) of the tile, i.e. row r, physical chunk p,
+    // with logical chunk swz(r, p) of that row.
+    int k_row[G::K_PER_W], k_col[G::K_PER_W], v_off[G::V_PER_W];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s)
-            qf[s] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * D + 16 * s + 8 * hi);
+    for (int i = 0; i < G::K_PER_W; ++i) {
+        const int byte = (w * G::K_PER_W + i) * 1024 + lane * 16;
+        const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
+        k_row[i] = r;
+        k_col[i] = k_swz<D>(r, p) * 8;
     }
+#pragma unroll
+    for (int i = 0; i < G::V_PER_W; ++i) {
+        const int byte = (w * G::V_PER_W + i) * 1024 + lane * 16;
+        const int d = byte / (2 * BN), p = (byte % (2 * BN)) / 16;
+        v_off[i] = d * a.npad + v_swz(d, p) * 8;
+    }
+    auto issue_tile = [&](int kb0, unsigned char* dK, unsigned char* dV) {
+#pragma unroll
+        for (int i = 0; i < G::K_PER_W; ++i) {
+            const int key = min(kb0 + k_row[i], N - 1);
+            dma16(Kh + (int64_t)key * D + k_col[i], dK + (w * G::K_PER_W + i) * 1024);
+        }
+#pragma unroll
+        for (int i = 0; i < G::V_PER_W; ++i)
+            dma16(Vth + (int64_t)kb0 + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
+    };
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
     float m_run = -__builtin_inff();   // running max, base-2 units (possibly stale by < kSlack)
-    float ell = 0.f;           // this lane's share of the denominator
+    float ell = 0.f;                   // this lane's share of the denominator
     const float sl2 = a.scale_log2;
-    const int qi = q0w + l32;  // this lane's query row
-
-    u32x4 kreg[G::K_PER_T];
-    u32x4 vreg[G::V_PER_T][4];
 
     if (ntiles > 0) {
-        TileDesc t0 = describe(0);
-        load_tile<D, NW>(Kh, Vh, t0.kb0, N, tid, kreg, vreg);
-        store_tile<D, NW>(smem, smem + G::K_ELEMS, tid, kreg, vreg);
-        __syncthreads();
-    }
-
-    for (int it = 0; it < ntiles; ++it) {
-        const TileDesc t = describe(it);
-        const bool more = it + 1 < ntiles;
-        if (more) {
-            const TileDesc tn = describe(it + 1);
-            load_tile<D, NW>(Kh, Vh, tn.kb0, N, tid, kreg, vreg);
+        // Query fragments (B operand of S^T = K Q^T): dims 16k+8hi..+7 of row qi.
+        bf16x8 qf[D / 16];
+        {
+            const int qrow = min(qi, N - 1);
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k)
+                qf[k] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * D + 16 * k + 8 * hi);
         }
-        const __bf16* sK = smem + (it & 1) * G::STAGE;
-        const __bf16* sV = sK + G::K_ELEMS;
+        // Q has landed before any tile load is issued: the vmcnt accounting
+        // below then only ever counts tile loads.
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < ntiles) issue_tile(describe(s).kb0, kbuf[s], vbuf[s]);
 
-        const bool wave_dead = t.skip || (t.causal_mask && t.kb0 > q0w + 31);
-        if (!wave_dead) {
-            // ---- scores S^T (keys x queries) ----
-            f32x16 sacc[BN / 32];
+        // Tile it, in stage buffer u = it % NS: wait for its loads, barrier
+        // (every wave's loads have landed and every wave is done with tile
+        // it-1), refill the buffer of tile it-1 with tile it+NS-1, compute.
+        auto tile = [&](int it, int u) {
+            const int ahead = min(NS - 2, ntiles - 1 - it);   // tiles issued after this one
+            if (ahead >= 2) wait_vmcnt<2 * G::PER_W>();
+            else if (ahead == 1) wait_vmcnt<G::PER_W>();
+            else wait_vmcnt<0>();
+            barrier();
+            const int un = (u + NS - 1) % NS;
+            if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, kbuf[un], vbuf[un]);
+            const TileDesc t = describe(it);
+            if (t.causal && t.kb0 > q0w + 31) return;   // every row of this wave precedes the tile
+            const unsigned char* bK = kbuf[u];
+            const unsigned char* bV = vbuf[u];
+
+            // ---- S^T: lane (l32, hi) gets, in s[c][v], the score of query l32
+            // and key kb0 + 32c + 8(v>>2) + 4hi + (v&3) ----
+            f32x16 s[BN / 32];
 #pragma unroll
             for (int c = 0; c < BN / 32; ++c) {
-                sacc[c] = f32x16{};
+                s[c] = f32x16{};
+                const int r = 32 * c + l32;
 #pragma unroll
-                for (int s = 0; s < D / 16; ++s) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + (32 * c + l32) * G::KS + 16 * s + 8 * hi);
-                    sacc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[c], 0, 0, 0);
+                for (int k = 0; k < D / 16; ++k) {
+                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(bK + r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16);
+                    s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], s[c], 0, 0, 0);
                 }
             }
-            // ---- masks: keys past N, and j > i on diagonal tiles ----
-            const bool need_n = t.kb0 + BN > N;
-            const bool need_c = t.causal_mask && (t.kb0 + BN - 1 > q0w);
-            if (need_n || need_c) {
+            if (t.masked) {
 #pragma unroll
                 for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
-                        const bool bad = (j >= N) || (need_c && j > qi);
-                        sacc[c][v] = bad ? -__builtin_inff() : sacc[c][v];
+                        const bool bad = (j >= t.nlim) || (t.causal && j > qi);
+                        s[c][v] = bad ? -__builtin_inff() : s[c][v];
                     }
             }
             // ---- online softmax ----
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
             for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[c][v]);
+                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[c][v]);
             mx = xor32_max(mx);
             const float mt = mx * sl2;
             const bool upd = mt > m_run + kSlack;
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                 const int c = g >> 1, t8 = (g & 1) * 8;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[c][t8 + i], sl2, -mu));
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][t8 + i], sl2, -mu));
                     ts[i] = g == 0 ? p : ts[i] + p;
                     pf[g][i] = (__bf16)p;
                 }
@@ -305,19 +306,19 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             ell += ((ts[0] + ts[1]) + (ts[2] + ts[3])) + ((ts[4] + ts[5]) + (ts[6] + ts[7]));
             // ---- O^T += V^T P^T ----
 #pragma unroll
-            for (int db = 0; db < D / 32; ++db)
+            for (int g = 0; g < BN / 16; ++g)
 #pragma unroll
-                for (int g = 0; g < BN / 16; ++g) {
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + (32 * db + l32) * G::VS + 16 * g + 8 * hi);
+                for (int db = 0; db < D / 32; ++db) {
+                    const int d = 32 * db + l32;
+                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz(d, 2 * g + hi) * 16);
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g], oacc[db], 0, 0, 0);
                 }
+        };
+        for (int base = 0; base < ntiles; base += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u)
+                if (base + u < ntiles) tile(base + u, u);
         }
-
-        if (more) {
-            __bf16* nK = smem + ((it + 1) & 1) * G::STAGE;
-            store_tile<D, NW>(nK, nK + G::K_ELEMS, tid, kreg, vreg);
-        }
-        __syncthreads();
     }
 
     // ---- epilogue: O = A / l, LSE = (m + log2 l) * ln 2 ----
@@ -329,7 +330,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
                 bf16x4 ov;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[db][4 * j + i] * inv);
@@ -341,28 +341,79 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     }
 }
 
-template <int D, int NW, int MODE>
+// V [BH][N][D] -> V^T [BH][D][npad].  Inside each 16-key group, slot 8h + w of
+// a row holds key 4h + (w & 3) + 8 (w >> 2): the keys that lane half h owns in
+// the S^T layout, so one 16-byte chunk is one MFMA operand.  Keys >= N are 0.
+// One workgroup per (64-key block, b*h).
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const __bf16* __restrict__ v, __bf16* __restrict__ vt,
+                                                           int N, int npad) {
+    __shared__ __bf16 tile[BN][D + 2];
+    const int kb0 = blockIdx.x * BN;
+    const int64_t bh = blockIdx.y;
+    const __bf16* src = v + bh * (int64_t)N * D;
+    for (int c = threadIdx.x; c < BN * D / 8; c += 256) {
+        const int r = c / (D / 8), ch = c % (D / 8);
+        const int key = kb0 + r;
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (key < N) x = *reinterpret_cast<const u32x4*>(src + (int64_t)key * D + 8 * ch);
+        const __bf16* xs = reinterpret_cast<const __bf16*>(&x);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[r][8 * ch + i] = xs[i];
+    }
+    __syncthreads();
+    __bf16* dst = vt + bh * (int64_t)npad * D;
+    for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
+        const int d = c / (BN / 8), ch = c % (BN / 8);
+        bf16x8 out;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int slot = 8 * ch + i;
+            const int grp = slot >> 4, h = (slot >> 3) & 1, ww = slot & 7;
+            out[i] = tile[16 * grp + 4 * h + (ww & 3) + 8 * (ww >> 2)][d];
+        }
+        *reinterpret_cast<bf16x8*>(dst + (int64_t)d * npad + kb0 + 8 * ch) = out;
+    }
+}
+
+template <int D, int NW, int NS, int MODE>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    using G = Geo<D, NW>;
+    using G = Geo<D, NW, NS>;
     const int64_t nqt = (a.N + G::BM - 1) / G::BM;
     const int64_t grid = nqt * a.BH;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, MODE>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
+    // dense and causal: 8 waves (256 query rows) share each K/V tile, one
+    // workgroup per CU, 3 tiles in flight; block-sparse: the workgroup is one
+    // query block, two workgroups per CU, 2 tiles in flight.
     switch (mode) {
-        case Mode::kDense: return launch<D, 4, (int)Mode::kDense>(a, stream);
-        case Mode::kCausal: return launch<D, 4, (int)Mode::kCausal>(a, stream);
+        case Mode::kDense: return launch<D, 8, 3, (int)Mode::kDense>(a, stream);
+        case Mode::kCausal: return launch<D, 8, 3, (int)Mode::kCausal>(a, stream);
         case Mode::kSparse:
-            if (a.block == 128) return launch<D, 4, (int)Mode::kSparse>(a, stream);
-            return launch<D, 2, (int)Mode::kSparse>(a, stream);
+            if (a.block == 128) return launch<D, 4, 2, (int)Mode::kSparse>(a, stream);
+            return launch<D, 2, 2, (int)Mode::kSparse>(a, stream);
     }
     return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+int64_t vt_padded_keys(int64_t N) { return (N + 127) / 128 * 128; }
+
+hipError_t launch_v_transpose(const FwdArgs& a, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.npad / BN), (unsigned)a.BH);
+    if (a.d == 64)
+        hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, stream, static_cast<const __bf16*>(a.v),
+                           static_cast<__bf16*>(a.vt), a.N, a.npad);
+    else
+        hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, stream, static_cast<const __bf16*>(a.v),
+                           static_cast<__bf16*>(a.vt), a.N, a.npad);
+    return hipGetLastError();
+}
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, Mode mode, hipStream_t stream) {
     if (a.d == 64) return launch_d<64>(a, mode, stream);

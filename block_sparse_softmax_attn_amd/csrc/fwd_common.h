@@ -26,6 +26,9 @@ struct FwdArgs {
     int64_t nnz;
     int meta_heads;
     int block;
+    // workspace: V transposed per head, [BH][d][npad] bf16 (bf16 path only)
+    void* vt;
+    int npad;            // N rounded up to the 64-key tile
 };
 
 enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2 };
@@ -33,6 +36,10 @@ enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2 };
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, Mode mode, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, Mode mode, hipStream_t stream);
+// Fill a.vt from a.v (bf16 path): V^T with the key order the forward kernel reads.
+hipError_t launch_v_transpose(const FwdArgs& a, hipStream_t stream);
+// Keys per head of the V^T workspace: N rounded up to 128.
+int64_t vt_padded_keys(int64_t N);
 
 // Workgroup index -> (tile order index) so that consecutive tile indices land
 // on the same XCD: the dispatcher hands workgroup i to XCD i % 8, so XCD x

@@ -24,8 +24,9 @@
  *   - Tensors are dense and contiguous: Q, K, V, O are [B, H, N, d] with row
  *     stride d; LSE is [B, H, N] fp32.  Q, K, V, O have the same dtype.
  *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
- *     aligned to 16 bytes.  The caller owns every buffer; the library never
- *     allocates device memory and keeps no pointer after a call returns.
+ *     aligned to 16 bytes.  The caller owns every buffer, including the
+ *     workspace the bf16 path needs (attn_fwd_workspace_bytes); the library
+ *     never allocates device memory and keeps no pointer after a call returns.
  *   - Calls are asynchronous on `stream` (0 = the null stream): the inputs
  *     must stay alive and unmodified until the stream has run the work.
  *   - Allowed pairs: causal keeps j <= i.  A query row with no allowed key
@@ -48,7 +49,7 @@ enum {
     ATTN_OK = 0,
     ATTN_EINVAL = -1,       /* null pointer, bad size, bad flag, misaligned pointer, malformed metadata */
     ATTN_EUNSUPPORTED = -2, /* valid request outside what the kernels implement (d, dtype, block size) */
-    ATTN_ECAPACITY = -3,    /* caller-provided output buffer too small */
+    ATTN_ECAPACITY = -3,    /* caller-provided output or workspace buffer too small */
     ATTN_EHIP = -4          /* the HIP runtime reported an error at launch */
 };
 
@@ -64,6 +65,14 @@ enum {
 const char* attn_status_string(int status);
 
 /*
+ * attn_fwd_workspace_bytes - bytes of device workspace attn_fwd and
+ * attn_fwd_blocksparse need for these sizes: B*H*d*ceil(N/128)*128*2 for
+ * ATTN_BF16 (V transposed per head, in the key order the kernel reads), 0 for
+ * ATTN_F32.  Returns -1 for sizes or a dtype the kernels do not accept.
+ */
+int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+/*
  * attn_fwd - dense or causal attention forward.
  *   q, k, v : device, [B,H,N,d] of `dtype` (ATTN_BF16 or ATTN_F32), read only.
  *   o       : device, [B,H,N,d] of `dtype`, written (O in the input dtype).
@@ -73,14 +82,18 @@ const char* attn_status_string(int status);
  *   scale   : finite and > 0 (e.g. 1/sqrt(d)); logits are scale * q.k.
  *   causal  : 0 or 1 (1 keeps j <= i; tiles wholly in the future are skipped,
  *             the diagonal tile gets the triangular element mask).
+ *   workspace, workspace_bytes : device scratch of at least
+ *             attn_fwd_workspace_bytes(...) bytes (may be NULL when that is 0);
+ *             overwritten by the call, must not overlap any tensor argument.
  * Source: "Exact Blocks, Rings, and Sparsity", section 2, forward kernel
  * ("What the forward kernel keeps on chip"): the host wrapper takes q, k, v
  * and a causal flag and returns O and the per-row LSE.
- * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY (workspace too
+ * small), ATTN_EHIP.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
-             hipStream_t stream);
+             void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
  * attn_blockmask_build - HOST-side canonicaliser of block-sparse metadata.
@@ -128,17 +141,20 @@ int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* raw_col,
  *                entries outside [0, nqb) are skipped, so malformed metadata
  *                cannot make the kernel read out of bounds.
  *   meta_heads : 1 (one pattern for every (b,h)) or H (pattern h for head h).
+ *   workspace, workspace_bytes : as for attn_fwd.
  * Source: "Exact Blocks, Rings, and Sparsity", section 5 (the outer loop runs
  * over b in C_a; skipped tiles skip their loads and both products) and
  * section 6 (drop-and-renormalize); "block-sparse attention patterns"
  * (triangular element mask inside diagonal blocks, empty rows).
- * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY (workspace too
+ * small), ATTN_EHIP.
  */
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
                          int causal, int64_t block,
                          const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
-                         int64_t nnz, int64_t meta_heads, hipStream_t stream);
+                         int64_t nnz, int64_t meta_heads, void* workspace, int64_t workspace_bytes,
+                         hipStream_t stream);
 
 #ifdef __cplusplus
 }

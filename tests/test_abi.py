@@ -18,6 +18,7 @@ HEADER = os.path.join(ROOT, "include", "bsattn.h")
 @pytest.fixture(scope="module")
 def m():
     import block_sparse_softmax_attn_amd as m
+    m._get_lib()      # loads now: a missing library fails here, loudly
     return m
 
 
@@ -54,29 +55,45 @@ FAKE = 1 << 20   # 16-aligned, never dereferenced: every call below fails valida
     (dict(causal=2), -1),
     (dict(q=FAKE + 2), -1),
     (dict(N=1 << 31), -1),
+    (dict(ws_bytes=100), -3), (dict(ws=0), -1), (dict(ws=FAKE + 8), -1),
 ])
 def test_attn_fwd_rejects_bad_arguments(m, args, expect):
-    from block_sparse_softmax_attn_amd._lib import lib
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, dtype=1, scale=0.125, causal=0)
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, dtype=1, scale=0.125, causal=0,
+             ws=FAKE, ws_bytes=1 << 20)
     a.update(args)
     st = lib.attn_fwd(a["q"] or None, a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
-                      a["dtype"], ctypes.c_float(a["scale"]), a["causal"], None)
+                      a["dtype"], ctypes.c_float(a["scale"]), a["causal"], a["ws"] or None, a["ws_bytes"], None)
     assert st == expect
 
 
 @pytest.mark.parametrize("args,expect", [
     (dict(block=32), -2), (dict(block=0), -2),
     (dict(meta_heads=3), -1), (dict(row_ptr=0), -1), (dict(nnz=-1), -1), (dict(nnz=4, col=0), -1),
-    (dict(d=80), -2),
+    (dict(d=80), -2), (dict(ws_bytes=4096), -3),
 ])
 def test_attn_fwd_blocksparse_rejects_bad_arguments(m, args, expect):
-    from block_sparse_softmax_attn_amd._lib import lib
-    a = dict(d=64, block=128, row_ptr=FAKE, col=FAKE, flags=FAKE, nnz=4, meta_heads=1)
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    a = dict(d=64, block=128, row_ptr=FAKE, col=FAKE, flags=FAKE, nnz=4, meta_heads=1, ws_bytes=1 << 20)
     a.update(args)
     st = lib.attn_fwd_blocksparse(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, a["d"], 1, ctypes.c_float(0.1), 1,
                                   a["block"], a["row_ptr"] or None, a["col"] or None, a["flags"], a["nnz"],
-                                  a["meta_heads"], None)
+                                  a["meta_heads"], FAKE, a["ws_bytes"], None)
     assert st == expect
+
+
+def test_workspace_bytes(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    assert lib.attn_fwd_workspace_bytes(1, 32, 8192, 128, 1) == 32 * 128 * 8192 * 2
+    assert lib.attn_fwd_workspace_bytes(1, 16, 16300, 128, 1) == 16 * 128 * 16384 * 2
+    assert lib.attn_fwd_workspace_bytes(2, 3, 1, 64, 1) == 6 * 64 * 128 * 2
+    assert lib.attn_fwd_workspace_bytes(1, 1, 256, 64, 0) == 0
+    assert lib.attn_fwd_workspace_bytes(1, 1, 256, 96, 1) == -1
+    assert lib.attn_fwd_workspace_bytes(0, 1, 256, 64, 1) == -1
+    assert m.workspace_bytes(1, 2, 300, 128, 1) == 2 * 128 * 384 * 2
 
 
 def _check_builder(m, rows, meta_heads, N, block, causal):
@@ -127,7 +144,8 @@ def test_builder_errors(m):
 
 
 def test_builder_capacity_error(m):
-    from block_sparse_softmax_attn_amd._lib import lib, ATTN_ECAPACITY
+    from block_sparse_softmax_attn_amd._lib import ATTN_ECAPACITY, get
+    lib = get()
     rp, col = workloads.lists_to_csr([[1, 0], [1, 1, 0]])
     out_rp = np.zeros(3, np.int32)
     out_col = np.zeros(2, np.int32)
