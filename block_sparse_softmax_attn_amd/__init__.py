@@ -26,7 +26,8 @@ import numpy as np
 from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN_FLAG_PARTIAL, ATTN_OK,
                    AttnError, LIB_PATH, check, get as _get_lib, status_string)
 
-__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "BlockMask", "AttnError", "LIB_PATH",
+__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "prepare_v", "attn_fwd_prepared",
+           "attn_fwd_blocksparse_prepared", "BlockMask", "AttnError", "LIB_PATH",
            "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
 
 
@@ -184,4 +185,56 @@ def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None
                                       mask.meta_heads, ws.data_ptr() if ws is not None else None, ws_bytes,
                                       _stream(q.device))
     check("attn_fwd_blocksparse", st)
+    return out, lse
+
+
+def prepare_v(v, workspace=None):
+    """bf16 only: V transposed into a workspace for attn_fwd_prepared /
+    attn_fwd_blocksparse_prepared (returns the workspace)."""
+    import torch
+    if v.dim() != 4 or not v.is_cuda or not v.is_contiguous() or v.dtype != torch.bfloat16:
+        raise ValueError("v must be a contiguous bfloat16 [B, H, N, d] tensor on a GPU")
+    B, H, N, d = v.shape
+    ws, ws_bytes = _workspace(v, workspace)
+    with torch.cuda.device(v.device):
+        st = _get_lib().attn_prepare_v(v.data_ptr(), B, H, N, d, ATTN_BF16, ws.data_ptr(), ws_bytes, _stream(v.device))
+    check("attn_prepare_v", st)
+    return ws
+
+
+def attn_fwd_prepared(q, k, workspace, scale: Optional[float] = None, causal: bool = False, out=None, lse=None):
+    """attn_fwd with V taken from a workspace filled by prepare_v (bf16)."""
+    import torch
+    _check_qkv(q, k, k)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    ws, ws_bytes = _workspace(q, workspace)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_fwd_prepared(q.data_ptr(), k.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
+                                          _dtype_code(q), ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(),
+                                          ws_bytes, _stream(q.device))
+    check("attn_fwd_prepared", st)
+    return out, lse
+
+
+def attn_fwd_blocksparse_prepared(q, k, workspace, mask: BlockMask, scale: Optional[float] = None,
+                                  causal: Optional[bool] = None, out=None, lse=None):
+    """attn_fwd_blocksparse with V taken from a workspace filled by prepare_v (bf16)."""
+    import torch
+    _check_qkv(q, k, k)
+    B, H, N, d = q.shape
+    if mask.N != N:
+        raise ValueError(f"mask was built for N={mask.N}, inputs have N={N}")
+    causal = mask.causal if causal is None else bool(causal)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    row_ptr, col, flags = mask.to_device(q.device)
+    ws, ws_bytes = _workspace(q, workspace)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_fwd_blocksparse_prepared(
+            q.data_ptr(), k.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, _dtype_code(q),
+            ctypes.c_float(scale), int(causal), mask.block, row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(),
+            mask.nnz, mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
+    check("attn_fwd_blocksparse_prepared", st)
     return out, lse

@@ -22,7 +22,7 @@ ATTN_FLAG_DIAGONAL = 1
 ATTN_FLAG_PARTIAL = 2
 
 EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_blockmask_build",
-            "attn_fwd_blocksparse")
+            "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared")
 
 
 class AttnError(RuntimeError):
@@ -48,6 +48,13 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd_blocksparse.restype = i32
     lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
                                          vp, vp, vp, i64, i64, vp, i64, vp]
+    lib.attn_prepare_v.restype = i32
+    lib.attn_prepare_v.argtypes = [vp, i64, i64, i64, i64, i32, vp, i64, vp]
+    lib.attn_fwd_prepared.restype = i32
+    lib.attn_fwd_prepared.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
+    lib.attn_fwd_blocksparse_prepared.restype = i32
+    lib.attn_fwd_blocksparse_prepared.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
+                                                  vp, vp, vp, i64, i64, vp, i64, vp]
     return lib
 
 

@@ -61,18 +61,52 @@ int check_workspace(void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t N,
     return ATTN_OK;
 }
 
-// bf16: V^T into the workspace, then the fused kernel, both on `stream`.
-int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, hipStream_t stream) {
-    hipError_t e;
+// bf16: V^T into the workspace (unless the caller prepared it), then the
+// fused kernel, both on `stream`.
+int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, bool prepared, hipStream_t stream) {
+    hipError_t e = hipSuccess;
     if (dtype == ATTN_BF16) {
         a.vt = ws;
         a.npad = static_cast<int>(bsattn::vt_padded_keys(a.N));
-        e = bsattn::launch_v_transpose(a, stream);
+        if (!prepared) e = bsattn::launch_v_transpose(a, stream);
         if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, mode, stream);
     } else {
         e = bsattn::launch_fwd_f32(a, mode, stream);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+int fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+              int64_t d, int dtype, float scale, int causal, void* workspace, int64_t ws_bytes, bool prepared,
+              hipStream_t stream) {
+    int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    st = check_workspace(workspace, ws_bytes, B, H, N, d, dtype);
+    if (st != ATTN_OK) return st;
+    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, workspace, prepared, stream);
+}
+
+int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+               int64_t d, int dtype, float scale, int causal, int64_t block, const int32_t* row_ptr,
+               const int32_t* col, const uint8_t* flags, int64_t nnz, int64_t meta_heads, void* workspace,
+               int64_t ws_bytes, bool prepared, hipStream_t stream) {
+    int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
+    if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
+    if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
+    if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
+    st = check_workspace(workspace, ws_bytes, B, H, N, d, dtype);
+    if (st != ATTN_OK) return st;
+    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    a.row_ptr = row_ptr;
+    a.col = col;
+    a.flags = flags;
+    a.nnz = nnz;
+    a.meta_heads = static_cast<int>(meta_heads);
+    a.block = static_cast<int>(block);
+    return run(a, dtype, bsattn::Mode::kSparse, workspace, prepared, stream);
 }
 
 }  // namespace
@@ -98,12 +132,8 @@ extern "C" int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                         int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
                         int64_t workspace_bytes_given, hipStream_t stream) {
-    int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
-    if (st != ATTN_OK) return st;
-    st = check_workspace(workspace, workspace_bytes_given, B, H, N, d, dtype);
-    if (st != ATTN_OK) return st;
-    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
-    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, workspace, stream);
+    return fwd_dense(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, workspace, workspace_bytes_given, false,
+                     stream);
 }
 
 extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -111,20 +141,43 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
                                     int64_t block, const int32_t* row_ptr, const int32_t* col,
                                     const uint8_t* flags, int64_t nnz, int64_t meta_heads, void* workspace,
                                     int64_t workspace_bytes_given, hipStream_t stream) {
-    int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
+    return fwd_sparse(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
+                      meta_heads, workspace, workspace_bytes_given, false, stream);
+}
+
+extern "C" int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* workspace,
+                              int64_t workspace_bytes_given, hipStream_t stream) {
+    if (!v) return ATTN_EINVAL;
+    if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    const int64_t need = attn_fwd_workspace_bytes(B, H, N, d, dtype);
+    if (need < 0) return (d != 64 && d != 128) ? ATTN_EUNSUPPORTED : ATTN_EINVAL;
+    if (!aligned16(v)) return ATTN_EINVAL;
+    const int st = check_workspace(workspace, workspace_bytes_given, B, H, N, d, dtype);
     if (st != ATTN_OK) return st;
-    if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
-    if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
-    if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
-    if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
-    st = check_workspace(workspace, workspace_bytes_given, B, H, N, d, dtype);
-    if (st != ATTN_OK) return st;
-    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
-    a.row_ptr = row_ptr;
-    a.col = col;
-    a.flags = flags;
-    a.nnz = nnz;
-    a.meta_heads = static_cast<int>(meta_heads);
-    a.block = static_cast<int>(block);
-    return run(a, dtype, bsattn::Mode::kSparse, workspace, stream);
+    bsattn::FwdArgs a{};
+    a.v = v;
+    a.vt = workspace;
+    a.BH = B * H;
+    a.N = static_cast<int>(N);
+    a.d = static_cast<int>(d);
+    a.npad = static_cast<int>(bsattn::vt_padded_keys(N));
+    return bsattn::launch_v_transpose(a, stream) == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+extern "C" int attn_fwd_prepared(const void* q, const void* k, void* o, float* lse, int64_t B, int64_t H, int64_t N,
+                                 int64_t d, int dtype, float scale, int causal, const void* workspace,
+                                 int64_t workspace_bytes_given, hipStream_t stream) {
+    if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    return fwd_dense(q, k, nullptr, o, lse, B, H, N, d, dtype, scale, causal, const_cast<void*>(workspace),
+                     workspace_bytes_given, true, stream);
+}
+
+extern "C" int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* lse, int64_t B, int64_t H,
+                                             int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
+                                             const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
+                                             int64_t nnz, int64_t meta_heads, const void* workspace,
+                                             int64_t workspace_bytes_given, hipStream_t stream) {
+    if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    return fwd_sparse(q, k, nullptr, o, lse, B, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
+                      meta_heads, const_cast<void*>(workspace), workspace_bytes_given, true, stream);
 }

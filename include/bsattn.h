@@ -121,7 +121,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * attention patterns" (duplicates count once, partial blocks, report logical
  * allowed pairs next to executed tile work).
  * Errors: ATTN_EINVAL, ATTN_ECAPACITY (row_ptr, nnz and the counts are still
- * written; col/flags are not).
+ * written; col/flags hold only the first `capacity` entries).
  */
 int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* raw_col,
                          int64_t meta_heads, int64_t N, int64_t block, int causal,
@@ -155,6 +155,38 @@ int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, f
                          const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
                          int64_t nnz, int64_t meta_heads, void* workspace, int64_t workspace_bytes,
                          hipStream_t stream);
+
+/*
+ * Two-step form of the bf16 path, for callers that run several forwards
+ * against the same V (or that time the fused kernel on its own):
+ *
+ * attn_prepare_v - write V transposed per head into `workspace` (the layout
+ *   the fused kernel reads: [B*H][d][ceil(N/128)*128] bf16, keys permuted
+ *   inside each 16-key group, keys >= N zero).
+ *   v : device [B,H,N,d] bf16.  workspace : as for attn_fwd.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype other than ATTN_BF16, d),
+ *   ATTN_ECAPACITY, ATTN_EHIP.
+ *
+ * attn_fwd_prepared / attn_fwd_blocksparse_prepared - attn_fwd /
+ *   attn_fwd_blocksparse without the V argument: V is read from a workspace
+ *   that attn_prepare_v filled for the same B, H, N, d (ATTN_BF16 only).
+ *   attn_fwd(...) is attn_prepare_v(...) followed by attn_fwd_prepared(...)
+ *   on the same stream.
+ * Source: as for attn_fwd and attn_fwd_blocksparse.
+ */
+int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                   void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+int attn_fwd_prepared(const void* q, const void* k, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
+                      const void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* lse,
+                                  int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
+                                  int causal, int64_t block,
+                                  const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
+                                  int64_t nnz, int64_t meta_heads, const void* workspace,
+                                  int64_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

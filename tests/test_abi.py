@@ -84,6 +84,28 @@ def test_attn_fwd_blocksparse_rejects_bad_arguments(m, args, expect):
     assert st == expect
 
 
+def test_prepared_entry_points_reject_bad_arguments(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    f = ctypes.c_float(0.125)
+    # prepare: fp32 has no V^T workspace, null v, bad d, small or misaligned workspace
+    assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 0, FAKE, 1 << 20, None) == -2
+    assert lib.attn_prepare_v(None, 1, 2, 100, 64, 1, FAKE, 1 << 20, None) == -1
+    assert lib.attn_prepare_v(FAKE, 1, 2, 100, 96, 1, FAKE, 1 << 20, None) == -2
+    assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 1, FAKE, 100, None) == -3
+    assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 1, FAKE + 4, 1 << 20, None) == -1
+    assert lib.attn_prepare_v(FAKE, 0, 2, 100, 64, 1, FAKE, 1 << 20, None) == -1
+    # prepared forwards: bf16 only, workspace required
+    assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0, f, 0, FAKE, 1 << 20, None) == -2
+    assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 0, None, 1 << 20, None) == -1
+    assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 0, FAKE, 64, None) == -3
+    assert lib.attn_fwd_prepared(None, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 0, FAKE, 1 << 20, None) == -1
+    assert lib.attn_fwd_blocksparse_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 1, 32, FAKE, FAKE, FAKE,
+                                             4, 1, FAKE, 1 << 20, None) == -2
+    assert lib.attn_fwd_blocksparse_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 1, 64, None, FAKE, FAKE,
+                                             4, 1, FAKE, 1 << 20, None) == -1
+
+
 def test_workspace_bytes(m):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()

@@ -220,3 +220,29 @@ def test_causal_row_zero_equals_v0(lib):
     o, _ = lib.attn_fwd(q, k, v, causal=True)
     torch.cuda.synchronize()
     assert torch.equal(o[:, :, 0], v[:, :, 0])
+
+
+def test_prepared_v_path_is_bitwise_equal(lib):
+    B, H, N, d = 1, 3, 517, 128
+    q, k, v = (t.cuda() for t in inputs(B, H, N, d, "bf16", 84))
+    for causal in (False, True):
+        ref = lib.attn_fwd(q, k, v, causal=causal)
+        ws = lib.prepare_v(v)
+        got = lib.attn_fwd_prepared(q, k, ws, causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+    nqb = -(-N // 128)
+    rng = workloads.SplitMix64(85)
+    rp, col = workloads.lists_to_csr(workloads.random_lists(nqb, nqb, rng, max_len=nqb, empty_prob_per_mille=200))
+    mask = lib.blockmask_build(rp, col, 1, N, 128, True)
+    ref = lib.attn_fwd_blocksparse(q, k, v, mask)
+    got = lib.attn_fwd_blocksparse_prepared(q, k, lib.prepare_v(v), mask)
+    torch.cuda.synchronize()
+    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+
+
+def test_workspace_too_small_is_rejected(lib):
+    q, k, v = (t.cuda() for t in inputs(1, 1, 64, 64, "bf16", 86))
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        lib.attn_fwd(q, k, v, workspace=small)
