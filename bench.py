@@ -3,10 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
 A step is one pass of the hot path over one batch of synthetic N(0,1) bf16
-input already resident in HBM: host validation and launch of the V transpose
-into the workspace, then of the fused kernel (exactly the two launches
-attn_fwd makes, issued through the two-step entry points so each is timed).  The default workload is the dense non-causal d=128 case (B=1 H=32
-N=8192), the one the throughput target is stated on.  Prints ONE JSON line:
+input already resident in HBM.  Dense and causal: host validation and launch
+of the V transpose into the workspace, then of the fused kernel (exactly the
+two launches attn_fwd makes, issued through the two-step entry points so each
+is timed).  Block-sparse: the single launch attn_fwd_blocksparse makes (its
+kernel transposes the V tiles it visits itself).  The default workload is the
+dense non-causal d=128 case (B=1 H=32 N=8192), the one the throughput target
+is stated on.  Prints ONE JSON line:
 
   value    allowed-pair TFLOP/s over the K timed steps (4*d flops per allowed
            query-key pair: the QK^T and PV contractions), wall clock between
@@ -165,11 +168,13 @@ def main():
                .to(torch.bfloat16).contiguous() for _ in range(3))
     o = torch.empty_like(q)
     lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
-    ws = torch.empty(attn.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws = None if cfg.sparse else torch.empty(attn.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, torch.bfloat16),
+                                             dtype=torch.uint8, device=dev)
 
-    # One step = the bf16 hot path: V transposed into the workspace, then the
-    # fused kernel (the two launches attn_fwd makes), timed per launch with
-    # HIP events on the launch stream.
+    # One step = the bf16 hot path as the one-call entry point runs it: dense
+    # and causal launch the V transpose into the workspace, then the fused
+    # kernel; block-sparse launches only the fused kernel.  Each launch is
+    # timed with HIP events on the launch stream.
     if cfg.sparse:
         rp, col = workloads.config_block_lists(cfg)
         t0 = time.perf_counter()
@@ -178,14 +183,15 @@ def main():
         pairs = int(mask.allowed_pairs[0]) * cfg.B * cfg.H
         executed = int(mask.executed_tile_pairs[0]) * cfg.B * cfg.H * cfg.block * cfg.block
         mask.to_device(dev)
-        fused = lambda: attn.attn_fwd_blocksparse_prepared(q, k, ws, mask, scale=cfg.scale, causal=cfg.causal,
-                                                           out=o, lse=lse)
+        fused = lambda: attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal,
+                                                  out=o, lse=lse)
+        prepare = lambda: None
     else:
         build_ms = None
         pairs = allowed_pairs_dense(cfg)
         executed = None
         fused = lambda: attn.attn_fwd_prepared(q, k, ws, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
-    prepare = lambda: attn.prepare_v(v, workspace=ws)
+        prepare = lambda: attn.prepare_v(v, workspace=ws)
     flops = 4 * cfg.d * pairs
 
     for _ in range(args.warmup):
@@ -241,7 +247,7 @@ def main():
             "traffic": read_traffic(args.workload),
             "kernel": "fwd_bf16_kernel",
             "mean_launch_ms": round(mean_launch_ms, 5),
-            "v_transpose_mean_ms": round(prep_ms, 5),
+            "v_transpose_mean_ms": None if cfg.sparse else round(prep_ms, 5),
         },
     }
     if executed is not None:

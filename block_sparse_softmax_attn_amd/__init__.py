@@ -166,7 +166,7 @@ def blockmask_build(raw_row_ptr, raw_col, meta_heads: int, N: int, block: int, c
 
 
 def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None, causal: Optional[bool] = None,
-                         out=None, lse=None, workspace=None):
+                         out=None, lse=None):
     """Block-sparse attention forward, renormalised over the allowed pairs."""
     import torch
     _check_qkv(q, k, v)
@@ -177,13 +177,11 @@ def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
     row_ptr, col, flags = mask.to_device(q.device)
-    ws, ws_bytes = _workspace(q, workspace)
     with torch.cuda.device(q.device):
         st = _get_lib().attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                       B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(causal), mask.block,
                                       row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz,
-                                      mask.meta_heads, ws.data_ptr() if ws is not None else None, ws_bytes,
-                                      _stream(q.device))
+                                      mask.meta_heads, _stream(q.device))
     check("attn_fwd_blocksparse", st)
     return out, lse
 

@@ -47,7 +47,7 @@ def _load() -> ctypes.CDLL:
     lib.attn_blockmask_build.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
     lib.attn_fwd_blocksparse.restype = i32
     lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
-                                         vp, vp, vp, i64, i64, vp, i64, vp]
+                                         vp, vp, vp, i64, i64, vp]
     lib.attn_prepare_v.restype = i32
     lib.attn_prepare_v.argtypes = [vp, i64, i64, i64, i64, i32, vp, i64, vp]
     lib.attn_fwd_prepared.restype = i32

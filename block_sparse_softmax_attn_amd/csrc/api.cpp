@@ -61,14 +61,19 @@ int check_workspace(void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t N,
     return ATTN_OK;
 }
 
-// bf16: V^T into the workspace (unless the caller prepared it), then the
-// fused kernel, both on `stream`.
+// bf16 dense/causal: V^T into the workspace (unless the caller prepared it),
+// then the fused kernel, both on `stream`.  bf16 block-sparse: the fused kernel
+// alone, reading V^T from the workspace only when the caller prepared it.
 int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, bool prepared, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (dtype == ATTN_BF16) {
         a.vt = ws;
         a.npad = static_cast<int>(bsattn::vt_padded_keys(a.N));
-        if (!prepared) e = bsattn::launch_v_transpose(a, stream);
+        if (mode == bsattn::Mode::kSparse && !prepared) {
+            a.vt = nullptr;   // the sparse kernel transposes the V tiles it loads itself
+        } else if (!prepared) {
+            e = bsattn::launch_v_transpose(a, stream);
+        }
         if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, mode, stream);
     } else {
         e = bsattn::launch_fwd_f32(a, mode, stream);
@@ -91,14 +96,17 @@ int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
                int64_t d, int dtype, float scale, int causal, int64_t block, const int32_t* row_ptr,
                const int32_t* col, const uint8_t* flags, int64_t nnz, int64_t meta_heads, void* workspace,
                int64_t ws_bytes, bool prepared, hipStream_t stream) {
+    // only the prepared form reads a workspace (V^T written by attn_prepare_v)
     int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
     if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
     if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
-    st = check_workspace(workspace, ws_bytes, B, H, N, d, dtype);
-    if (st != ATTN_OK) return st;
+    if (prepared) {
+        st = check_workspace(workspace, ws_bytes, B, H, N, d, dtype);
+        if (st != ATTN_OK) return st;
+    }
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
     a.row_ptr = row_ptr;
     a.col = col;
@@ -139,10 +147,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
 extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                     int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
                                     int64_t block, const int32_t* row_ptr, const int32_t* col,
-                                    const uint8_t* flags, int64_t nnz, int64_t meta_heads, void* workspace,
-                                    int64_t workspace_bytes_given, hipStream_t stream) {
+                                    const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
     return fwd_sparse(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
-                      meta_heads, workspace, workspace_bytes_given, false, stream);
+                      meta_heads, nullptr, 0, false, stream);
 }
 
 extern "C" int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* workspace,

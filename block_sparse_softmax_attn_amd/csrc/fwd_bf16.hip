@@ -41,21 +41,28 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int BN = 64;                 // keys per tile step
 constexpr float kSlack = 8.0f;         // lazy-rescale headroom, base-2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, bool VREG>
 struct Geo {
     static constexpr int NT = 64 * NW;               // threads per workgroup
     static constexpr int BM = 32 * NW;               // query rows per workgroup
     static constexpr int K_BYTES = BN * D * 2;       // K tile: BN rows of D bf16
     static constexpr int V_BYTES = D * BN * 2;       // V^T tile: D rows of BN bf16
     static constexpr int K_PER_W = K_BYTES / 1024 / NW;   // 1 KiB direct-to-LDS loads per wave
-    static constexpr int V_PER_W = V_BYTES / 1024 / NW;
+    static constexpr int V_PER_W = VREG ? 0 : V_BYTES / 1024 / NW;
     static constexpr int PER_W = K_PER_W + V_PER_W;
+    // V staged through registers (VREG): each thread moves 4 keys x 8 dims and
+    // writes them transposed into a padded V^T tile.
+    static constexpr int VS = BN + 8;                     // padded V^T row, bf16
+    static constexpr int V_PAIRS = (BN / 4) * (D / 8);
+    static constexpr int V_PER_T = (V_PAIRS + NT - 1) / NT;
     static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "tile must split over waves");
+    static_assert(!VREG || NS == 2, "register-staged V runs two stages");
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     static_assert((NS - 2) * PER_W < 64, "vmcnt range");
 };
@@ -97,6 +104,14 @@ __device__ __forceinline__ int k_swz(int r, int c) {
 }
 __device__ __forceinline__ int v_swz(int d, int c) { return c ^ ((d >> 1) & 7); }   // V^T rows are 128 bytes
 
+// Slot of the first key of quad kq (keys 4kq..4kq+3 of a tile) in a V^T row:
+// inside each 16-key group, keys {4h..4h+3, 8+4h..8+4h+3} (the ones lane half
+// h holds in its S^T registers) take slots 8h..8h+7.  Same order as the
+// transpose pass writes.
+__device__ __forceinline__ int vt_pos_of_quad(int kq) {
+    return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+}
+
 __device__ __forceinline__ float xor32_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -115,15 +130,18 @@ struct TileDesc {
     int masked;    // any element mask needed (uniform over the workgroup)
 };
 
-template <int D, int NW, int NS, int MODE>
+template <int D, int NW, int NS, int MODE, bool VREG>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
-    using G = Geo<D, NW, NS>;
+    using G = Geo<D, NW, NS, VREG>;
     // One array per stage: distinct objects let the compiler see that a tile in
     // flight never aliases the tile being read.
     constexpr int KB2 = NS > 2 ? G::K_BYTES : 16, KB3 = NS > 3 ? G::K_BYTES : 16;
-    constexpr int VB2 = NS > 2 ? G::V_BYTES : 16, VB3 = NS > 3 ? G::V_BYTES : 16;
+    constexpr int VB0 = VREG ? 16 : G::V_BYTES;
+    constexpr int VB2 = (NS > 2 && !VREG) ? G::V_BYTES : 16, VB3 = (NS > 3 && !VREG) ? G::V_BYTES : 16;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[G::K_BYTES], sK1[G::K_BYTES], sK2[KB2], sK3[KB3];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::V_BYTES], sV1[G::V_BYTES], sV2[VB2], sV3[VB3];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[VB0], sV1[VB0], sV2[VB2], sV3[VB3];
+    // register-staged V: two padded V^T tiles
+    __shared__ __attribute__((aligned(16))) __bf16 sVt[VREG ? 2 : 1][VREG ? D * G::VS : 8];
     unsigned char* const kbuf[4] = {sK0, sK1, sK2, sK3};
     unsigned char* const vbuf[4] = {sV0, sV1, sV2, sV3};
 
@@ -144,6 +162,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
     const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
     const __bf16* Vth = static_cast<const __bf16*>(a.vt) + bh * (int64_t)a.npad * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
 
     // ---- tile schedule ----
     int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0;
@@ -185,7 +204,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // Source offsets of this wave's direct-to-LDS loads: lane i of load g fills
     // bytes [1024 g + 16 i, +16) of the tile, i.e. row r, physical chunk p,
     // with logical chunk swz(r, p) of that row.
-    int k_row[G::K_PER_W], k_col[G::K_PER_W], v_off[G::V_PER_W];
+    int k_row[G::K_PER_W], k_col[G::K_PER_W], v_off[G::V_PER_W > 0 ? G::V_PER_W : 1];
 #pragma unroll
     for (int i = 0; i < G::K_PER_W; ++i) {
         const int byte = (w * G::K_PER_W + i) * 1024 + lane * 16;
@@ -208,6 +227,38 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < G::V_PER_W; ++i)
             dma16(Vth + (int64_t)kb0 + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
+    };
+    u32x4 vreg[VREG ? G::V_PER_T : 1][4];
+    auto load_v = [&](int kb0) {   // VREG: 4 keys x 8 dims per thread into registers
+#pragma unroll
+        for (int u2 = 0; u2 < G::V_PER_T; ++u2) {
+            const int pr = min(tid + u2 * G::NT, G::V_PAIRS - 1);
+            const int kq = pr % (BN / 4), dq = pr / (BN / 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int key = min(kb0 + 4 * kq + r, N - 1);
+                vreg[u2][r] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + dq * 8);
+            }
+        }
+    };
+    auto store_v = [&](__bf16* sV) {   // VREG: per dim, the 4 keys as one 8-byte piece of V^T
+#pragma unroll
+        for (int u2 = 0; u2 < G::V_PER_T; ++u2) {
+            const int pr = tid + u2 * G::NT;
+            if (pr < G::V_PAIRS) {
+                const int kq = pr % (BN / 4), dq = pr / (BN / 4);
+                const int pos = vt_pos_of_quad(kq);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int ww = e >> 1;
+                    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                    u32x2 pk;
+                    pk[0] = __builtin_amdgcn_perm(vreg[u2][1][ww], vreg[u2][0][ww], sel);
+                    pk[1] = __builtin_amdgcn_perm(vreg[u2][3][ww], vreg[u2][2][ww], sel);
+                    *reinterpret_cast<u32x2*>(sV + (dq * 8 + e) * G::VS + pos) = pk;
+                }
+            }
+        }
     };
 
     f32x16 oacc[D / 32];
@@ -232,23 +283,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
             if (s < ntiles) issue_tile(describe(s).kb0, kbuf[s], vbuf[s]);
+        if constexpr (VREG) {
+            load_v(describe(0).kb0);
+            store_v(sVt[0]);
+        }
 
-        // Tile it, in stage buffer u = it % NS: wait for its loads, barrier
-        // (every wave's loads have landed and every wave is done with tile
-        // it-1), refill the buffer of tile it-1 with tile it+NS-1, compute.
-        auto tile = [&](int it, int u) {
-            const int ahead = min(NS - 2, ntiles - 1 - it);   // tiles issued after this one
-            if (ahead >= 2) wait_vmcnt<2 * G::PER_W>();
-            else if (ahead == 1) wait_vmcnt<G::PER_W>();
-            else wait_vmcnt<0>();
-            barrier();
-            const int un = (u + NS - 1) % NS;
-            if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, kbuf[un], vbuf[un]);
-            const TileDesc t = describe(it);
-            if (t.causal && t.kb0 > q0w + 31) return;   // every row of this wave precedes the tile
-            const unsigned char* bK = kbuf[u];
-            const unsigned char* bV = vbuf[u];
-
+        // One tile's math for this wave: scores, masks, online softmax, PV.
+        auto compute = [&](const TileDesc& t, const unsigned char* bK, const unsigned char* bV, const __bf16* bVt) {
             // ---- S^T: lane (l32, hi) gets, in s[c][v], the score of query l32
             // and key kb0 + 32c + 8(v>>2) + 4hi + (v&3) ----
             f32x16 s[BN / 32];
@@ -310,10 +351,35 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
                     const int d = 32 * db + l32;
-                    const bf16x8 vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz(d, 2 * g + hi) * 16);
+                    bf16x8 vf;
+                    if constexpr (VREG)
+                        vf = *reinterpret_cast<const bf16x8*>(bVt + d * G::VS + 16 * g + 8 * hi);
+                    else
+                        vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz(d, 2 * g + hi) * 16);
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g], oacc[db], 0, 0, 0);
                 }
         };
+
+        // Tile it, in stage buffer u = it % NS: wait for its loads, barrier
+        // (every wave's loads have landed and every wave is done with tile
+        // it-1), refill the buffer of tile it-1 with tile it+NS-1, compute.
+        auto tile = [&](int it, int u) {
+            const int ahead = min(NS - 2, ntiles - 1 - it);   // tiles issued after this one
+            if (ahead >= 2) wait_vmcnt<2 * G::PER_W>();
+            else if (ahead == 1) wait_vmcnt<G::PER_W>();
+            else wait_vmcnt<0>();
+            if constexpr (VREG) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): V^T stores done
+            barrier();
+            const int un = (u + NS - 1) % NS;
+            const bool vnext = VREG && it + 1 < ntiles;
+            if (vnext) load_v(describe(it + 1).kb0);
+            if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, kbuf[un], vbuf[un]);
+            const TileDesc t = describe(it);
+            // a wave whose rows all precede the tile skips it (still stages V)
+            if (!(t.causal && t.kb0 > q0w + 31)) compute(t, kbuf[u], vbuf[u], sVt[VREG ? (it & 1) : 0]);
+            if (vnext) store_v(sVt[(it + 1) & 1]);
+        };
+
         for (int base = 0; base < ntiles; base += NS) {
 #pragma unroll
             for (int u = 0; u < NS; ++u)
@@ -376,26 +442,33 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const __bf16* __restri
     }
 }
 
-template <int D, int NW, int NS, int MODE>
+template <int D, int NW, int NS, int MODE, bool VREG = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    using G = Geo<D, NW, NS>;
+    using G = Geo<D, NW, NS, VREG>;
     const int64_t nqt = (a.N + G::BM - 1) / G::BM;
     const int64_t grid = nqt * a.BH;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VREG>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     // dense and causal: 8 waves (256 query rows) share each K/V tile, one
-    // workgroup per CU, 3 tiles in flight; block-sparse: the workgroup is one
-    // query block, two workgroups per CU, 2 tiles in flight.
+    // workgroup per CU, 3 tiles in flight, V^T from the workspace.  Block-
+    // sparse: the workgroup is one query block, two workgroups per CU, 2 tiles
+    // in flight; each V block is reused by only a few query blocks, so unless
+    // the caller prepared V^T (a.vt set) the kernel transposes V tiles itself
+    // instead of paying a transpose pass over all of V.
+    const bool vreg = a.vt == nullptr;
     switch (mode) {
         case Mode::kDense: return launch<D, 8, 3, (int)Mode::kDense>(a, stream);
         case Mode::kCausal: return launch<D, 8, 3, (int)Mode::kCausal>(a, stream);
         case Mode::kSparse:
-            if (a.block == 128) return launch<D, 4, 2, (int)Mode::kSparse>(a, stream);
-            return launch<D, 2, 2, (int)Mode::kSparse>(a, stream);
+            if (a.block == 128)
+                return vreg ? launch<D, 4, 2, (int)Mode::kSparse, true>(a, stream)
+                            : launch<D, 4, 2, (int)Mode::kSparse>(a, stream);
+            return vreg ? launch<D, 2, 2, (int)Mode::kSparse, true>(a, stream)
+                        : launch<D, 2, 2, (int)Mode::kSparse>(a, stream);
     }
     return hipErrorInvalidValue;
 }

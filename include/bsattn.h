@@ -65,10 +65,11 @@ enum {
 const char* attn_status_string(int status);
 
 /*
- * attn_fwd_workspace_bytes - bytes of device workspace attn_fwd and
- * attn_fwd_blocksparse need for these sizes: B*H*d*ceil(N/128)*128*2 for
- * ATTN_BF16 (V transposed per head, in the key order the kernel reads), 0 for
- * ATTN_F32.  Returns -1 for sizes or a dtype the kernels do not accept.
+ * attn_fwd_workspace_bytes - bytes of device workspace that attn_fwd and
+ * attn_prepare_v need for these sizes: B*H*d*ceil(N/128)*128*2 for ATTN_BF16
+ * (V transposed per head, in the key order the kernel reads), 0 for ATTN_F32.
+ * attn_fwd_blocksparse needs none.  Returns -1 for sizes or a dtype the
+ * kernels do not accept.
  */
 int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
 
@@ -141,20 +142,20 @@ int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* raw_col,
  *                entries outside [0, nqb) are skipped, so malformed metadata
  *                cannot make the kernel read out of bounds.
  *   meta_heads : 1 (one pattern for every (b,h)) or H (pattern h for head h).
- *   workspace, workspace_bytes : as for attn_fwd.
+ * No workspace: a key block is visited by only a few query blocks, so the
+ * kernel transposes each V tile it loads on chip rather than in a separate
+ * pass over all of V.
  * Source: "Exact Blocks, Rings, and Sparsity", section 5 (the outer loop runs
  * over b in C_a; skipped tiles skip their loads and both products) and
  * section 6 (drop-and-renormalize); "block-sparse attention patterns"
  * (triangular element mask inside diagonal blocks, empty rows).
- * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY (workspace too
- * small), ATTN_EHIP.
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                          int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
                          int causal, int64_t block,
                          const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
-                         int64_t nnz, int64_t meta_heads, void* workspace, int64_t workspace_bytes,
-                         hipStream_t stream);
+                         int64_t nnz, int64_t meta_heads, hipStream_t stream);
 
 /*
  * Two-step form of the bf16 path, for callers that run several forwards
@@ -171,7 +172,9 @@ int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, f
  *   attn_fwd_blocksparse without the V argument: V is read from a workspace
  *   that attn_prepare_v filled for the same B, H, N, d (ATTN_BF16 only).
  *   attn_fwd(...) is attn_prepare_v(...) followed by attn_fwd_prepared(...)
- *   on the same stream.
+ *   on the same stream; attn_fwd_blocksparse_prepared gives results bitwise
+ *   equal to attn_fwd_blocksparse (same arithmetic in the same order), and
+ *   pays off when several sparse forwards share one V.
  * Source: as for attn_fwd and attn_fwd_blocksparse.
  */
 int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,

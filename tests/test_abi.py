@@ -71,16 +71,16 @@ def test_attn_fwd_rejects_bad_arguments(m, args, expect):
 @pytest.mark.parametrize("args,expect", [
     (dict(block=32), -2), (dict(block=0), -2),
     (dict(meta_heads=3), -1), (dict(row_ptr=0), -1), (dict(nnz=-1), -1), (dict(nnz=4, col=0), -1),
-    (dict(d=80), -2), (dict(ws_bytes=4096), -3),
+    (dict(d=80), -2), (dict(v=0), -1), (dict(lse=FAKE + 4), -1),
 ])
 def test_attn_fwd_blocksparse_rejects_bad_arguments(m, args, expect):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
-    a = dict(d=64, block=128, row_ptr=FAKE, col=FAKE, flags=FAKE, nnz=4, meta_heads=1, ws_bytes=1 << 20)
+    a = dict(d=64, block=128, row_ptr=FAKE, col=FAKE, flags=FAKE, nnz=4, meta_heads=1, v=FAKE, lse=FAKE)
     a.update(args)
-    st = lib.attn_fwd_blocksparse(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, a["d"], 1, ctypes.c_float(0.1), 1,
-                                  a["block"], a["row_ptr"] or None, a["col"] or None, a["flags"], a["nnz"],
-                                  a["meta_heads"], FAKE, a["ws_bytes"], None)
+    st = lib.attn_fwd_blocksparse(FAKE, FAKE, a["v"] or None, FAKE, a["lse"], 1, 2, 256, a["d"], 1,
+                                  ctypes.c_float(0.1), 1, a["block"], a["row_ptr"] or None, a["col"] or None,
+                                  a["flags"], a["nnz"], a["meta_heads"], None)
     assert st == expect
 
 
