@@ -1,4 +1,4 @@
-"""CPU oracle for the fused attention forward (test infrastructure only).
+"""CPU oracle for the fused attention forward and its gradient (test infrastructure only).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import anything from this package.  It shares no code with
@@ -8,10 +8,13 @@ against which the GPU kernels are checked.
 from .attention import (attention_head, attn_fwd, attn_fwd_blocksparse, merge_states,
                         output_stage, scores_stage, softmax_stage, token_mask_block_sparse,
                         token_mask_dense)
+from .backward import (attention_head_bwd, attn_bwd, attn_bwd_blocksparse, probabilities_from_lse,
+                       row_scalar_d, score_gradient)
 from .blockmask import canonical_blockmask
 
 __all__ = [
     "attention_head", "attn_fwd", "attn_fwd_blocksparse", "merge_states", "output_stage",
     "scores_stage", "softmax_stage", "token_mask_block_sparse", "token_mask_dense",
-    "canonical_blockmask",
+    "canonical_blockmask", "attention_head_bwd", "attn_bwd", "attn_bwd_blocksparse",
+    "probabilities_from_lse", "row_scalar_d", "score_gradient",
 ]
