@@ -1,4 +1,4 @@
-"""Fused softmax-attention forward (dense, causal, block-sparse) for AMD MI355X.
+"""Fused softmax attention (dense, causal, block-sparse), forward and backward, for AMD MI355X.
 
 Thin Python layer over the C ABI of ``libbsattn.so``: it checks tensors,
 passes raw device pointers and the current HIP stream, and returns the
@@ -8,11 +8,15 @@ in the gfx950 kernels.
     o, lse = attn_fwd(q, k, v, scale=None, causal=False)
     meta   = blockmask_build(raw_row_ptr, raw_col, meta_heads, N, block, causal)
     o, lse = attn_fwd_blocksparse(q, k, v, meta, causal=True)
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False)
+    dq, dk, dv = attn_bwd_blocksparse(q, k, v, o, lse, do, meta)
 
 Operator ("Exact Blocks, Rings, and Sparsity", sections 1, 2 and 5;
 "block-sparse attention patterns"): O = softmax(scale * Q K^T) V over the
 allowed pairs, LSE = log-sum-exp of the scaled logits (natural log); rows with
-no allowed key give O = 0 and LSE = -inf.
+no allowed key give O = 0 and LSE = -inf.  The backward ("Exact Blocks,
+Rings, and Sparsity", section 3) returns dQ, dK, dV for an upstream gradient
+dO, rebuilding P from LSE (bfloat16 only).
 """
 from __future__ import annotations
 
@@ -27,7 +31,8 @@ from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN
                    AttnError, LIB_PATH, check, get as _get_lib, status_string)
 
 __all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "prepare_v", "attn_fwd_prepared",
-           "attn_fwd_blocksparse_prepared", "BlockMask", "AttnError", "LIB_PATH",
+           "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_blocksparse", "bwd_workspace_bytes",
+           "BlockMask", "AttnError", "LIB_PATH",
            "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
 
 
@@ -140,6 +145,29 @@ class BlockMask:
                                       for x in (self.row_ptr, col, flags))
         return self._device[key]
 
+    def transposed(self):
+        """Host (t_row_ptr, t_col): for each key block, the query blocks that
+        list it, in increasing order (computed once, in the library)."""
+        if "_t" not in self._device:
+            nb = -(-self.N // self.block)
+            t_row_ptr = np.zeros(self.meta_heads * nb + 1, dtype=np.int32)
+            t_col = np.zeros(max(self.nnz, 1), dtype=np.int32)
+            col = self.col if self.col.size else np.zeros(1, np.int32)
+            ptr = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+            st = _get_lib().attn_blockmask_transpose(ptr(self.row_ptr), ptr(col), self.meta_heads, self.N,
+                                                     self.block, ptr(t_row_ptr), ptr(t_col), t_col.size)
+            check("attn_blockmask_transpose", st)
+            self._device["_t"] = (t_row_ptr, t_col)
+        return self._device["_t"]
+
+    def transposed_to_device(self, device):
+        """Device copies of ``transposed()``, cached per device."""
+        import torch
+        key = "_t:" + str(device)
+        if key not in self._device:
+            self._device[key] = tuple(torch.from_numpy(x).to(device) for x in self.transposed())
+        return self._device[key]
+
 
 def blockmask_build(raw_row_ptr, raw_col, meta_heads: int, N: int, block: int, causal: bool) -> BlockMask:
     """Canonicalise raw per-query-block key-block lists (host, in the library)."""
@@ -236,3 +264,78 @@ def attn_fwd_blocksparse_prepared(q, k, workspace, mask: BlockMask, scale: Optio
             mask.nnz, mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
     check("attn_fwd_blocksparse_prepared", st)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    """Device workspace (bytes) the bf16 backward needs for these sizes."""
+    n = int(_get_lib().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d), ATTN_BF16))
+    if n < 0:
+        raise ValueError("sizes not supported by the backward")
+    return n
+
+
+def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace):
+    import torch
+    _check_qkv(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise TypeError("the backward takes bfloat16 tensors")
+    B, H, N, d = q.shape
+    for name, t in (("o", o), ("dout", dout)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype, device and be contiguous")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    grads = []
+    for g in (dq, dk, dv):
+        g = torch.empty_like(q) if g is None else g
+        if g.shape != q.shape or g.dtype != q.dtype or not g.is_contiguous() or g.device != q.device:
+            raise ValueError("gradient outputs must match q in shape, dtype, device and be contiguous")
+        grads.append(g)
+    need = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on q's device")
+    return grads, workspace, workspace.numel() * workspace.element_size()
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = False,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Gradients (dQ, dK, dV) of attn_fwd for the upstream gradient ``dout``;
+    ``o`` and ``lse`` are the forward's outputs for the same inputs (bf16)."""
+    import torch
+    B, H, N, d = q.shape
+    (dq, dk, dv), ws, ws_bytes = _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, ATTN_BF16,
+                                 ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(), ws_bytes, _stream(q.device))
+    check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_blocksparse(q, k, v, o, lse, dout, mask: BlockMask, scale: Optional[float] = None,
+                         causal: Optional[bool] = None, dq=None, dk=None, dv=None, workspace=None):
+    """Gradients of attn_fwd_blocksparse (bf16)."""
+    import torch
+    B, H, N, d = q.shape
+    if mask.N != N:
+        raise ValueError(f"mask was built for N={mask.N}, inputs have N={N}")
+    (dq, dk, dv), ws, ws_bytes = _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    causal = mask.causal if causal is None else bool(causal)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    row_ptr, col, flags = mask.to_device(q.device)
+    t_row_ptr, t_col = mask.transposed_to_device(q.device)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_bwd_blocksparse(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, ATTN_BF16, ctypes.c_float(scale), int(causal),
+            mask.block, row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz, t_row_ptr.data_ptr(),
+            t_col.data_ptr(), mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
+    check("attn_bwd_blocksparse", st)
+    return dq, dk, dv

@@ -22,7 +22,8 @@ ATTN_FLAG_DIAGONAL = 1
 ATTN_FLAG_PARTIAL = 2
 
 EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_blockmask_build",
-            "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared")
+            "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared",
+            "attn_bwd_workspace_bytes", "attn_bwd", "attn_blockmask_transpose", "attn_bwd_blocksparse")
 
 
 class AttnError(RuntimeError):
@@ -55,6 +56,15 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd_blocksparse_prepared.restype = i32
     lib.attn_fwd_blocksparse_prepared.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
                                                   vp, vp, vp, i64, i64, vp, i64, vp]
+    lib.attn_bwd_workspace_bytes.restype = i64
+    lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_bwd.restype = i32
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
+    lib.attn_blockmask_transpose.restype = i32
+    lib.attn_blockmask_transpose.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64]
+    lib.attn_bwd_blocksparse.restype = i32
+    lib.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
+                                         vp, vp, vp, i64, vp, vp, i64, vp, i64, vp]
     return lib
 
 

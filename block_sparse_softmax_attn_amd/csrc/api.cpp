@@ -188,3 +188,94 @@ extern "C" int attn_fwd_blocksparse_prepared(const void* q, const void* k, void*
     return fwd_sparse(q, k, nullptr, o, lse, B, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
                       meta_heads, const_cast<void*>(workspace), workspace_bytes_given, true, stream);
 }
+
+// ---------------------------------------------------------------------------
+// backward (bf16)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
+              int causal, void* ws, int64_t ws_bytes) {
+    int st = check_common(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, N, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (!dout || !dq || !dk || !dv) return ATTN_EINVAL;
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_EINVAL;
+    if (ws_bytes < bsattn::bwd_workspace_bytes(B * H, N, d)) return ATTN_ECAPACITY;
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+bsattn::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                              int64_t d, float scale, int causal, void* ws) {
+    bsattn::BwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.dout = dout;
+    a.lse = lse;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.BH = B * H;
+    a.H = static_cast<int>(H);
+    a.N = static_cast<int>(N);
+    a.d = static_cast<int>(d);
+    a.scale = scale;
+    a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+    a.causal = causal;
+    bsattn::bwd_workspace_carve(a, ws);
+    return a;
+}
+
+}  // namespace
+
+extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128) || dtype != ATTN_BF16) return -1;
+    if (B > (int64_t(1) << 62) / H || B * H > (int64_t(1) << 58) / (8 * d * bsattn::vt_padded_keys(N))) return -1;
+    return bsattn::bwd_workspace_bytes(B * H, N, d);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                        int dtype, float scale, int causal, void* workspace, int64_t workspace_bytes_given,
+                        hipStream_t stream) {
+    const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, scale, causal, workspace,
+                             workspace_bytes_given);
+    if (st != ATTN_OK) return st;
+    bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, workspace);
+    const hipError_t e =
+        bsattn::launch_bwd_bf16(a, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                    const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                                    int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
+                                    const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz,
+                                    const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
+                                    void* workspace, int64_t workspace_bytes_given, hipStream_t stream) {
+    int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, scale, causal, workspace,
+                       workspace_bytes_given);
+    if (st != ATTN_OK) return st;
+    if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
+    if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
+    if (!row_ptr || !t_row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
+    if (nnz > 0 && (!col || !flags || !t_col)) return ATTN_EINVAL;
+    bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, workspace);
+    a.row_ptr = row_ptr;
+    a.col = col;
+    a.flags = flags;
+    a.nnz = nnz;
+    a.t_row_ptr = t_row_ptr;
+    a.t_col = t_col;
+    a.t_nnz = nnz;
+    a.meta_heads = static_cast<int>(meta_heads);
+    a.block = static_cast<int>(block);
+    const hipError_t e = bsattn::launch_bwd_bf16(a, bsattn::Mode::kSparse, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}

@@ -104,3 +104,40 @@ extern "C" int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* r
     if (out > 0 && (!col || !flags)) return ATTN_EINVAL;
     return overflow ? ATTN_ECAPACITY : ATTN_OK;
 }
+
+// Transpose of canonical (or any valid) CSR metadata: for each key block, the
+// query blocks whose lists name it, in increasing order.  The backward's dK/dV
+// pass owns a key block and visits exactly these query blocks ("Exact Blocks,
+// Rings, and Sparsity", section 3: the dK/dV reduction runs over queries).
+extern "C" int attn_blockmask_transpose(const int32_t* row_ptr, const int32_t* col, int64_t meta_heads,
+                                        int64_t N, int64_t block, int32_t* t_row_ptr, int32_t* t_col,
+                                        int64_t capacity) {
+    if (!row_ptr || !t_row_ptr) return ATTN_EINVAL;
+    if (meta_heads < 1 || N < 1 || block < 1 || N > INT32_MAX || meta_heads > INT32_MAX) return ATTN_EINVAL;
+    if (capacity < 0) return ATTN_EINVAL;
+    const int64_t nb = (N + block - 1) / block;
+    const int64_t nrows = meta_heads * nb;
+    if (nrows > INT32_MAX) return ATTN_EINVAL;
+    if (row_ptr[0] != 0) return ATTN_EINVAL;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (row_ptr[r + 1] < row_ptr[r]) return ATTN_EINVAL;
+    const int64_t nnz = row_ptr[nrows];
+    if (nnz > 0 && !col) return ATTN_EINVAL;
+    for (int64_t e = 0; e < nnz; ++e)
+        if (col[e] < 0 || col[e] >= nb) return ATTN_EINVAL;
+    // counts per (meta head, key block), then offsets
+    std::vector<int64_t> fill(static_cast<size_t>(nrows + 1), 0);
+    for (int64_t h = 0; h < meta_heads; ++h)
+        for (int64_t qb = 0; qb < nb; ++qb)
+            for (int64_t e = row_ptr[h * nb + qb]; e < row_ptr[h * nb + qb + 1]; ++e) ++fill[h * nb + col[e] + 1];
+    for (int64_t r = 0; r < nrows; ++r) fill[r + 1] += fill[r];
+    for (int64_t r = 0; r <= nrows; ++r) t_row_ptr[r] = static_cast<int32_t>(fill[r]);
+    if (nnz > capacity) return ATTN_ECAPACITY;
+    if (nnz > 0 && !t_col) return ATTN_EINVAL;
+    // query blocks in increasing order keep every transposed row sorted
+    for (int64_t h = 0; h < meta_heads; ++h)
+        for (int64_t qb = 0; qb < nb; ++qb)
+            for (int64_t e = row_ptr[h * nb + qb]; e < row_ptr[h * nb + qb + 1]; ++e)
+                t_col[fill[h * nb + col[e]]++] = static_cast<int32_t>(qb);
+    return ATTN_OK;
+}

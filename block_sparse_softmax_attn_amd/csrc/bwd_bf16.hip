@@ -1,0 +1,602 @@
+// Attention backward, bf16 inputs, fp32 accumulation, for gfx950 (CDNA4).
+//
+// The method ("Exact Blocks, Rings, and Sparsity", section 3, "FlashAttention
+// Backward: recomputing P"; FlashAttention notes, section 5.3): P is rebuilt
+// tile by tile from Q, K and the saved LSE, dP = dO V^T, dS = P (dP - D) with
+// the per-row scalar D = dO . O from a preprocessing pass, and each tile's
+// contributions to dQ, dK and dV are accumulated on chip; S, P, dP and dS never
+// reach HBM.  The two opposing reductions (dK, dV sum over queries; dQ sums over
+// keys) are split over two kernels, without atomics, the two-traversal choice
+// that section describes:
+//   * dK/dV: a workgroup owns a block of keys (32 per wave, kept in registers
+//     together with their V rows) and streams 64-query tiles of Q, dO, Q^T,
+//     dO^T and the row statistics through LDS;
+//   * dQ: a workgroup owns a block of queries (as in the forward) and streams
+//     64-key tiles of K, V and K^T.
+// Both recompute S and dP for their tiles.
+//
+// gfx950 mapping (ours, not the pages'):
+//   * dK/dV computes S = Q K^T and dP = dO V^T with the keys as the MFMA
+//     columns: a lane holds 16 queries of ONE key, and those registers (P and
+//     dS rounded to bf16) are directly the B operand of dV^T += dO^T P and
+//     dK^T += Q^T dS.  The query order inside each 16-query MFMA step is the
+//     order the transposed tiles are stored in, so every A operand is one
+//     16-byte LDS read.
+//   * dQ computes S^T = K Q^T and dP^T = V dO^T (a lane holds keys of ONE query,
+//     the forward's layout): LSE_i and D_i are lane scalars, and dS^T is the B
+//     operand of dQ^T += K^T dS^T.
+//   * Q^T, K^T and dO^T are written once per call by the forward's V^T
+//     transpose pass (same 16-token permutation).
+//   * Every tile goes from global memory straight into LDS
+//     (global_load_lds_dwordx4) with the forward's XOR swizzles; two tiles in
+//     flight for dK/dV, up to three for dQ.
+//   * Rows without allowed keys, and rows past N, get LSE = +inf in the row
+//     statistics, so exp2(s - lse) = 0 and they contribute nothing.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
+#include "gfx950_util.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int BT = 64;   // tokens per streamed tile: queries (dK/dV) or keys (dQ)
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------------------
+// row statistics: one workgroup per 64-row block (plus one padding block)
+// ---------------------------------------------------------------------------
+
+// stats[bh][blk][0..63]   = LSE_i * log2 e  (+inf: row without keys, or i >= N)
+// stats[bh][blk][64..127] = D_i = dO_i . O_i (0 for i >= N)
+template <int D>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse, float* __restrict__ stats,
+                                                        int N, int nblk) {
+    const int blk = blockIdx.x;
+    const int64_t bh = blockIdx.y;
+    const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
+    const int i = blk * BT + r;
+    float acc = 0.f;
+    if (i < N) {
+        const __bf16* orow = o + (bh * N + i) * (int64_t)D;
+        const __bf16* drow = dout + (bh * N + i) * (int64_t)D;
+#pragma unroll
+        for (int c = part; c < D / 8; c += 4) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(orow + 8 * c);
+            const bf16x8 y = *reinterpret_cast<const bf16x8*>(drow + 8 * c);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)x[e], (float)y[e], acc);
+        }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (part == 0) {
+        float* st = stats + (bh * (nblk + 1) + blk) * 128;
+        float l2 = __builtin_inff();
+        if (i < N) {
+            const float L = lse[bh * N + i];
+            if (L > -__builtin_inff()) l2 = L * kLog2e;
+        }
+        st[r] = l2;
+        st[64 + r] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: key-stationary
+// ---------------------------------------------------------------------------
+
+template <int D, int NW>
+struct DkdvGeo {
+    static constexpr int NT = 64 * NW;
+    static constexpr int BKV = 32 * NW;              // keys per workgroup
+    static constexpr int TB = BT * D * 2;            // bytes of a Q, dO, Q^T or dO^T tile
+    static constexpr int PER_T = TB / 1024 / NW;     // 1 KiB direct-to-LDS loads per wave per tile
+    static_assert(TB % (1024 * NW) == 0, "tile must split over waves");
+    static_assert(4 * PER_T + 1 < 64, "vmcnt range");
+};
+
+template <int D, int NW, int MODE>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
+    using G = DkdvGeo<D, NW>;
+    __shared__ __attribute__((aligned(1024))) unsigned char sQ0[G::TB], sQ1[G::TB], sO0[G::TB], sO1[G::TB];
+    __shared__ __attribute__((aligned(1024))) unsigned char sQT0[G::TB], sQT1[G::TB], sOT0[G::TB], sOT1[G::TB];
+    __shared__ __attribute__((aligned(1024))) float sS0[NW][256], sS1[NW][256];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int N = a.N;
+    const int nkt = (N + G::BKV - 1) / G::BKV;
+    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nkt * a.BH);
+    const int64_t bh = ord / nkt;
+    const int kt = (int)(ord % nkt);   // causal: the first key tiles see the most queries and start first
+    const int kb0 = kt * G::BKV;
+    const int kw0 = kb0 + 32 * w;      // this wave's first key
+    const int kj = kw0 + l32;          // this lane's key
+    const int nblk = a.npad / BT;
+    const bool causal = MODE == (int)Mode::kCausal || (MODE == (int)Mode::kSparse && a.causal);
+
+    const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
+    const __bf16* dOh = static_cast<const __bf16*>(a.dout) + bh * (int64_t)N * D;
+    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
+    const __bf16* QTh = static_cast<const __bf16*>(a.qt) + bh * (int64_t)a.npad * D;
+    const __bf16* dOTh = static_cast<const __bf16*>(a.dot) + bh * (int64_t)a.npad * D;
+    const float* Sh = a.stats + bh * (int64_t)(nblk + 1) * 128;
+
+    // ---- schedule of 64-query tiles ----
+    int ntiles = 0, first = 0, e0 = 0, subs = 1, nqb_meta = 0;
+    if (MODE == (int)Mode::kDense) {
+        ntiles = (N + BT - 1) / BT;
+    } else if (MODE == (int)Mode::kCausal) {
+        first = kb0 / BT;   // queries before the first key see none of these keys
+        ntiles = (N + BT - 1) / BT - first;
+    } else {
+        subs = a.block / BT;
+        nqb_meta = (N + a.block - 1) / a.block;
+        const int h = (int)(bh % a.H);
+        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + kt;   // BKV == block for sparse launches
+        int lo = a.t_row_ptr[r], hi_ = a.t_row_ptr[r + 1];
+        lo = (int)min<int64_t>(max(lo, 0), a.t_nnz);
+        hi_ = (int)min<int64_t>(max(hi_, lo), a.t_nnz);
+        e0 = lo;
+        ntiles = (hi_ - lo) * subs;
+    }
+    // first query of tile it; -1 for an out-of-range metadata entry
+    auto tile_q0 = [&](int it) -> int {
+        if (MODE != (int)Mode::kSparse) return (first + it) * BT;
+        const int qb = a.t_col[e0 + it / subs];
+        return (qb >= 0 && qb < nqb_meta) ? qb * a.block + (it % subs) * BT : -1;
+    };
+
+    // Direct-to-LDS sources: load i of this wave fills bytes [1024 (w PER_T + i)
+    // + 16 lane, +16) of a tile.  Row-major tiles: row r, physical chunk p
+    // holds logical chunk k_swz(r, p); transposed tiles: row d (128 bytes),
+    // physical chunk p holds logical chunk v_swz(d, p).
+    int rm_row[G::PER_T], rm_col[G::PER_T], tr_off[G::PER_T];
+#pragma unroll
+    for (int i = 0; i < G::PER_T; ++i) {
+        const int byte = (w * G::PER_T + i) * 1024 + lane * 16;
+        const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
+        rm_row[i] = r;
+        rm_col[i] = k_swz<D>(r, p) * 8;
+        const int d = byte / (2 * BT), p2 = (byte % (2 * BT)) / 16;
+        tr_off[i] = d * a.npad + v_swz(d, p2) * 8;
+    }
+    auto issue = [&](int q0, int u) {
+        unsigned char* dQ = u ? sQ1 : sQ0;
+        unsigned char* dO = u ? sO1 : sO0;
+        unsigned char* dQT = u ? sQT1 : sQT0;
+        unsigned char* dOT = u ? sOT1 : sOT0;
+        q0 = max(q0, 0);
+#pragma unroll
+        for (int i = 0; i < G::PER_T; ++i) {
+            const int row = min(q0 + rm_row[i], N - 1);
+            const int off = (w * G::PER_T + i) * 1024;
+            dma16(Qh + (int64_t)row * D + rm_col[i], dQ + off);
+            dma16(dOh + (int64_t)row * D + rm_col[i], dO + off);
+            dma16(QTh + q0 + tr_off[i], dQT + off);
+            dma16(dOTh + q0 + tr_off[i], dOT + off);
+        }
+        // row statistics of this block (lanes 0-31) and of the next (32-63)
+        dma16(Sh + (q0 / BT) * 128 + lane * 4, u ? sS1[w] : sS0[w]);
+    };
+
+    // this lane's key and value rows: B operands of S = Q K^T and dP = dO V^T
+    bf16x8 kf[D / 16], vf[D / 16];
+    {
+        const int row = min(kj, N - 1);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            kf[k] = *reinterpret_cast<const bf16x8*>(Kh + (int64_t)row * D + 16 * k + 8 * hi);
+            vf[k] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)row * D + 16 * k + 8 * hi);
+        }
+    }
+    wait_vmcnt<0>();
+
+    f32x16 dkacc[D / 32], dvacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+        dkacc[i] = f32x16{};
+        dvacc[i] = f32x16{};
+    }
+    const float sl2 = a.scale_log2;
+
+    auto compute = [&](int q0, int u) {
+        const unsigned char* bQ = u ? sQ1 : sQ0;
+        const unsigned char* bO = u ? sO1 : sO0;
+        const unsigned char* bQT = u ? sQT1 : sQT0;
+        const unsigned char* bOT = u ? sOT1 : sOT0;
+        const float* st = u ? sS1[w] : sS0[w];
+#pragma unroll
+        for (int qc = 0; qc < BT / 32; ++qc) {
+            const int qb0 = q0 + 32 * qc;
+            if (causal && qb0 + 31 < kw0) continue;   // all 32 queries precede all keys of this wave
+            const bool cmask = causal && qb0 < kw0 + 31;
+            // ---- S and dP, queries as rows: lane (l32, hi) gets query
+            // qb0 + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
+            f32x16 s = f32x16{}, dp = f32x16{};
+            const int r = 32 * qc + l32;
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                const int off = r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16;
+                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(bQ + off);
+                const bf16x8 da = *reinterpret_cast<const bf16x8*>(bO + off);
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[k], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[k], dp, 0, 0, 0);
+            }
+            // ---- P = exp2(s * scale log2 e - lse2), dS = P (dP - D) ----
+            bf16x8 pb[2], dsb[2];
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 l4 = *reinterpret_cast<const float4*>(st + 32 * qc + 8 * g4 + 4 * hi);
+                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 32 * qc + 8 * g4 + 4 * hi);
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int v = 4 * g4 + e;
+                    const int iq = qb0 + 8 * g4 + 4 * hi + e;
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lv[e]));
+                    if (cmask && kj > iq) p = 0.f;
+                    const float ds = p * (dp[v] - dv[e]);
+                    pb[v >> 3][v & 7] = (__bf16)p;
+                    dsb[v >> 3][v & 7] = (__bf16)ds;
+                }
+            }
+            // ---- dV^T += dO^T P, dK^T += Q^T dS over 16-query steps ----
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int g = 2 * qc + t;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int d = 32 * db + l32;
+                    const int off = d * (2 * BT) + v_swz(d, 2 * g + hi) * 16;
+                    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(bOT + off);
+                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(bQT + off);
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[t], dvacc[db], 0, 0, 0);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[t], dkacc[db], 0, 0, 0);
+                }
+            }
+        }
+    };
+
+    // Tile it sits in buffer it & 1: wait for its loads, barrier (every wave's
+    // loads have landed, every wave is done with tile it-1), refill the other
+    // buffer with tile it+1, compute.
+    auto step = [&](int it, int u) {
+        wait_vmcnt<0>();
+        barrier();
+        if (it + 1 < ntiles) issue(tile_q0(it + 1), u ^ 1);
+        const int q0 = tile_q0(it);
+        if (q0 < 0 || q0 >= N) return;
+        if (causal && q0 + BT - 1 < kw0) return;   // the whole tile precedes this wave's keys
+        compute(q0, u);
+    };
+    if (ntiles > 0) issue(tile_q0(0), 0);
+    for (int base = 0; base < ntiles; base += 2) {
+        step(base, 0);
+        if (base + 1 < ntiles) step(base + 1, 1);
+    }
+
+    // ---- epilogue: dK = scale * (Q^T dS)^T, dV = (dO^T P)^T ----
+    if (kj < N) {
+        __bf16* dKr = static_cast<__bf16*>(a.dk) + (bh * N + kj) * (int64_t)D;
+        __bf16* dVr = static_cast<__bf16*>(a.dv) + (bh * N + kj) * (int64_t)D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 kv, vv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    kv[i] = (__bf16)(dkacc[db][4 * j + i] * a.scale);
+                    vv[i] = (__bf16)dvacc[db][4 * j + i];
+                }
+                *reinterpret_cast<bf16x4*>(dKr + 32 * db + 8 * j + 4 * hi) = kv;
+                *reinterpret_cast<bf16x4*>(dVr + 32 * db + 8 * j + 4 * hi) = vv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dQ: query-stationary
+// ---------------------------------------------------------------------------
+
+template <int D, int NW, int NS>
+struct DqGeo {
+    static constexpr int NT = 64 * NW;
+    static constexpr int BM = 32 * NW;               // queries per workgroup
+    static constexpr int TB = BT * D * 2;            // bytes of a K, V or K^T tile
+    static constexpr int PER_T = TB / 1024 / NW;
+    static constexpr int PER_W = 3 * PER_T;
+    static_assert(TB % (1024 * NW) == 0, "tile must split over waves");
+    static_assert(NS == 2 || NS == 3, "2 or 3 stages");
+    static_assert((NS - 2) * PER_W < 64, "vmcnt range");
+};
+
+struct KeyTile {
+    int kb0;      // first key
+    int nlim;     // keys j >= nlim are masked (N; 0 for an invalid metadata entry)
+    int causal;   // element mask j <= i applies
+    int masked;   // any element mask needed
+};
+
+template <int D, int NW, int NS, int MODE>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
+    using G = DqGeo<D, NW, NS>;
+    constexpr int T2 = NS > 2 ? G::TB : 16;
+    __shared__ __attribute__((aligned(1024))) unsigned char sK0[G::TB], sK1[G::TB], sK2[T2];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::TB], sV1[G::TB], sV2[T2];
+    __shared__ __attribute__((aligned(1024))) unsigned char sKT0[G::TB], sKT1[G::TB], sKT2[T2];
+    unsigned char* const kbuf[3] = {sK0, sK1, sK2};
+    unsigned char* const vbuf[3] = {sV0, sV1, sV2};
+    unsigned char* const tbuf[3] = {sKT0, sKT1, sKT2};
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hi = lane >> 5;
+    const int N = a.N;
+    const int nqt = (N + G::BM - 1) / G::BM;
+    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nqt * a.BH);
+    const int64_t bh = ord / nqt;
+    int qt = (int)(ord % nqt);
+    if (MODE != (int)Mode::kDense) qt = nqt - 1 - qt;   // heaviest query tiles first
+    const int q0 = qt * G::BM;
+    const int q0w = q0 + 32 * w;
+    const int qi = q0w + l32;
+    const int nblk = a.npad / BT;
+
+    const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
+    const __bf16* dOh = static_cast<const __bf16*>(a.dout) + bh * (int64_t)N * D;
+    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
+    const __bf16* KTh = static_cast<const __bf16*>(a.kt) + bh * (int64_t)a.npad * D;
+    const float* Sh = a.stats + bh * (int64_t)(nblk + 1) * 128;
+
+    // ---- schedule of 64-key tiles (the forward's) ----
+    int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0;
+    if (MODE == (int)Mode::kDense) {
+        ntiles = (N + BT - 1) / BT;
+    } else if (MODE == (int)Mode::kCausal) {
+        ntiles = (min(N, q0 + G::BM) + BT - 1) / BT;
+    } else {
+        subs = a.block / BT;
+        nqb_meta = (N + a.block - 1) / a.block;
+        const int h = (int)(bh % a.H);
+        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + qt;   // BM == block for sparse launches
+        int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
+        lo = (int)min<int64_t>(max(lo, 0), a.nnz);
+        hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);
+        e0 = lo;
+        ntiles = (hi_ - lo) * subs;
+    }
+    auto describe = [&](int it) -> KeyTile {
+        KeyTile t;
+        if (MODE == (int)Mode::kSparse) {
+            const int e = e0 + it / subs;
+            const int kb = a.col[e];
+            const bool valid = kb >= 0 && kb < nqb_meta;
+            t.kb0 = valid ? kb * a.block + (it % subs) * BT : 0;
+            t.nlim = valid ? N : 0;
+            t.causal = ((a.flags[e] & 1) != 0) || (a.causal && t.kb0 + BT - 1 > q0);
+        } else {
+            t.kb0 = it * BT;
+            t.nlim = N;
+            t.causal = (MODE == (int)Mode::kCausal) && (t.kb0 + BT - 1 > q0);
+        }
+        t.masked = t.causal || (t.kb0 + BT > t.nlim);
+        return t;
+    };
+
+    int k_row[G::PER_T], k_col[G::PER_T], t_off[G::PER_T];
+#pragma unroll
+    for (int i = 0; i < G::PER_T; ++i) {
+        const int byte = (w * G::PER_T + i) * 1024 + lane * 16;
+        const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
+        k_row[i] = r;
+        k_col[i] = k_swz<D>(r, p) * 8;
+        const int d = byte / (2 * BT), p2 = (byte % (2 * BT)) / 16;
+        t_off[i] = d * a.npad + v_swz(d, p2) * 8;
+    }
+    auto issue = [&](int kb0, int u) {
+#pragma unroll
+        for (int i = 0; i < G::PER_T; ++i) {
+            const int key = min(kb0 + k_row[i], N - 1);
+            const int off = (w * G::PER_T + i) * 1024;
+            dma16(Kh + (int64_t)key * D + k_col[i], kbuf[u] + off);
+            dma16(Vh + (int64_t)key * D + k_col[i], vbuf[u] + off);
+            dma16(KTh + kb0 + t_off[i], tbuf[u] + off);
+        }
+    };
+
+    f32x16 dqacc[D / 32];
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) dqacc[i] = f32x16{};
+    const float sl2 = a.scale_log2;
+
+    if (ntiles > 0) {
+        // this lane's query and dO rows: B operands of S^T = K Q^T, dP^T = V dO^T
+        bf16x8 qf[D / 16], dof[D / 16];
+        {
+            const int row = min(qi, N - 1);
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                qf[k] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)row * D + 16 * k + 8 * hi);
+                dof[k] = *reinterpret_cast<const bf16x8*>(dOh + (int64_t)row * D + 16 * k + 8 * hi);
+            }
+        }
+        float lse2 = __builtin_inff(), dval = 0.f;
+        if (qi < N) {
+            lse2 = Sh[(qi / BT) * 128 + (qi % BT)];
+            dval = Sh[(qi / BT) * 128 + 64 + (qi % BT)];
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s)
+            if (s < ntiles) issue(describe(s).kb0, s);
+
+        auto compute = [&](const KeyTile& t, int u) {
+            const unsigned char* bK = kbuf[u];
+            const unsigned char* bV = vbuf[u];
+            const unsigned char* bT = tbuf[u];
+#pragma unroll
+            for (int c = 0; c < BT / 32; ++c) {
+                // ---- S^T and dP^T: lane (l32, hi) gets key
+                // kb0 + 32c + 8(v>>2) + 4hi + (v&3) of query qi in element v ----
+                f32x16 s = f32x16{}, dp = f32x16{};
+                const int r = 32 * c + l32;
+#pragma unroll
+                for (int k = 0; k < D / 16; ++k) {
+                    const int off = r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16;
+                    const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(bK + off);
+                    const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(bV + off);
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[k], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, dof[k], dp, 0, 0, 0);
+                }
+                bf16x8 dsb[2];
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lse2));
+                    if (t.masked) {
+                        const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
+                        if (j >= t.nlim || (t.causal && j > qi)) p = 0.f;
+                    }
+                    dsb[v >> 3][v & 7] = (__bf16)(p * (dp[v] - dval));
+                }
+                // ---- dQ^T += K^T dS^T over this block's two 16-key steps ----
+#pragma unroll
+                for (int tt = 0; tt < 2; ++tt) {
+                    const int g = 2 * c + tt;
+#pragma unroll
+                    for (int db = 0; db < D / 32; ++db) {
+                        const int d = 32 * db + l32;
+                        const bf16x8 ka =
+                            *reinterpret_cast<const bf16x8*>(bT + d * (2 * BT) + v_swz(d, 2 * g + hi) * 16);
+                        dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsb[tt], dqacc[db], 0, 0, 0);
+                    }
+                }
+            }
+        };
+
+        auto tile = [&](int it, int u) {
+            const int ahead = min(NS - 2, ntiles - 1 - it);
+            if (ahead >= 1) wait_vmcnt<G::PER_W>();
+            else wait_vmcnt<0>();
+            barrier();
+            const int un = (u + NS - 1) % NS;
+            if (it + NS - 1 < ntiles) issue(describe(it + NS - 1).kb0, un);
+            const KeyTile t = describe(it);
+            if (!(t.causal && t.kb0 > q0w + 31)) compute(t, u);
+        };
+        for (int base = 0; base < ntiles; base += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u)
+                if (base + u < ntiles) tile(base + u, u);
+        }
+    }
+
+    // ---- epilogue: dQ = scale * (K^T dS^T)^T ----
+    if (qi < N) {
+        __bf16* dQr = static_cast<__bf16*>(a.dq) + (bh * N + qi) * (int64_t)D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 qv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qv[i] = (__bf16)(dqacc[db][4 * j + i] * a.scale);
+                *reinterpret_cast<bf16x4*>(dQr + 32 * db + 8 * j + 4 * hi) = qv;
+            }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+template <int D, int NW, int MODE>
+hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
+    const int64_t nkt = (a.N + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE>), dim3((unsigned)(nkt * a.BH)), dim3(64 * NW), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D, int NW, int NS, int MODE>
+hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
+    const int64_t nqt = (a.N + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NS, MODE>), dim3((unsigned)(nqt * a.BH)), dim3(64 * NW), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
+    const int nblk = a.npad / BT;
+    hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((unsigned)(nblk + 1), (unsigned)a.BH), dim3(256), 0, stream,
+                       static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), a.lse, a.stats, a.N, nblk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // dK/dV: 4 waves x 32 keys per workgroup (one key block of a sparse
+    // pattern); dQ: the forward's shapes (8 waves and 3 stages dense/causal,
+    // one query block and 2 stages block-sparse).
+    switch (mode) {
+        case Mode::kDense:
+            e = launch_dkdv<D, 4, (int)Mode::kDense>(a, stream);
+            return e != hipSuccess ? e : launch_dq<D, 8, 3, (int)Mode::kDense>(a, stream);
+        case Mode::kCausal:
+            e = launch_dkdv<D, 4, (int)Mode::kCausal>(a, stream);
+            return e != hipSuccess ? e : launch_dq<D, 8, 3, (int)Mode::kCausal>(a, stream);
+        case Mode::kSparse:
+            if (a.block == 128) {
+                e = launch_dkdv<D, 4, (int)Mode::kSparse>(a, stream);
+                return e != hipSuccess ? e : launch_dq<D, 4, 2, (int)Mode::kSparse>(a, stream);
+            }
+            e = launch_dkdv<D, 2, (int)Mode::kSparse>(a, stream);
+            return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int64_t bwd_workspace_bytes(int64_t BH, int64_t N, int64_t d) {
+    const int64_t npad = vt_padded_keys(N);
+    const int64_t tr = BH * d * npad * 2;                    // one transposed tensor
+    const int64_t st = BH * (npad / BT + 1) * 128 * 4;       // row statistics
+    return 3 * tr + st;
+}
+
+void bwd_workspace_carve(BwdArgs& a, void* ws) {
+    const int64_t npad = vt_padded_keys(a.N);
+    const int64_t tr = a.BH * a.d * npad * 2;
+    unsigned char* p = static_cast<unsigned char*>(ws);
+    a.npad = (int)npad;
+    a.qt = p;
+    a.kt = p + tr;
+    a.dot = p + 2 * tr;
+    a.stats = reinterpret_cast<float*>(p + 3 * tr);
+}
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream) {
+    // Q^T, K^T, dO^T through the forward's transpose pass
+    FwdArgs t{};
+    t.BH = a.BH;
+    t.N = a.N;
+    t.d = a.d;
+    t.npad = a.npad;
+    const void* src[3] = {a.q, a.k, a.dout};
+    void* dst[3] = {a.qt, a.kt, a.dot};
+    for (int i = 0; i < 3; ++i) {
+        t.v = src[i];
+        t.vt = dst[i];
+        const hipError_t e = launch_v_transpose(t, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (a.d == 64) return launch_d<64>(a, mode, stream);
+    return launch_d<128>(a, mode, stream);
+}
+
+}  // namespace bsattn

@@ -1,4 +1,4 @@
-// Internal declarations shared by the C-ABI layer and the gfx950 forward kernels.
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -32,6 +32,53 @@ struct FwdArgs {
 };
 
 enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2 };
+
+// Everything a backward launch needs (bf16 path); built and validated by the
+// host layer.
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* o;       // forward output
+    const void* dout;    // upstream gradient dO
+    const float* lse;    // forward LSE (natural log)
+    void* dq;
+    void* dk;
+    void* dv;
+    int64_t BH;
+    int H;
+    int N;
+    int d;
+    float scale;
+    float scale_log2;
+    int causal;
+    // block-sparse schedule: key blocks per query block (dQ) and, transposed,
+    // query blocks per key block (dK, dV)
+    const int32_t* row_ptr;
+    const int32_t* col;
+    const uint8_t* flags;
+    int64_t nnz;
+    const int32_t* t_row_ptr;
+    const int32_t* t_col;
+    int64_t t_nnz;
+    int meta_heads;
+    int block;
+    // workspace: Q^T, K^T, dO^T ([BH][d][npad] bf16, the transposed-tile key
+    // order) and per-row statistics ([BH][npad/64 + 1][2][64] fp32: LSE in
+    // base-2 units, then D = dO . O, for each 64-row block)
+    void* qt;
+    void* kt;
+    void* dot;
+    float* stats;
+    int npad;
+};
+
+// Bytes of backward workspace for B*H heads of N rows and head dim d.
+int64_t bwd_workspace_bytes(int64_t BH, int64_t N, int64_t d);
+// Split a workspace into the BwdArgs pieces (a.BH, a.N, a.d set).
+void bwd_workspace_carve(BwdArgs& a, void* ws);
+// Transposes, row statistics, then the dK/dV and dQ kernels, all on `stream`.
+hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream);
 
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, Mode mode, hipStream_t stream);

@@ -191,6 +191,77 @@ int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* 
                                   int64_t nnz, int64_t meta_heads, const void* workspace,
                                   int64_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Backward pass (gradients of the forward above; ATTN_BF16 only).
+ *
+ * Given the forward's inputs, its outputs O and LSE, and the upstream
+ * gradient dO, the library rebuilds P tile by tile from Q, K and LSE
+ * (P_ij = exp(scale q_i.k_j - LSE_i) on allowed pairs), forms dP = dO V^T and
+ * dS = P (dP - D) with D_i = dO_i . O_i, and accumulates dV = P^T dO,
+ * dK = scale dS^T Q and dQ = scale dS K, never writing S, P, dP or dS to HBM.
+ * Source: "Exact Blocks, Rings, and Sparsity", section 3 ("FlashAttention
+ * Backward: recomputing P": the D_i preprocessing step, the LSE-based
+ * reconstruction of P, the two traversals that own dK/dV and dQ); FlashAttention
+ * notes, section 5.3 (backward recomputation).  Rows without allowed keys
+ * (LSE = -inf) get dQ = 0 and contribute nothing.  The launch sequence is:
+ * transposes of Q, K, dO into the workspace, the row statistics (LSE in base 2
+ * and D), the dK/dV kernel, the dQ kernel, all on `stream`; results are
+ * deterministic (no atomics).
+ *
+ * attn_bwd_workspace_bytes - device workspace attn_bwd and attn_bwd_blocksparse
+ *   need: 3*B*H*d*ceil(N/128)*128*2 + B*H*(ceil(N/128)*2 + 1)*512 bytes.
+ *   Returns -1 for sizes or a dtype the kernels do not accept.
+ *
+ * attn_bwd - gradients of attn_fwd.
+ *   q, k, v  : device [B,H,N,d] bf16, the forward's inputs.
+ *   o, lse   : device, the forward's outputs for the same q, k, v, scale and
+ *              causal flag (O [B,H,N,d] bf16, LSE [B,H,N] fp32).
+ *   dout     : device [B,H,N,d] bf16, the upstream gradient dO.
+ *   dq, dk, dv : device [B,H,N,d] bf16, written (overwritten, not accumulated).
+ *   B, H, N, d, scale, causal : as for attn_fwd; dtype must be ATTN_BF16.
+ *   workspace : device, at least attn_bwd_workspace_bytes(...) bytes, aligned to
+ *              256 bytes, overwritten, not overlapping any tensor argument.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype, d), ATTN_ECAPACITY
+ *   (workspace too small), ATTN_EHIP.
+ */
+int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
+             int causal, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_blockmask_transpose - HOST-side transpose of block-sparse metadata: for
+ *   each key block, the query blocks whose lists name it, in increasing order
+ *   (the dK/dV pass of the backward owns a key block and visits exactly these).
+ *   row_ptr, col : host, CSR as written by attn_blockmask_build ([meta_heads *
+ *                  nb + 1] offsets, nb = ceil(N / block); entries in [0, nb)).
+ *   t_row_ptr    : host [meta_heads * nb + 1], written.
+ *   t_col        : host [capacity], written (nnz = row_ptr[last] entries).
+ *   Errors: ATTN_EINVAL (malformed CSR, null pointers), ATTN_ECAPACITY
+ *   (t_row_ptr is still written).
+ */
+int attn_blockmask_transpose(const int32_t* row_ptr, const int32_t* col, int64_t meta_heads, int64_t N,
+                             int64_t block, int32_t* t_row_ptr, int32_t* t_col, int64_t capacity);
+
+/*
+ * attn_bwd_blocksparse - gradients of attn_fwd_blocksparse.
+ *   Tensor, size and workspace arguments as for attn_bwd; block, row_ptr, col,
+ *   flags, nnz, meta_heads as for attn_fwd_blocksparse (DEVICE copies of the
+ *   canonical metadata); t_row_ptr, t_col: DEVICE copies of
+ *   attn_blockmask_transpose's output for the same metadata (nnz entries).
+ *   Offsets are clamped to nnz and out-of-range entries are skipped, as in the
+ *   forward.  Source: as for attn_bwd, over the active key-block sets of
+ *   "Exact Blocks, Rings, and Sparsity", section 5.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY, ATTN_EHIP.
+ */
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                         int dtype, float scale, int causal, int64_t block,
+                         const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz,
+                         const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
+                         void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

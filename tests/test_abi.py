@@ -178,3 +178,102 @@ def test_builder_capacity_error(m):
     p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
     st = lib.attn_blockmask_build(p(rp), p(col), 1, 16, 8, 0, p(out_rp), p(out_col), p(out_fl), 2, p(nnz), p(al), p(ex))
     assert st == ATTN_ECAPACITY and nnz[0] == 4 and list(out_rp) == [0, 2, 4] and al[0] == 256 and ex[0] == 4
+
+
+# ---------------------------------------------------------------------------
+# backward entry points (argument checks only; no launch without a GPU)
+# ---------------------------------------------------------------------------
+
+def test_bwd_workspace_bytes(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    # three transposed tensors [BH][d][npad] bf16 + row statistics [BH][npad/64 + 1][128] fp32
+    assert lib.attn_bwd_workspace_bytes(1, 32, 8192, 128, 1) == 3 * 32 * 128 * 8192 * 2 + 32 * 129 * 512
+    assert lib.attn_bwd_workspace_bytes(1, 16, 16300, 128, 1) == 3 * 16 * 128 * 16384 * 2 + 16 * 257 * 512
+    assert lib.attn_bwd_workspace_bytes(2, 3, 1, 64, 1) == 3 * 6 * 64 * 128 * 2 + 6 * 3 * 512
+    assert lib.attn_bwd_workspace_bytes(1, 1, 256, 64, 0) == -1          # fp32 backward not provided
+    assert lib.attn_bwd_workspace_bytes(1, 1, 256, 96, 1) == -1
+    assert lib.attn_bwd_workspace_bytes(1, 0, 256, 64, 1) == -1
+    assert m.bwd_workspace_bytes(1, 2, 300, 128) == 3 * 2 * 128 * 384 * 2 + 2 * 7 * 512
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(q=0), -1), (dict(dout=0), -1), (dict(dq=0), -1), (dict(dv=FAKE + 4), -1), (dict(lse=FAKE + 8), -1),
+    (dict(B=0), -1), (dict(N=0), -1), (dict(d=96), -2), (dict(dtype=0), -2), (dict(dtype=5), -2),
+    (dict(scale=0.0), -1), (dict(scale=float("nan")), -1), (dict(causal=3), -1),
+    (dict(ws_bytes=1000), -3), (dict(ws=0), -1), (dict(ws=FAKE + 16), -1),
+])
+def test_attn_bwd_rejects_bad_arguments(m, args, expect):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=2, N=100, d=64,
+             dtype=1, scale=0.125, causal=0, ws=FAKE, ws_bytes=1 << 24)
+    a.update(args)
+    st = lib.attn_bwd(a["q"] or None, a["k"], a["v"], a["o"], a["lse"], a["dout"] or None, a["dq"] or None,
+                      a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["dtype"], ctypes.c_float(a["scale"]),
+                      a["causal"], a["ws"] or None, a["ws_bytes"], None)
+    assert st == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    (dict(block=32), -2), (dict(meta_heads=3), -1), (dict(row_ptr=0), -1), (dict(t_row_ptr=0), -1),
+    (dict(t_col=0), -1), (dict(nnz=-2), -1), (dict(ws_bytes=10), -3),
+])
+def test_attn_bwd_blocksparse_rejects_bad_arguments(m, args, expect):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    a = dict(block=128, row_ptr=FAKE, t_row_ptr=FAKE, t_col=FAKE, nnz=4, meta_heads=1, ws_bytes=1 << 24)
+    a.update(args)
+    st = lib.attn_bwd_blocksparse(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1,
+                                  ctypes.c_float(0.1), 1, a["block"], a["row_ptr"] or None, FAKE, FAKE, a["nnz"],
+                                  a["t_row_ptr"] or None, a["t_col"] or None, a["meta_heads"], FAKE, a["ws_bytes"],
+                                  None)
+    assert st == expect
+
+
+def _transpose_brute(row_ptr, col, meta_heads, nb):
+    lists = [[] for _ in range(meta_heads * nb)]
+    for h in range(meta_heads):
+        for qb in range(nb):
+            for e in range(row_ptr[h * nb + qb], row_ptr[h * nb + qb + 1]):
+                lists[h * nb + int(col[e])].append(qb)
+    return workloads.lists_to_csr(lists)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_blockmask_transpose_matches_brute_force(m, causal):
+    rng = workloads.SplitMix64(303 + causal)
+    for _ in range(40):
+        block = [1, 8, 64, 128][rng.below(4)]
+        N = 1 + rng.below(3000)
+        nb = -(-N // block)
+        if nb > 150:
+            continue
+        mh = 1 + rng.below(3)
+        rows = workloads.random_lists(mh * nb, nb, rng, max_len=min(2 * nb, 30), empty_prob_per_mille=150)
+        rp, col = workloads.lists_to_csr(rows)
+        mask = m.blockmask_build(rp, col, mh, N, block, causal)
+        t_rp, t_col = mask.transposed()
+        ref_rp, ref_col = _transpose_brute(mask.row_ptr, mask.col, mh, nb)
+        assert np.array_equal(t_rp, ref_rp)
+        assert np.array_equal(t_col[:mask.nnz], ref_col)
+        # every transposed row is strictly increasing (canonical rows are unique)
+        for r in range(mh * nb):
+            seg = t_col[t_rp[r]:t_rp[r + 1]]
+            assert np.all(np.diff(seg) > 0)
+
+
+def test_blockmask_transpose_errors(m):
+    from block_sparse_softmax_attn_amd._lib import ATTN_ECAPACITY, get
+    lib = get()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rp = np.array([0, 1, 3], np.int32)
+    col = np.array([0, 0, 1], np.int32)
+    t_rp = np.zeros(3, np.int32)
+    t_col = np.zeros(3, np.int32)
+    assert lib.attn_blockmask_transpose(p(rp), p(col), 1, 16, 8, p(t_rp), p(t_col), 3) == 0
+    assert list(t_rp) == [0, 2, 3] and list(t_col) == [0, 1, 1]
+    assert lib.attn_blockmask_transpose(p(rp), p(col), 1, 16, 8, p(t_rp), p(t_col), 2) == ATTN_ECAPACITY
+    bad = np.array([0, 1, 3], np.int32), np.array([0, 0, 2], np.int32)   # block 2 of 2 blocks
+    assert lib.attn_blockmask_transpose(p(bad[0]), p(bad[1]), 1, 16, 8, p(t_rp), p(t_col), 3) == -1
+    assert lib.attn_blockmask_transpose(None, p(col), 1, 16, 8, p(t_rp), p(t_col), 3) == -1

@@ -103,6 +103,15 @@ def make_qkv(B: int, H: int, N: int, d: int, dtype: str, seed: int, device: str 
     return tuple(out)
 
 
+def make_grad(B: int, H: int, N: int, d: int, seed: int, device: str = "cpu"):
+    """Upstream gradient dO [B,H,N,d] bf16: fp32 N(0,1) from a generator seeded
+    with ``seed + 7919`` (independent of the Q, K, V draw), rounded to bf16."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + 7919)
+    return torch.randn((B, H, N, d), generator=gen, dtype=torch.float32, device=device).to(torch.bfloat16).contiguous()
+
+
 def local_global_random_lists(N: int, block: int, seed: int, band: int = 4, n_global: int = 2,
                               n_random: int = 2, n_empty: int = 4) -> List[List[int]]:
     """Raw per-query-block key-block lists of the local/global/random pattern.
