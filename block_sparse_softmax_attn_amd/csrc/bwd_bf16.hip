@@ -99,7 +99,7 @@ struct DkdvGeo {
 };
 
 template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
     using G = DkdvGeo<D, NW>;
     __shared__ __attribute__((aligned(1024))) unsigned char sQ0[G::TB], sQ1[G::TB], sO0[G::TB], sO1[G::TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sQT0[G::TB], sQT1[G::TB], sOT0[G::TB], sOT1[G::TB];
@@ -205,6 +205,9 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
     const float sl2 = a.scale_log2;
 
+    // One 64-query tile for this wave, as two 32-query blocks.  Each phase
+    // loads all of its LDS operands first, then issues its MFMAs, so the
+    // matrix pipe is not stalled by one LDS round trip per product.
     auto compute = [&](int q0, int u) {
         const unsigned char* bQ = u ? sQ1 : sQ0;
         const unsigned char* bO = u ? sO1 : sO0;
@@ -216,19 +219,35 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
             const int qb0 = q0 + 32 * qc;
             if (causal && qb0 + 31 < kw0) continue;   // all 32 queries precede all keys of this wave
             const bool cmask = causal && qb0 < kw0 + 31;
-            // ---- S and dP, queries as rows: lane (l32, hi) gets query
-            // qb0 + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
-            f32x16 s = f32x16{}, dp = f32x16{};
             const int r = 32 * qc + l32;
+            // ---- S = Q K^T and dP = dO V^T, queries as rows: lane (l32, hi)
+            // gets query qb0 + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
+            bf16x8 fa[D / 16], fb[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) {
                 const int off = r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16;
-                const bf16x8 qa = *reinterpret_cast<const bf16x8*>(bQ + off);
-                const bf16x8 da = *reinterpret_cast<const bf16x8*>(bO + off);
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[k], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[k], dp, 0, 0, 0);
+                fa[k] = *reinterpret_cast<const bf16x8*>(bQ + off);
+                fb[k] = *reinterpret_cast<const bf16x8*>(bO + off);
             }
-            // ---- P = exp2(s * scale log2 e - lse2), dS = P (dP - D) ----
+            f32x16 s = f32x16{}, dp = f32x16{};
+            __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) {
+                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], kf[k], s, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[k], vf[k], dp, 0, 0, 0);
+            }
+            // operands of the dV and dK products, fetched while S and dP run
+            bf16x8 ta[2][D / 32], tb[2][D / 32];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int d = 32 * db + l32;
+                    const int off = d * (2 * BT) + v_swz(d, 2 * (2 * qc + t) + hi) * 16;
+                    ta[t][db] = *reinterpret_cast<const bf16x8*>(bOT + off);
+                    tb[t][db] = *reinterpret_cast<const bf16x8*>(bQT + off);
+                }
+            // ---- P = exp2(s * scale log2 e - lse2) and dS = P (dP - D), bf16 ----
             bf16x8 pb[2], dsb[2];
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
@@ -239,28 +258,21 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g4 + e;
-                    const int iq = qb0 + 8 * g4 + 4 * hi + e;
                     float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lv[e]));
-                    if (cmask && kj > iq) p = 0.f;
-                    const float ds = p * (dp[v] - dv[e]);
-                    pb[v >> 3][v & 7] = (__bf16)p;
-                    dsb[v >> 3][v & 7] = (__bf16)ds;
+                    if (cmask && kj > qb0 + 8 * g4 + 4 * hi + e) p = 0.f;
+                    const __bf16 pr = (__bf16)p;
+                    pb[v >> 3][v & 7] = pr;
+                    dsb[v >> 3][v & 7] = (__bf16)((float)pr * (dp[v] - dv[e]));
                 }
             }
-            // ---- dV^T += dO^T P, dK^T += Q^T dS over 16-query steps ----
+            // ---- dV^T += dO^T P, dK^T += Q^T dS over the two 16-query steps ----
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const int g = 2 * qc + t;
+            for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int d = 32 * db + l32;
-                    const int off = d * (2 * BT) + v_swz(d, 2 * g + hi) * 16;
-                    const bf16x8 ao = *reinterpret_cast<const bf16x8*>(bOT + off);
-                    const bf16x8 aq = *reinterpret_cast<const bf16x8*>(bQT + off);
-                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[t], dvacc[db], 0, 0, 0);
-                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, dsb[t], dkacc[db], 0, 0, 0);
+                    dvacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t][db], pb[t], dvacc[db], 0, 0, 0);
+                    dkacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tb[t][db], dsb[t], dkacc[db], 0, 0, 0);
                 }
-            }
         }
     };
 
