@@ -25,7 +25,10 @@ is stated on.  Prints ONE JSON line:
 Other flags: --no-cpu-baseline, --no-gemm-ceiling (skip the library bf16 GEMM
 that measures the sustained matrix-core rate next to the published peak),
 --copy-calibration (a plain device copy of known size, run under rocprofv3
---pmc to calibrate the byte counters).
+--pmc to calibrate the byte counters), --pass bwd (time the backward instead:
+one step = one attn_bwd / attn_bwd_blocksparse call on the workload's shapes,
+10*d flops per allowed pair for the recomputed S and the dP, dV, dK, dQ
+products; its cpu_baseline is the float64 gradient oracle).
 """
 from __future__ import annotations
 
@@ -141,6 +144,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -162,6 +166,9 @@ def main():
     cfg = workloads.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.which == "bwd":
+        bench_bwd(args, cfg, dev)
+        return
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
     q, k, v = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
@@ -258,6 +265,100 @@ def main():
         rec["roofline"]["measured_bf16_gemm_ceiling"] = gemm_ceiling()
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v)
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline_bwd(cfg, q, k, v, do, mask_lists, budget_s: float = 10.0):
+    """The gradient oracle as it stands, on whole heads, until the budget is spent."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    done, flops, t_total = 0, 0, 0.0
+    for h in range(cfg.H):
+        qh, kh, vh, dh = (t[:, h:h + 1].to("cpu") for t in (q, k, v, do))
+        t0 = time.perf_counter()
+        if mask_lists is None:
+            oracle.attn_bwd(qh, kh, vh, dh, cfg.scale, cfg.causal)
+        else:
+            rp, col, pairs_head = mask_lists
+            oracle.attn_bwd_blocksparse(qh, kh, vh, dh, cfg.scale, cfg.causal, cfg.block, rp, col, 1)
+        t_total += time.perf_counter() - t0
+        done += 1
+        per_head = (mask_lists[2] if mask_lists is not None
+                    else (cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.N))
+        flops += 10 * cfg.d * per_head * cfg.B
+        if t_total >= budget_s:
+            break
+    return {
+        "value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "sample": f"{done} of {cfg.B * cfg.H} (batch, head) pairs of {cfg.name}, float64 numpy gradient oracle "
+                  f"(forward recomputed), {t_total:.1f} s",
+    }
+
+
+def bench_bwd(args, cfg, dev):
+    """One step = one backward call on inputs resident in HBM (forward outputs
+    computed once, untimed)."""
+    import torch
+    import block_sparse_softmax_attn_amd as attn
+    import workloads
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    q, k, v, do = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
+                   .to(torch.bfloat16).contiguous() for _ in range(4))
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(attn.bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.uint8, device=dev)
+    if cfg.sparse:
+        rp, col = workloads.config_block_lists(cfg)
+        mask = attn.blockmask_build(rp, col, 1, cfg.N, cfg.block, cfg.causal)
+        pairs_head = int(mask.allowed_pairs[0])
+        o, lse = attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal)
+        step = lambda: attn.attn_bwd_blocksparse(q, k, v, o, lse, do, mask, scale=cfg.scale, causal=cfg.causal,
+                                                 dq=dq, dk=dk, dv=dv, workspace=ws)
+        mask_lists = (rp, col, pairs_head)
+    else:
+        pairs_head = cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.N
+        o, lse = attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal)
+        step = lambda: attn.attn_bwd(q, k, v, o, lse, do, scale=cfg.scale, causal=cfg.causal,
+                                     dq=dq, dk=dk, dv=dv, workspace=ws)
+        mask_lists = None
+    pairs = pairs_head * cfg.B * cfg.H
+    flops = 10 * cfg.d * pairs
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (mean_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention bwd TFLOP/s (allowed pairs, 10*d flops per pair) + % of bf16 MFMA peak, 1\u00d7MI355X",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {"workload": cfg.description, "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d,
+                   "causal": cfg.causal, "block_sparse": cfg.sparse, "scale": cfg.scale, "seed": cfg.seed,
+                   "allowed_pairs": pairs, "flops_per_step": flops,
+                   "flop_count": "10*d per allowed (query, key) pair: S recomputed, dP, dV, dK, dQ",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bwd call: Q/K/dO transposes, row statistics, dK/dV kernel, dQ kernel",
+                     "mean_call_ms": round(mean_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline_bwd(cfg, q, k, v, do, mask_lists)
     print(json.dumps(rec), flush=True)
 
 
