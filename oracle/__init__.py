@@ -5,9 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 the HIP path: it is the plain definition of the operator, in float64 numpy,
 against which the GPU kernels are checked.
 """
-from .attention import (attention_head, attn_fwd, attn_fwd_blocksparse, merge_states,
-                        output_stage, scores_stage, softmax_stage, token_mask_block_sparse,
-                        token_mask_dense)
+from .attention import (attention_head, attn_fwd, attn_fwd_block, attn_fwd_blocksparse, merge_lse,
+                        merge_states, output_stage, scores_stage, softmax_stage, token_mask_block_sparse,
+                        token_mask_dense, token_mask_offsets)
 from .backward import (attention_head_bwd, attn_bwd, attn_bwd_blocksparse, probabilities_from_lse,
                        row_scalar_d, score_gradient)
 from .blockmask import canonical_blockmask
@@ -16,5 +16,6 @@ __all__ = [
     "attention_head", "attn_fwd", "attn_fwd_blocksparse", "merge_states", "output_stage",
     "scores_stage", "softmax_stage", "token_mask_block_sparse", "token_mask_dense",
     "canonical_blockmask", "attention_head_bwd", "attn_bwd", "attn_bwd_blocksparse",
-    "probabilities_from_lse", "row_scalar_d", "score_gradient",
+    "probabilities_from_lse", "row_scalar_d", "score_gradient", "attn_fwd_block", "merge_lse",
+    "token_mask_offsets",
 ]

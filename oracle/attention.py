@@ -209,3 +209,64 @@ def merge_states(m_a, l_a, a_a, m_b, l_b, a_b):
     l = wa * l_a + wb * l_b
     a = wa[..., None] * a_a + wb[..., None] * a_b
     return m, l, a
+
+
+# ---------------------------------------------------------------------------
+# one ring step: a query block against a key/value block at global positions
+# ---------------------------------------------------------------------------
+
+def token_mask_offsets(n_q: int, n_k: int, causal: bool, q_offset: int, k_offset: int) -> np.ndarray:
+    """allowed[i, j] for query i at global position q_offset + i and key j at
+    global position k_offset + j: every pair, or, when causal, the pairs with
+    k_offset + j <= q_offset + i."""
+    allowed = np.ones((n_q, n_k), dtype=bool)
+    if causal:
+        qpos = q_offset + np.arange(n_q)
+        kpos = k_offset + np.arange(n_k)
+        allowed &= kpos[None, :] <= qpos[:, None]
+    return allowed
+
+
+def attn_fwd_block(q, k, v, scale: float, causal: bool, q_offset: int = 0, k_offset: int = 0):
+    """Partial attention of query rows [B,H,Nq,d] against one key/value block
+    [B,H,Nk,d] whose tokens sit at global positions k_offset + j ("Exact Blocks,
+    Rings, and Sparsity", section 4: device g keeps Q_g and meets one KV block
+    per ring step; a causal step masks the pairs in the future).  Returns the
+    block's normalised output O_b [B,H,Nq,d] and LSE_b [B,H,Nq] (natural log;
+    -inf and O_b = 0 for rows that see no key of the block), the state that
+    ``merge_lse`` combines."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, H, n_q, d = q.shape
+    n_k = k.shape[2]
+    if k.shape != (B, H, n_k, d) or v.shape != k.shape:
+        raise ValueError("K and V must be [B, H, Nk, d] with Q's B, H and d")
+    allowed = token_mask_offsets(n_q, n_k, causal, q_offset, k_offset)
+    o = np.empty((B, H, n_q, d))
+    lse = np.empty((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            s = scores_stage(q[b, h], k[b, h], scale, allowed)
+            p, lse[b, h] = softmax_stage(s)
+            o[b, h] = output_stage(p, v[b, h])
+    return o, lse
+
+
+def merge_lse(o_parts, lse_parts):
+    """Merge normalised partial outputs over disjoint key sets, given in the
+    (O, LSE) form: LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.
+    This is the (m, l, A) merge of ``merge_states`` with A_s = l_s O_s and
+    LSE_s = m_s + ln l_s ("Exact Blocks, Rings, and Sparsity", sections 2 and
+    4).  Parts with LSE = -inf contribute nothing; if every part is empty the
+    result is O = 0 and LSE = -inf.  o_parts [S, ..., d], lse_parts [S, ...]."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = np.max(lse_parts, axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lse_parts - m_safe[None])              # exp(-inf) = 0 for empty parts
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))
+        o = np.where(empty[..., None], 0.0,
+                     np.einsum("s...,s...d->...d", w, o_parts) / np.where(empty, 1.0, tot)[..., None])
+    return o, lse
