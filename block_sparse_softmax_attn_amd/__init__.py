@@ -10,6 +10,9 @@ in the gfx950 kernels.
     o, lse = attn_fwd_blocksparse(q, k, v, meta, causal=True)
     dq, dk, dv = attn_bwd(q, k, v, o, lse, do, causal=False)
     dq, dk, dv = attn_bwd_blocksparse(q, k, v, o, lse, do, meta)
+    o, lse = attn_fwd_splitkv(q, k, v, num_splits=4)
+    o_b, lse_b = attn_fwd_block(q_rows, k_blk, v_blk, q_offset=..., k_offset=...)
+    o, lse = attn_merge(o_parts, lse_parts)
 
 Operator ("Exact Blocks, Rings, and Sparsity", sections 1, 2 and 5;
 "block-sparse attention patterns"): O = softmax(scale * Q K^T) V over the
@@ -32,6 +35,7 @@ from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN
 
 __all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "prepare_v", "attn_fwd_prepared",
            "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_blocksparse", "bwd_workspace_bytes",
+           "attn_fwd_splitkv", "attn_fwd_block", "attn_merge",
            "BlockMask", "AttnError", "LIB_PATH",
            "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
 
@@ -339,3 +343,93 @@ def attn_bwd_blocksparse(q, k, v, o, lse, dout, mask: BlockMask, scale: Optional
             t_col.data_ptr(), mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
     check("attn_bwd_blocksparse", st)
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# key splits, ring steps and the partial-state merge (bf16 inputs)
+# ---------------------------------------------------------------------------
+
+def _ws_buffer(dev, need, workspace, align=256):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if (workspace.device != dev or not workspace.is_contiguous()
+            or workspace.numel() * workspace.element_size() < need or workspace.data_ptr() % align):
+        raise ValueError(f"workspace must be a contiguous, {align}-byte aligned buffer of at least {need} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def attn_fwd_splitkv(q, k, v, scale: Optional[float] = None, causal: bool = False, num_splits: int = 4,
+                     out=None, lse=None, workspace=None):
+    """attn_fwd over ``num_splits`` key ranges launched together, then merged."""
+    import torch
+    _check_qkv(q, k, v)
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _outputs(q, out, lse)
+    need = int(_get_lib().attn_fwd_splitkv_workspace_bytes(B, H, N, d, _dtype_code(q), int(num_splits)))
+    if need < 0:
+        raise ValueError("sizes, dtype or num_splits not supported by the split-key forward")
+    ws, ws_bytes = _ws_buffer(q.device, need, workspace)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                         B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
+                                         int(num_splits), ws.data_ptr(), ws_bytes, _stream(q.device))
+    check("attn_fwd_splitkv", st)
+    return out, lse
+
+
+def attn_fwd_block(q, k, v, scale: Optional[float] = None, causal: bool = False, q_offset: int = 0,
+                   k_offset: int = 0, o_part=None, lse_part=None, workspace=None):
+    """One ring step: fp32 partial state (O_b, LSE_b) of the rows of ``q``
+    (global positions q_offset + i) against the key/value block ``k``, ``v``
+    (global positions k_offset + j)."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda) or len({q.device, k.device, v.device}) != 1:
+        raise ValueError("q, k, v must live on one GPU")
+    if not all(t.dtype == torch.bfloat16 and t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must be contiguous bfloat16")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if o_part is None:
+        o_part = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    if lse_part is None:
+        lse_part = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    need = int(_get_lib().attn_fwd_block_workspace_bytes(B, H, Nk, d, ATTN_BF16))
+    if need < 0:
+        raise ValueError("sizes not supported")
+    ws, ws_bytes = _ws_buffer(q.device, need, workspace, align=16)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_fwd_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                       lse_part.data_ptr(), B, H, Nq, Nk, d, ATTN_BF16, ctypes.c_float(scale),
+                                       int(bool(causal)), int(q_offset), int(k_offset), ws.data_ptr(), ws_bytes,
+                                       _stream(q.device))
+    check("attn_fwd_block", st)
+    return o_part, lse_part
+
+
+def attn_merge(o_parts, lse_parts, out_dtype=None, out=None, lse=None):
+    """Merge partial states: o_parts fp32 [S, B, H, N, d], lse_parts fp32
+    [S, B, H, N] -> (O of out_dtype (float32 default), LSE)."""
+    import torch
+    if o_parts.dim() != 5 or lse_parts.shape != o_parts.shape[:4]:
+        raise ValueError("o_parts must be [S, B, H, N, d] and lse_parts [S, B, H, N]")
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise TypeError("partial states are float32")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()):
+        raise ValueError("partial states must be contiguous")
+    S, B, H, N, d = o_parts.shape
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    code = ATTN_BF16 if out_dtype == torch.bfloat16 else ATTN_F32
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=o_parts.device)
+    with torch.cuda.device(o_parts.device):
+        st = _get_lib().attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), S, B, H, N, d, out.data_ptr(),
+                                   lse.data_ptr(), code, _stream(o_parts.device))
+    check("attn_merge", st)
+    return out, lse

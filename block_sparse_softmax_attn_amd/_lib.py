@@ -23,7 +23,9 @@ ATTN_FLAG_PARTIAL = 2
 
 EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_blockmask_build",
             "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared",
-            "attn_bwd_workspace_bytes", "attn_bwd", "attn_blockmask_transpose", "attn_bwd_blocksparse")
+            "attn_bwd_workspace_bytes", "attn_bwd", "attn_blockmask_transpose", "attn_bwd_blocksparse",
+            "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv", "attn_fwd_block_workspace_bytes",
+            "attn_fwd_block", "attn_merge")
 
 
 class AttnError(RuntimeError):
@@ -65,6 +67,17 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_blocksparse.restype = i32
     lib.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64,
                                          vp, vp, vp, i64, vp, vp, i64, vp, i64, vp]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = i64
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
+    lib.attn_fwd_splitkv.restype = i32
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64, vp, i64, vp]
+    lib.attn_fwd_block_workspace_bytes.restype = i64
+    lib.attn_fwd_block_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_fwd_block.restype = i32
+    lib.attn_fwd_block.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, i64, i64, vp, i64,
+                                   vp]
+    lib.attn_merge.restype = i32
+    lib.attn_merge.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, i32, vp]
     return lib
 
 

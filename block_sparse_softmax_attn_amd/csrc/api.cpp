@@ -279,3 +279,119 @@ extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
     const hipError_t e = bsattn::launch_bwd_bf16(a, bsattn::Mode::kSparse, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
+
+// ---------------------------------------------------------------------------
+// key splits and ring steps (bf16): partial states and their merge
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int64_t kMaxSplits = 64;
+
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// keys per split: whole 64-key tiles, spread as evenly as the tiles allow
+int64_t split_chunk(int64_t N, int64_t splits) {
+    const int64_t tiles = (N + 63) / 64;
+    return (tiles + splits - 1) / splits * 64;
+}
+
+int64_t partial_bytes(int64_t BH, int64_t N, int64_t d, int64_t splits) {
+    return align256(splits * BH * N * d * 4) + align256(splits * BH * N * 4);
+}
+
+}  // namespace
+
+extern "C" int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                                                    int64_t num_splits) {
+    if (dtype != ATTN_BF16 || num_splits < 1 || num_splits > kMaxSplits) return -1;
+    const int64_t vt = attn_fwd_workspace_bytes(B, H, N, d, dtype);
+    if (vt < 0 || B * H > (int64_t(1) << 56) / (N * (d + 1) * 4 * num_splits)) return -1;
+    const int64_t splits = (N + split_chunk(N, num_splits) - 1) / split_chunk(N, num_splits);
+    return align256(vt) + partial_bytes(B * H, N, d, splits);
+}
+
+extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
+                                int64_t num_splits, void* workspace, int64_t workspace_bytes_given,
+                                hipStream_t stream) {
+    int st = check_common(q, k, v, o, lse, B, H, N, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (num_splits < 1 || num_splits > kMaxSplits) return ATTN_EINVAL;
+    const int64_t need = attn_fwd_splitkv_workspace_bytes(B, H, N, d, dtype, num_splits);
+    if (need < 0) return ATTN_EINVAL;
+    if (workspace_bytes_given < need) return ATTN_ECAPACITY;
+    if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_EINVAL;
+    const int64_t chunk = split_chunk(N, num_splits);
+    const int64_t splits = (N + chunk - 1) / chunk;
+    bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    a.vt = ws;
+    a.npad = static_cast<int>(bsattn::vt_padded_keys(N));
+    a.Nk = static_cast<int>(N);
+    a.kv_chunk = static_cast<int>(chunk);
+    a.nsplit = static_cast<int>(splits);
+    a.o_part = reinterpret_cast<float*>(ws + align256(workspace_bytes(B, H, N, d, dtype)));
+    a.lse_part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.o_part) + align256(splits * B * H * N * d * 4));
+    if ((int64_t)((N + 255) / 256) * B * H * splits > INT32_MAX) return ATTN_EINVAL;
+    hipError_t e = bsattn::launch_v_transpose(a, stream);
+    if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, bsattn::Mode::kRange, stream);
+    if (e == hipSuccess)
+        e = bsattn::launch_merge(a.o_part, a.lse_part, a.nsplit, a.BH, a.N, a.d, o, lse, true, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+extern "C" int64_t attn_fwd_block_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, int dtype) {
+    if (dtype != ATTN_BF16) return -1;
+    return attn_fwd_workspace_bytes(B, H, Nk, d, dtype);
+}
+
+extern "C" int attn_fwd_block(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype, float scale,
+                              int causal, int64_t q_offset, int64_t k_offset, void* workspace,
+                              int64_t workspace_bytes_given, hipStream_t stream) {
+    // shapes: Q [B,H,Nq,d]; K, V [B,H,Nk,d]; both sides pass the common checks
+    int st = check_common(q, k, v, o_part, lse_part, B, H, Nq, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    st = check_common(q, k, v, o_part, lse_part, B, H, Nk, d, dtype, scale, causal);
+    if (st != ATTN_OK) return st;
+    if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (q_offset < 0 || k_offset < 0 || q_offset > (int64_t(1) << 40) || k_offset > (int64_t(1) << 40))
+        return ATTN_EINVAL;
+    const int64_t need = attn_fwd_block_workspace_bytes(B, H, Nk, d, dtype);
+    if (need < 0) return ATTN_EINVAL;
+    if (workspace_bytes_given < need) return ATTN_ECAPACITY;
+    if (!workspace || !aligned16(workspace)) return ATTN_EINVAL;
+    bsattn::FwdArgs a = make_args(q, k, v, o_part, lse_part, B, H, Nq, d, scale, causal);
+    a.vt = workspace;
+    a.npad = static_cast<int>(bsattn::vt_padded_keys(Nk));
+    a.Nk = static_cast<int>(Nk);
+    a.q_off = q_offset;
+    a.k_off = k_offset;
+    a.kv_chunk = static_cast<int>(bsattn::vt_padded_keys(Nk));   // one split covers every key
+    a.nsplit = 1;
+    a.o_part = o_part;
+    a.lse_part = lse_part;
+    // the transpose pass reads V with Nk rows
+    bsattn::FwdArgs t = a;
+    t.N = static_cast<int>(Nk);
+    hipError_t e = bsattn::launch_v_transpose(t, stream);
+    if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, bsattn::Mode::kRange, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+extern "C" int attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B, int64_t H,
+                          int64_t N, int64_t d, void* o, float* lse, int out_dtype, hipStream_t stream) {
+    if (!o_parts || !lse_parts || !o || !lse) return ATTN_EINVAL;
+    if (num_parts < 1 || num_parts > 1024 || B < 1 || H < 1 || N < 1 || N > kMaxN) return ATTN_EINVAL;
+    if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+    if (out_dtype != ATTN_F32 && out_dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (B > (int64_t(1) << 40) / H || B * H * N > (int64_t(1) << 40) / (num_parts * d)) return ATTN_EINVAL;
+    if (!aligned16(o_parts) || !aligned16(lse_parts) || !aligned16(o) || !aligned16(lse)) return ATTN_EINVAL;
+    if ((B * H * N + 7) / 8 > INT32_MAX) return ATTN_EINVAL;
+    const hipError_t e = bsattn::launch_merge(o_parts, lse_parts, static_cast<int>(num_parts), B * H,
+                                              static_cast<int>(N), static_cast<int>(d), o, lse,
+                                              out_dtype == ATTN_BF16, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}

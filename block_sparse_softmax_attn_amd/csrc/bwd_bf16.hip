@@ -568,6 +568,7 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
             }
             e = launch_dkdv<D, 2, (int)Mode::kSparse>(a, stream);
             return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse>(a, stream);
+        case Mode::kRange: break;   // no backward for key-range launches
     }
     return hipErrorInvalidValue;
 }

@@ -88,28 +88,47 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
-    const int N = a.N;
+    constexpr bool RANGE = MODE == (int)Mode::kRange;
+    const int N = a.N;                   // query rows
+    const int NK = RANGE ? a.Nk : N;     // keys
     const int nqt = (N + G::BM - 1) / G::BM;
-    const int64_t total = (int64_t)nqt * a.BH;
+    const int nsplit = RANGE ? a.nsplit : 1;
+    const int64_t total = (int64_t)nqt * a.BH * nsplit;
     const int64_t ord = xcd_tile_order(blockIdx.x, total);
-    const int64_t bh = ord / nqt;
+    // the query tiles of one (head, split) are consecutive: they share its K/V
+    const int64_t rest = ord / nqt;
+    const int split = (int)(rest % nsplit);
+    const int64_t bh = rest / nsplit;
     int qt = (int)(ord % nqt);
-    if (MODE != (int)Mode::kDense) qt = nqt - 1 - qt;   // heaviest query tiles first
+    if (MODE == (int)Mode::kCausal || MODE == (int)Mode::kSparse || (RANGE && a.causal))
+        qt = nqt - 1 - qt;   // heaviest query tiles first
     const int q0 = qt * G::BM;
     const int q0w = q0 + 32 * w;
     const int qi = q0w + l32;  // this lane's query row
+    // Causal limits in key indices: key j is allowed for row i when j <= i +
+    // shift (shift = q_off - k_off for key-range launches, else 0).
+    const int64_t shift = RANGE ? a.q_off - a.k_off : 0;
+    auto diag_of = [&](int64_t row) { return (int)min<int64_t>(max<int64_t>(row + shift, -1), (int64_t)NK); };
+    const int qdiag = diag_of(qi);           // last key this lane's row may see
+    const int wdiag = diag_of(q0w + 31);     // last key any row of this wave may see
 
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
-    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
+    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)NK * D;
     const __bf16* Vth = static_cast<const __bf16*>(a.vt) + bh * (int64_t)a.npad * D;
-    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)NK * D;
 
     // ---- tile schedule ----
-    int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0;
+    int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0, kv_lo = 0, kv_hi = 0;
     if (MODE == (int)Mode::kDense) {
         ntiles = (N + BN - 1) / BN;
     } else if (MODE == (int)Mode::kCausal) {
         ntiles = (min(N, q0 + G::BM) + BN - 1) / BN;
+    } else if (RANGE) {
+        kv_lo = split * a.kv_chunk;
+        kv_hi = min(NK, kv_lo + a.kv_chunk);
+        // causal: keys past the last row's diagonal are never visited
+        const int vis = a.causal ? min(kv_hi, diag_of(q0 + G::BM - 1) + 1) : kv_hi;
+        ntiles = vis > kv_lo ? (vis - kv_lo + BN - 1) / BN : 0;
     } else {
         subs = a.block / BN;
         nqb_meta = (N + a.block - 1) / a.block;
@@ -132,6 +151,10 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             // the flag comes from canonical metadata; the geometric test keeps a
             // causal launch correct even for lists that were not pruned
             t.causal = ((a.flags[e] & 1) != 0) || (a.causal && t.kb0 + BN - 1 > q0);
+        } else if (RANGE) {
+            t.kb0 = kv_lo + it * BN;
+            t.nlim = kv_hi;
+            t.causal = a.causal && (t.kb0 + BN - 1 > diag_of(q0));
         } else {
             t.kb0 = it * BN;
             t.nlim = N;
@@ -161,7 +184,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     auto issue_tile = [&](int kb0, unsigned char* dK, unsigned char* dV) {
 #pragma unroll
         for (int i = 0; i < G::K_PER_W; ++i) {
-            const int key = min(kb0 + k_row[i], N - 1);
+            const int key = min(kb0 + k_row[i], NK - 1);
             dma16(Kh + (int64_t)key * D + k_col[i], dK + (w * G::K_PER_W + i) * 1024);
         }
 #pragma unroll
@@ -176,7 +199,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             const int kq = pr % (BN / 4), dq = pr / (BN / 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = min(kb0 + 4 * kq + r, N - 1);
+                const int key = min(kb0 + 4 * kq + r, NK - 1);
                 vreg[u2][r] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + dq * 8);
             }
         }
@@ -249,7 +272,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
-                        const bool bad = (j >= t.nlim) || (t.causal && j > qi);
+                        const bool bad = (j >= t.nlim) || (t.causal && j > qdiag);
                         s[c][v] = bad ? -__builtin_inff() : s[c][v];
                     }
             }
@@ -316,7 +339,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, kbuf[un], vbuf[un]);
             const TileDesc t = describe(it);
             // a wave whose rows all precede the tile skips it (still stages V)
-            if (!(t.causal && t.kb0 > q0w + 31)) compute(t, kbuf[u], vbuf[u], sVt[VREG ? (it & 1) : 0]);
+            if (!(t.causal && t.kb0 > wdiag)) compute(t, kbuf[u], vbuf[u], sVt[VREG ? (it & 1) : 0]);
             if (vnext) store_v(sVt[(it + 1) & 1]);
         };
 
@@ -330,6 +353,25 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // ---- epilogue: O = A / l, LSE = (m + log2 l) * ln 2 ----
     const float l_tot = xor32_sum(ell);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    if (RANGE) {   // normalised fp32 partial state of this split
+        if (qi < N) {
+            const int64_t row = ((int64_t)split * a.BH + bh) * N + qi;
+            float* Or = a.o_part + row * D;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float4 ov;
+                    ov.x = oacc[db][4 * j + 0] * inv;
+                    ov.y = oacc[db][4 * j + 1] * inv;
+                    ov.z = oacc[db][4 * j + 2] * inv;
+                    ov.w = oacc[db][4 * j + 3] * inv;
+                    *reinterpret_cast<float4*>(Or + 32 * db + 8 * j + 4 * hi) = ov;
+                }
+            if (hi == 0) a.lse_part[row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+        }
+        return;
+    }
     if (qi < N) {
         __bf16* Oh = static_cast<__bf16*>(a.o) + bh * (int64_t)N * D + (int64_t)qi * D;
 #pragma unroll
@@ -386,7 +428,7 @@ template <int D, int NW, int NS, int MODE, bool VREG = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     using G = Geo<D, NW, NS, VREG>;
     const int64_t nqt = (a.N + G::BM - 1) / G::BM;
-    const int64_t grid = nqt * a.BH;
+    const int64_t grid = nqt * a.BH * (MODE == (int)Mode::kRange ? a.nsplit : 1);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VREG>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
     return hipGetLastError();
 }
@@ -403,6 +445,7 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     switch (mode) {
         case Mode::kDense: return launch<D, 8, 3, (int)Mode::kDense>(a, stream);
         case Mode::kCausal: return launch<D, 8, 3, (int)Mode::kCausal>(a, stream);
+        case Mode::kRange: return launch<D, 8, 3, (int)Mode::kRange>(a, stream);
         case Mode::kSparse:
             if (a.block == 128)
                 return vreg ? launch<D, 4, 2, (int)Mode::kSparse, true>(a, stream)

@@ -28,10 +28,25 @@ struct FwdArgs {
     int block;
     // workspace: V transposed per head, [BH][d][npad] bf16 (bf16 path only)
     void* vt;
-    int npad;            // N rounded up to the 64-key tile
+    int npad;            // keys rounded up to 128 (the V^T row length)
+    // key-range launches (Mode::kRange): the queries meet keys [s*kv_chunk,
+    // min(Nk, (s+1)*kv_chunk)) of a key/value block for split s, at global
+    // positions q_off + i and k_off + j, and write normalised fp32 partials
+    int Nk;              // keys per head in k and v
+    int64_t q_off;
+    int64_t k_off;
+    int kv_chunk;        // keys per split, a multiple of 64
+    int nsplit;
+    float* o_part;       // [nsplit][BH][N][d]
+    float* lse_part;     // [nsplit][BH][N]
 };
 
-enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2 };
+enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2, kRange = 3 };
+
+// Merge nsplit normalised partial states (o_part, lse_part as in FwdArgs)
+// into O (bf16 when out_bf16, else fp32) and LSE.
+hipError_t launch_merge(const float* o_part, const float* lse_part, int nsplit, int64_t BH, int N, int d,
+                        void* o, float* lse, bool out_bf16, hipStream_t stream);
 
 // Everything a backward launch needs (bf16 path); built and validated by the
 // host layer.

@@ -198,6 +198,7 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
         case Mode::kDense: return launch<D, (int)Mode::kDense>(a, stream);
         case Mode::kCausal: return launch<D, (int)Mode::kCausal>(a, stream);
         case Mode::kSparse: return launch<D, (int)Mode::kSparse>(a, stream);
+        case Mode::kRange: break;   // key-range launches are bf16 only
     }
     return hipErrorInvalidValue;
 }

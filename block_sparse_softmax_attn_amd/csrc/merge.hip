@@ -1,0 +1,88 @@
+// Merge of normalised partial attention states over disjoint key sets, for
+// gfx950.
+//
+// Each partial s holds, per query row, the output O_s normalised over its own
+// keys and LSE_s (natural log; -inf when the row saw none of them).  The merge
+// is the online-softmax state merge in (O, LSE) form ("Exact Blocks, Rings, and
+// Sparsity", section 2 merge invariant, section 4 associative ring merge):
+//     LSE = m + ln sum_s exp(LSE_s - m),   m = max_s LSE_s
+//     O   = sum_s exp(LSE_s - LSE) O_s
+// with O = 0 and LSE = -inf when every part is empty.  Memory-bound: each row
+// reads S * (d + 1) floats and writes d outputs plus one LSE.
+//
+// Layout: parts [S][BH][N][d] fp32 and [S][BH][N] fp32; outputs [BH][N][d]
+// (bf16 or fp32) and [BH][N].  One row per d/4 consecutive lanes (one float4
+// each), so a row never spans two waves: every lane of a row reads all of
+// the row's partial LSEs before any lane of that wave writes, which makes an
+// in-place merge into part 0 (fp32 output) safe.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fwd_common.h"
+#include "gfx950_util.h"
+
+namespace bsattn {
+namespace {
+
+template <int D, bool OUT_BF16>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
+                                                    const float* __restrict__ lse_part, int nsplit, int64_t rows,
+                                                    void* o, float* lse) {
+    constexpr int TPR = D / 4;                    // lanes per row
+    constexpr int RPB = 256 / TPR;                // rows per workgroup
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c = (threadIdx.x % TPR) * 4;
+    if (row >= rows) return;
+    float m = -__builtin_inff();
+    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lse_part[(int64_t)s * rows + row]);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    float tot = 0.f;
+    if (m > -__builtin_inff()) {
+        for (int s = 0; s < nsplit; ++s) {
+            const float ls = lse_part[(int64_t)s * rows + row];
+            const float wgt = ls > -__builtin_inff() ? expf(ls - m) : 0.f;
+            const float4 x = *reinterpret_cast<const float4*>(o_part + ((int64_t)s * rows + row) * D + c);
+            acc.x += wgt * x.x;
+            acc.y += wgt * x.y;
+            acc.z += wgt * x.z;
+            acc.w += wgt * x.w;
+            tot += wgt;
+        }
+    }
+    const float inv = tot > 0.f ? 1.0f / tot : 0.f;
+    if (OUT_BF16) {
+        bf16x4 ov;
+        ov[0] = (__bf16)(acc.x * inv);
+        ov[1] = (__bf16)(acc.y * inv);
+        ov[2] = (__bf16)(acc.z * inv);
+        ov[3] = (__bf16)(acc.w * inv);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(o) + row * D + c) = ov;
+    } else {
+        const float4 ov = {acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
+        *reinterpret_cast<float4*>(static_cast<float*>(o) + row * D + c) = ov;
+    }
+    if (c == 0) lse[row] = tot > 0.f ? m + logf(tot) : -__builtin_inff();
+}
+
+template <int D>
+hipError_t launch_d(const float* o_part, const float* lse_part, int nsplit, int64_t rows, void* o, float* lse,
+                    bool out_bf16, hipStream_t stream) {
+    constexpr int RPB = 256 / (D / 4);
+    const dim3 grid((unsigned)((rows + RPB - 1) / RPB));
+    if (out_bf16)
+        hipLaunchKernelGGL((merge_kernel<D, true>), grid, dim3(256), 0, stream, o_part, lse_part, nsplit, rows, o, lse);
+    else
+        hipLaunchKernelGGL((merge_kernel<D, false>), grid, dim3(256), 0, stream, o_part, lse_part, nsplit, rows, o, lse);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const float* o_part, const float* lse_part, int nsplit, int64_t BH, int N, int d, void* o,
+                        float* lse, bool out_bf16, hipStream_t stream) {
+    const int64_t rows = BH * N;
+    if (d == 64) return launch_d<64>(o_part, lse_part, nsplit, rows, o, lse, out_bf16, stream);
+    return launch_d<128>(o_part, lse_part, nsplit, rows, o, lse, out_bf16, stream);
+}
+
+}  // namespace bsattn

@@ -262,6 +262,67 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
                          const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
                          void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Key splits and ring steps (ATTN_BF16): partial states and their merge.
+ *
+ * A partial state of a query row over a set of keys is (O_s, LSE_s): the
+ * output normalised over those keys only, and the log-sum-exp of their scaled
+ * logits (natural log; O_s = 0 and LSE_s = -inf when the row sees none of
+ * them).  States over disjoint key sets merge exactly, in any order:
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s.
+ * Source: "Exact Blocks, Rings, and Sparsity", section 2 (mergeable online
+ * softmax state), section 4 (Ring Attention: device g keeps Q_g, meets one
+ * KV block per step, merges; causal steps skip blocks wholly in the future and
+ * mask the one crossing the diagonal).  Partial outputs are fp32.
+ *
+ * attn_fwd_splitkv - attn_fwd computed as num_splits key ranges in one
+ *   launch (for shapes whose B*H*ceil(N/256) query tiles cannot fill the
+ *   GPU), then merged: same arguments as attn_fwd plus num_splits in [1, 64]
+ *   (key ranges of whole 64-key tiles; fewer ranges when N is small).
+ *   workspace : at least attn_fwd_splitkv_workspace_bytes(...) bytes, aligned
+ *   to 256 bytes (V^T, then the fp32 partial states).
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype, d), ATTN_ECAPACITY, ATTN_EHIP.
+ */
+int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
+                                         int64_t num_splits);
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                     int64_t N, int64_t d, int dtype, float scale, int causal, int64_t num_splits,
+                     void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * attn_fwd_block - one ring step: the partial state of query rows against one
+ *   key/value block.
+ *   q        : device [B,H,Nq,d] bf16; row i sits at global position q_offset + i.
+ *   k, v     : device [B,H,Nk,d] bf16; key j sits at global position k_offset + j.
+ *   o_part   : device [B,H,Nq,d] fp32, written: O_s of each row over this block.
+ *   lse_part : device [B,H,Nq] fp32, written: LSE_s (-inf for rows that see no key).
+ *   causal   : 1 keeps the pairs with k_offset + j <= q_offset + i.
+ *   q_offset, k_offset : in [0, 2^40].
+ *   workspace : device, attn_fwd_block_workspace_bytes(B, H, Nk, d, dtype)
+ *              bytes (V^T of the block), 16-byte aligned.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY, ATTN_EHIP.
+ */
+int64_t attn_fwd_block_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, int dtype);
+
+int attn_fwd_block(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,
+                   int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype, float scale, int causal,
+                   int64_t q_offset, int64_t k_offset, void* workspace, int64_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * attn_merge - merge num_parts partial states over disjoint key sets.
+ *   o_parts   : device fp32 [num_parts][B,H,N,d]; lse_parts : device fp32
+ *               [num_parts][B,H,N] (num_parts in [1, 1024]).
+ *   o, lse    : device, written: O [B,H,N,d] of out_dtype (ATTN_F32 or
+ *               ATTN_BF16) and LSE [B,H,N] fp32.  With out_dtype ATTN_F32, o
+ *               and lse may be exactly part 0 (merge in place, as a ring step
+ *               folds its new block into the running state); no other overlap.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (d, out_dtype), ATTN_EHIP.
+ */
+int attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B, int64_t H,
+               int64_t N, int64_t d, void* o, float* lse, int out_dtype, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

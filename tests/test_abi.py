@@ -277,3 +277,46 @@ def test_blockmask_transpose_errors(m):
     bad = np.array([0, 1, 3], np.int32), np.array([0, 0, 2], np.int32)   # block 2 of 2 blocks
     assert lib.attn_blockmask_transpose(p(bad[0]), p(bad[1]), 1, 16, 8, p(t_rp), p(t_col), 3) == -1
     assert lib.attn_blockmask_transpose(None, p(col), 1, 16, 8, p(t_rp), p(t_col), 3) == -1
+
+
+# ---------------------------------------------------------------------------
+# key splits, ring steps, merge (argument checks only)
+# ---------------------------------------------------------------------------
+
+def test_splitkv_workspace_bytes(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    a256 = lambda x: (x + 255) // 256 * 256
+    # B1 H4 N8192 d128, 4 splits of 2048 keys: V^T + fp32 partials
+    vt = 4 * 128 * 8192 * 2
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 4, 8192, 128, 1, 4) == a256(vt) + a256(4 * 4 * 8192 * 128 * 4) + a256(4 * 4 * 8192 * 4)
+    # N = 100 holds two 64-key tiles: at most two ranges
+    vt = 128 * 64 * 2
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 8) == a256(vt) + a256(2 * 100 * 64 * 4) + a256(2 * 100 * 4)
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 0, 2) == -1     # bf16 only
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 0) == -1
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 65) == -1
+    assert lib.attn_fwd_block_workspace_bytes(2, 3, 300, 128, 1) == 6 * 128 * 384 * 2
+
+
+def test_split_and_ring_entry_points_reject_bad_arguments(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    f = ctypes.c_float(0.1)
+    # split-KV: bad splits, fp32, small workspace, misaligned workspace
+    assert lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 0, FAKE, 1 << 24, None) == -1
+    assert lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 0, f, 0, 2, FAKE, 1 << 24, None) == -2
+    assert lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 2, FAKE, 100, None) == -3
+    assert lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 2, FAKE + 16, 1 << 24, None) == -1
+    assert lib.attn_fwd_splitkv(None, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 2, FAKE, 1 << 24, None) == -1
+    # ring step: negative offsets, zero keys, fp32, small workspace
+    blk = lambda **kw: lib.attn_fwd_block(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, kw.get("nq", 64), kw.get("nk", 128), 64,
+                                          kw.get("dt", 1), f, 1, kw.get("qo", 0), kw.get("ko", 0), FAKE,
+                                          kw.get("ws", 1 << 24), None)
+    assert blk(qo=-1) == -1 and blk(ko=-5) == -1 and blk(nk=0) == -1 and blk(nq=0) == -1
+    assert blk(dt=0) == -2 and blk(ws=10) == -3
+    # merge: parts, d, dtype, alignment
+    mg = lambda **kw: lib.attn_merge(kw.get("op", FAKE), FAKE, kw.get("s", 2), 1, 2, 64, kw.get("d", 64), FAKE, FAKE,
+                                     kw.get("dt", 0), None)
+    assert mg(s=0) == -1 and mg(s=2000) == -1 and mg(d=96) == -2 and mg(dt=5) == -2
+    assert mg(op=None) == -1 and mg(op=FAKE + 4) == -1
