@@ -11,11 +11,12 @@ from .attention import (attention_head, attn_fwd, attn_fwd_block, attn_fwd_block
 from .backward import (attention_head_bwd, attn_bwd, attn_bwd_blocksparse, probabilities_from_lse,
                        row_scalar_d, score_gradient)
 from .blockmask import canonical_blockmask
+from .gqa import attn_bwd_gqa, attn_fwd_gqa, expand_kv, expand_lists
 
 __all__ = [
     "attention_head", "attn_fwd", "attn_fwd_blocksparse", "merge_states", "output_stage",
     "scores_stage", "softmax_stage", "token_mask_block_sparse", "token_mask_dense",
     "canonical_blockmask", "attention_head_bwd", "attn_bwd", "attn_bwd_blocksparse",
     "probabilities_from_lse", "row_scalar_d", "score_gradient", "attn_fwd_block", "merge_lse",
-    "token_mask_offsets",
+    "token_mask_offsets", "attn_fwd_gqa", "attn_bwd_gqa", "expand_kv", "expand_lists",
 ]
