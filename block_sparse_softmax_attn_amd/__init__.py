@@ -50,8 +50,12 @@ def _dtype_code(t) -> int:
 
 
 def _check_qkv(q, k, v):
-    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
+    """q [B, H, N, d]; k, v [B, Hkv, N, d] with H a multiple of Hkv (Hkv < H is
+    grouped-query attention)."""
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, H, N, d] and k, v [B, Hkv, N, d]")
+    if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:] or k.shape[1] < 1 or q.shape[1] % k.shape[1]:
+        raise ValueError("k, v must be [B, Hkv, N, d] with H a multiple of Hkv")
     if not (q.is_cuda and k.is_cuda and v.is_cuda) or len({q.device, k.device, v.device}) != 1:
         raise ValueError("q, k, v must live on one GPU")
     if q.dtype != k.dtype or q.dtype != v.dtype:
@@ -83,16 +87,17 @@ def workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
     return n
 
 
-def _workspace(q, workspace):
+def _workspace(kv, workspace):
+    """The forward's V^T workspace, sized by the key/value heads of ``kv``."""
     import torch
-    B, H, N, d = q.shape
-    need = workspace_bytes(B, H, N, d, _dtype_code(q))
+    B, H, N, d = kv.shape
+    need = workspace_bytes(B, H, N, d, _dtype_code(kv))
     if need == 0:
         return None, 0
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on q's device")
+        workspace = torch.empty(need, dtype=torch.uint8, device=kv.device)
+    if workspace.device != kv.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on the inputs' device")
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -109,13 +114,20 @@ def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, out=N
     import torch
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
-    ws, ws_bytes = _workspace(q, workspace)
+    ws, ws_bytes = _workspace(k, workspace)
+    wsp = ws.data_ptr() if ws is not None else None
     with torch.cuda.device(q.device):
-        st = _get_lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
-                          ws.data_ptr() if ws is not None else None, ws_bytes, _stream(q.device))
+        if Hkv == H:
+            st = _get_lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                     B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
+                                     wsp, ws_bytes, _stream(q.device))
+        else:
+            st = _get_lib().attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                         B, H, Hkv, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
+                                         wsp, ws_bytes, _stream(q.device))
     check("attn_fwd", st)
     return out, lse
 
@@ -209,11 +221,19 @@ def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
     row_ptr, col, flags = mask.to_device(q.device)
+    Hkv = k.shape[1]
     with torch.cuda.device(q.device):
-        st = _get_lib().attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                      B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(causal), mask.block,
-                                      row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz,
-                                      mask.meta_heads, _stream(q.device))
+        if Hkv == H:
+            st = _get_lib().attn_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                 lse.data_ptr(), B, H, N, d, _dtype_code(q), ctypes.c_float(scale),
+                                                 int(causal), mask.block, row_ptr.data_ptr(), col.data_ptr(),
+                                                 flags.data_ptr(), mask.nnz, mask.meta_heads, _stream(q.device))
+        else:
+            st = _get_lib().attn_fwd_blocksparse_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                                     lse.data_ptr(), B, H, Hkv, N, d, _dtype_code(q),
+                                                     ctypes.c_float(scale), int(causal), mask.block,
+                                                     row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz,
+                                                     mask.meta_heads, _stream(q.device))
     check("attn_fwd_blocksparse", st)
     return out, lse
 
@@ -274,9 +294,11 @@ def attn_fwd_blocksparse_prepared(q, k, workspace, mask: BlockMask, scale: Optio
 # backward
 # ---------------------------------------------------------------------------
 
-def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    """Device workspace (bytes) the bf16 backward needs for these sizes."""
-    n = int(_get_lib().attn_bwd_workspace_bytes(int(B), int(H), int(N), int(d), ATTN_BF16))
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int, Hkv: Optional[int] = None) -> int:
+    """Device workspace (bytes) the bf16 backward needs for these sizes
+    (Hkv key/value heads; default H)."""
+    Hkv = H if Hkv is None else int(Hkv)
+    n = int(_get_lib().attn_bwd_gqa_workspace_bytes(int(B), int(H), Hkv, int(N), int(d), ATTN_BF16))
     if n < 0:
         raise ValueError("sizes not supported by the backward")
     return n
@@ -294,16 +316,19 @@ def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace):
     if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     grads = []
-    for g in (dq, dk, dv):
-        g = torch.empty_like(q) if g is None else g
-        if g.shape != q.shape or g.dtype != q.dtype or not g.is_contiguous() or g.device != q.device:
-            raise ValueError("gradient outputs must match q in shape, dtype, device and be contiguous")
+    for g, like in ((dq, q), (dk, k), (dv, v)):
+        g = torch.empty_like(like) if g is None else g
+        if g.shape != like.shape or g.dtype != q.dtype or not g.is_contiguous() or g.device != q.device:
+            raise ValueError("gradient outputs must match q (dq) or k, v (dk, dv) and be contiguous")
         grads.append(g)
-    need = bwd_workspace_bytes(B, H, N, d)
+    n = int(_get_lib().attn_bwd_gqa_workspace_bytes(B, H, k.shape[1], N, d, ATTN_BF16))
+    if n < 0:
+        raise ValueError("sizes not supported by the backward")
+    need = n
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on q's device")
+        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on the inputs' device")
     return grads, workspace, workspace.numel() * workspace.element_size()
 
 
@@ -315,10 +340,15 @@ def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool 
     B, H, N, d = q.shape
     (dq, dk, dv), ws, ws_bytes = _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    Hkv = k.shape[1]
     with torch.cuda.device(q.device):
-        st = _get_lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, ATTN_BF16,
-                                 ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(), ws_bytes, _stream(q.device))
+        st = _get_lib().attn_bwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d,
+                                     ATTN_BF16, ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(), ws_bytes,
+                                     _stream(q.device)) if Hkv != H else \
+            _get_lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, ATTN_BF16,
+                                ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(), ws_bytes, _stream(q.device))
     check("attn_bwd", st)
     return dq, dk, dv
 
@@ -335,12 +365,13 @@ def attn_bwd_blocksparse(q, k, v, o, lse, dout, mask: BlockMask, scale: Optional
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     row_ptr, col, flags = mask.to_device(q.device)
     t_row_ptr, t_col = mask.transposed_to_device(q.device)
+    Hkv = k.shape[1]
     with torch.cuda.device(q.device):
-        st = _get_lib().attn_bwd_blocksparse(
+        st = _get_lib().attn_bwd_blocksparse_gqa(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, ATTN_BF16, ctypes.c_float(scale), int(causal),
-            mask.block, row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz, t_row_ptr.data_ptr(),
-            t_col.data_ptr(), mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, ATTN_BF16, ctypes.c_float(scale),
+            int(causal), mask.block, row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(), mask.nnz,
+            t_row_ptr.data_ptr(), t_col.data_ptr(), mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
     check("attn_bwd_blocksparse", st)
     return dq, dk, dv
 

@@ -25,7 +25,8 @@ EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_
             "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared",
             "attn_bwd_workspace_bytes", "attn_bwd", "attn_blockmask_transpose", "attn_bwd_blocksparse",
             "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv", "attn_fwd_block_workspace_bytes",
-            "attn_fwd_block", "attn_merge")
+            "attn_fwd_block", "attn_merge", "attn_fwd_gqa", "attn_fwd_blocksparse_gqa",
+            "attn_bwd_gqa_workspace_bytes", "attn_bwd_gqa", "attn_bwd_blocksparse_gqa")
 
 
 class AttnError(RuntimeError):
@@ -78,6 +79,19 @@ def _load() -> ctypes.CDLL:
                                    vp]
     lib.attn_merge.restype = i32
     lib.attn_merge.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, i32, vp]
+    lib.attn_fwd_gqa.restype = i32
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
+    lib.attn_fwd_blocksparse_gqa.restype = i32
+    lib.attn_fwd_blocksparse_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, i64,
+                                             vp, vp, vp, i64, i64, vp]
+    lib.attn_bwd_gqa_workspace_bytes.restype = i64
+    lib.attn_bwd_gqa_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i32]
+    lib.attn_bwd_gqa.restype = i32
+    lib.attn_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp, i64,
+                                 vp]
+    lib.attn_bwd_blocksparse_gqa.restype = i32
+    lib.attn_bwd_blocksparse_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32,
+                                             i32, i64, vp, vp, vp, i64, vp, vp, i64, vp, i64, vp]
     return lib
 
 

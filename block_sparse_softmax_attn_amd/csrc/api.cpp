@@ -41,12 +41,15 @@ bsattn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, 
     a.lse = lse;
     a.BH = B * H;
     a.H = static_cast<int>(H);
+    a.Hkv = static_cast<int>(H);
     a.N = static_cast<int>(N);
     a.d = static_cast<int>(d);
     a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
     a.causal = causal;
     return a;
 }
+
+bool valid_groups(int64_t H, int64_t Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
 
 int64_t workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
     if (dtype != ATTN_BF16) return 0;
@@ -72,7 +75,9 @@ int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, bool prepare
         if (mode == bsattn::Mode::kSparse && !prepared) {
             a.vt = nullptr;   // the sparse kernel transposes the V tiles it loads itself
         } else if (!prepared) {
-            e = bsattn::launch_v_transpose(a, stream);
+            bsattn::FwdArgs t = a;
+            t.BH = a.BH / (a.H / a.Hkv);   // V has the key/value heads
+            e = bsattn::launch_v_transpose(t, stream);
         }
         if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, mode, stream);
     } else {
@@ -81,33 +86,37 @@ int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, bool prepare
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
-int fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-              int64_t d, int dtype, float scale, int causal, void* workspace, int64_t ws_bytes, bool prepared,
-              hipStream_t stream) {
+int fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Hkv,
+              int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace, int64_t ws_bytes,
+              bool prepared, hipStream_t stream) {
     int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
-    st = check_workspace(workspace, ws_bytes, B, H, N, d, dtype);
+    if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
+    st = check_workspace(workspace, ws_bytes, B, Hkv, N, d, dtype);
     if (st != ATTN_OK) return st;
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    a.Hkv = static_cast<int>(Hkv);
     return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, workspace, prepared, stream);
 }
 
-int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-               int64_t d, int dtype, float scale, int causal, int64_t block, const int32_t* row_ptr,
-               const int32_t* col, const uint8_t* flags, int64_t nnz, int64_t meta_heads, void* workspace,
-               int64_t ws_bytes, bool prepared, hipStream_t stream) {
+int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+               int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
+               const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz, int64_t meta_heads,
+               void* workspace, int64_t ws_bytes, bool prepared, hipStream_t stream) {
     // only the prepared form reads a workspace (V^T written by attn_prepare_v)
     int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
-    if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
+    if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
+    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv) return ATTN_EINVAL;
     if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
     if (prepared) {
-        st = check_workspace(workspace, ws_bytes, B, H, N, d, dtype);
+        st = check_workspace(workspace, ws_bytes, B, Hkv, N, d, dtype);
         if (st != ATTN_OK) return st;
     }
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
+    a.Hkv = static_cast<int>(Hkv);
     a.row_ptr = row_ptr;
     a.col = col;
     a.flags = flags;
@@ -140,7 +149,7 @@ extern "C" int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                         int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
                         int64_t workspace_bytes_given, hipStream_t stream) {
-    return fwd_dense(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, workspace, workspace_bytes_given, false,
+    return fwd_dense(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, workspace, workspace_bytes_given, false,
                      stream);
 }
 
@@ -148,7 +157,7 @@ extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v,
                                     int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
                                     int64_t block, const int32_t* row_ptr, const int32_t* col,
                                     const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
-    return fwd_sparse(q, k, v, o, lse, B, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
+    return fwd_sparse(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
                       meta_heads, nullptr, 0, false, stream);
 }
 
@@ -175,7 +184,7 @@ extern "C" int attn_fwd_prepared(const void* q, const void* k, void* o, float* l
                                  int64_t d, int dtype, float scale, int causal, const void* workspace,
                                  int64_t workspace_bytes_given, hipStream_t stream) {
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    return fwd_dense(q, k, nullptr, o, lse, B, H, N, d, dtype, scale, causal, const_cast<void*>(workspace),
+    return fwd_dense(q, k, nullptr, o, lse, B, H, H, N, d, dtype, scale, causal, const_cast<void*>(workspace),
                      workspace_bytes_given, true, stream);
 }
 
@@ -185,7 +194,7 @@ extern "C" int attn_fwd_blocksparse_prepared(const void* q, const void* k, void*
                                              int64_t nnz, int64_t meta_heads, const void* workspace,
                                              int64_t workspace_bytes_given, hipStream_t stream) {
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    return fwd_sparse(q, k, nullptr, o, lse, B, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
+    return fwd_sparse(q, k, nullptr, o, lse, B, H, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
                       meta_heads, const_cast<void*>(workspace), workspace_bytes_given, true, stream);
 }
 
@@ -196,21 +205,22 @@ extern "C" int attn_fwd_blocksparse_prepared(const void* q, const void* k, void*
 namespace {
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
-              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
-              int causal, void* ws, int64_t ws_bytes) {
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype,
+              float scale, int causal, void* ws, int64_t ws_bytes) {
     int st = check_common(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
     if (!dout || !dq || !dk || !dv) return ATTN_EINVAL;
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_EINVAL;
-    if (ws_bytes < bsattn::bwd_workspace_bytes(B * H, N, d)) return ATTN_ECAPACITY;
+    if (ws_bytes < bsattn::bwd_workspace_bytes(B * H, B * Hkv, N, d)) return ATTN_ECAPACITY;
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ATTN_EINVAL;
     return ATTN_OK;
 }
 
 bsattn::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                              const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
-                              int64_t d, float scale, int causal, void* ws) {
+                              const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv,
+                              int64_t N, int64_t d, float scale, int causal, void* ws) {
     bsattn::BwdArgs a{};
     a.q = q;
     a.k = k;
@@ -223,6 +233,7 @@ bsattn::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const
     a.dv = dv;
     a.BH = B * H;
     a.H = static_cast<int>(H);
+    a.Hkv = static_cast<int>(Hkv);
     a.N = static_cast<int>(N);
     a.d = static_cast<int>(d);
     a.scale = scale;
@@ -234,39 +245,40 @@ bsattn::BwdArgs make_bwd_args(const void* q, const void* k, const void* v, const
 
 }  // namespace
 
-extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+namespace {
+
+int64_t bwd_ws(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype) {
     if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128) || dtype != ATTN_BF16) return -1;
+    if (!valid_groups(H, Hkv)) return -1;
     if (B > (int64_t(1) << 62) / H || B * H > (int64_t(1) << 58) / (8 * d * bsattn::vt_padded_keys(N))) return -1;
-    return bsattn::bwd_workspace_bytes(B * H, N, d);
+    return bsattn::bwd_workspace_bytes(B * H, B * Hkv, N, d);
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                        const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
-                        int dtype, float scale, int causal, void* workspace, int64_t workspace_bytes_given,
-                        hipStream_t stream) {
-    const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, scale, causal, workspace,
-                             workspace_bytes_given);
+int bwd_dense(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+              void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype,
+              float scale, int causal, void* workspace, int64_t ws_bytes, hipStream_t stream) {
+    const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, dtype, scale, causal, workspace,
+                             ws_bytes);
     if (st != ATTN_OK) return st;
-    bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, workspace);
+    bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace);
     const hipError_t e =
         bsattn::launch_bwd_bf16(a, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
-extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                                    const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
-                                    int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
-                                    const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz,
-                                    const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
-                                    void* workspace, int64_t workspace_bytes_given, hipStream_t stream) {
-    int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, dtype, scale, causal, workspace,
-                       workspace_bytes_given);
+int bwd_sparse(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype,
+               float scale, int causal, int64_t block, const int32_t* row_ptr, const int32_t* col,
+               const uint8_t* flags, int64_t nnz, const int32_t* t_row_ptr, const int32_t* t_col,
+               int64_t meta_heads, void* workspace, int64_t ws_bytes, hipStream_t stream) {
+    int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, dtype, scale, causal, workspace,
+                       ws_bytes);
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
-    if (meta_heads != 1 && meta_heads != H) return ATTN_EINVAL;
+    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv) return ATTN_EINVAL;
     if (!row_ptr || !t_row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags || !t_col)) return ATTN_EINVAL;
-    bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, scale, causal, workspace);
+    bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace);
     a.row_ptr = row_ptr;
     a.col = col;
     a.flags = flags;
@@ -278,6 +290,73 @@ extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
     a.block = static_cast<int>(block);
     const hipError_t e = bsattn::launch_bwd_bf16(a, bsattn::Mode::kSparse, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+}  // namespace
+
+extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    return bwd_ws(B, H, H, N, d, dtype);
+}
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                        int dtype, float scale, int causal, void* workspace, int64_t workspace_bytes_given,
+                        hipStream_t stream) {
+    return bwd_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, dtype, scale, causal, workspace,
+                     workspace_bytes_given, stream);
+}
+
+extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                    const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                                    int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
+                                    const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz,
+                                    const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
+                                    void* workspace, int64_t workspace_bytes_given, hipStream_t stream) {
+    return bwd_sparse(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, dtype, scale, causal, block, row_ptr, col,
+                      flags, nnz, t_row_ptr, t_col, meta_heads, workspace, workspace_bytes_given, stream);
+}
+
+// ---------------------------------------------------------------------------
+// grouped-query attention: Hkv key/value heads shared by H query heads
+// ---------------------------------------------------------------------------
+
+extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                            int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
+                            int64_t workspace_bytes_given, hipStream_t stream) {
+    return fwd_dense(q, k, v, o, lse, B, H, Hkv, N, d, dtype, scale, causal, workspace, workspace_bytes_given, false,
+                     stream);
+}
+
+extern "C" int attn_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                        int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype, float scale,
+                                        int causal, int64_t block, const int32_t* row_ptr, const int32_t* col,
+                                        const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
+    return fwd_sparse(q, k, v, o, lse, B, H, Hkv, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
+                      meta_heads, nullptr, 0, false, stream);
+}
+
+extern "C" int64_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                                int dtype) {
+    return bwd_ws(B, H, Hkv, N, d, dtype);
+}
+
+extern "C" int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                            const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv,
+                            int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
+                            int64_t workspace_bytes_given, hipStream_t stream) {
+    return bwd_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, dtype, scale, causal, workspace,
+                     workspace_bytes_given, stream);
+}
+
+extern "C" int attn_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const void* o,
+                                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int64_t B,
+                                        int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype, float scale,
+                                        int causal, int64_t block, const int32_t* row_ptr, const int32_t* col,
+                                        const uint8_t* flags, int64_t nnz, const int32_t* t_row_ptr,
+                                        const int32_t* t_col, int64_t meta_heads, void* workspace,
+                                        int64_t workspace_bytes_given, hipStream_t stream) {
+    return bwd_sparse(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, dtype, scale, causal, block, row_ptr, col,
+                      flags, nnz, t_row_ptr, t_col, meta_heads, workspace, workspace_bytes_given, stream);
 }
 
 // ---------------------------------------------------------------------------

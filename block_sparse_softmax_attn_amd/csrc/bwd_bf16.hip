@@ -110,46 +110,89 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
     const int l32 = lane & 31, hi = lane >> 5;
     const int N = a.N;
     const int nkt = (N + G::BKV - 1) / G::BKV;
-    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nkt * a.BH);
-    const int64_t bh = ord / nkt;
+    // one workgroup per (key/value head, key tile); it sums the contributions
+    // of every query head of the key/value head's group
+    const int group = a.H / a.Hkv;
+    const int64_t BHkv = a.BH / group;
+    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nkt * BHkv);
+    const int64_t kvbh = ord / nkt;
     const int kt = (int)(ord % nkt);   // causal: the first key tiles see the most queries and start first
+    const int64_t bh0 = (kvbh / a.Hkv) * a.H + (kvbh % a.Hkv) * group;   // first query head of the group
     const int kb0 = kt * G::BKV;
     const int kw0 = kb0 + 32 * w;      // this wave's first key
     const int kj = kw0 + l32;          // this lane's key
     const int nblk = a.npad / BT;
     const bool causal = MODE == (int)Mode::kCausal || (MODE == (int)Mode::kSparse && a.causal);
 
-    const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
-    const __bf16* dOh = static_cast<const __bf16*>(a.dout) + bh * (int64_t)N * D;
-    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
-    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
-    const __bf16* QTh = static_cast<const __bf16*>(a.qt) + bh * (int64_t)a.npad * D;
-    const __bf16* dOTh = static_cast<const __bf16*>(a.dot) + bh * (int64_t)a.npad * D;
-    const float* Sh = a.stats + bh * (int64_t)(nblk + 1) * 128;
+    const __bf16* Kh = static_cast<const __bf16*>(a.k) + kvbh * (int64_t)N * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + kvbh * (int64_t)N * D;
 
-    // ---- schedule of 64-query tiles ----
-    int ntiles = 0, first = 0, e0 = 0, subs = 1, nqb_meta = 0;
+    // ---- schedule: 64-query tiles of each query head of the group ----
+    int per = 0, first = 0, subs = 1, nqb_meta = 0;
+    bool uniform = true;   // every query head of the group has the same tile list
     if (MODE == (int)Mode::kDense) {
-        ntiles = (N + BT - 1) / BT;
+        per = (N + BT - 1) / BT;
     } else if (MODE == (int)Mode::kCausal) {
         first = kb0 / BT;   // queries before the first key see none of these keys
-        ntiles = (N + BT - 1) / BT - first;
+        per = (N + BT - 1) / BT - first;
     } else {
         subs = a.block / BT;
         nqb_meta = (N + a.block - 1) / a.block;
-        const int h = (int)(bh % a.H);
-        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + kt;   // BKV == block for sparse launches
-        int lo = a.t_row_ptr[r], hi_ = a.t_row_ptr[r + 1];
+        uniform = group == 1 || a.meta_heads == 1 || a.meta_heads == a.Hkv;
+    }
+    // entries [lo, hi) of the transposed list of query head bh0 + gi (BKV == block)
+    auto list_of = [&](int gi, int& lo, int& hi_) {
+        const int64_t r = meta_of(bh0 + gi, a.H, a.Hkv, a.meta_heads) * nqb_meta + kt;
+        lo = a.t_row_ptr[r];
+        hi_ = a.t_row_ptr[r + 1];
         lo = (int)min<int64_t>(max(lo, 0), a.t_nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.t_nnz);
-        e0 = lo;
-        ntiles = (hi_ - lo) * subs;
+    };
+    int ntiles = 0;
+    if (MODE != (int)Mode::kSparse) {
+        ntiles = per * group;
+    } else if (uniform) {
+        int lo, hi_;
+        list_of(0, lo, hi_);
+        per = (hi_ - lo) * subs;
+        ntiles = per * group;
+    } else {
+        for (int gi = 0; gi < group; ++gi) {
+            int lo, hi_;
+            list_of(gi, lo, hi_);
+            ntiles += (hi_ - lo) * subs;
+        }
     }
-    // first query of tile it; -1 for an out-of-range metadata entry
-    auto tile_q0 = [&](int it) -> int {
-        if (MODE != (int)Mode::kSparse) return (first + it) * BT;
-        const int qb = a.t_col[e0 + it / subs];
-        return (qb >= 0 && qb < nqb_meta) ? qb * a.block + (it % subs) * BT : -1;
+    // Tile it: its query head and first query (-1 for an out-of-range entry).
+    struct QTile {
+        int64_t bhq;
+        int q0;
+    };
+    auto locate = [&](int it) -> QTile {
+        int gi = 0, loc = it;
+        if (uniform) {
+            gi = it / per;
+            loc = it % per;
+        } else {
+            for (;;) {
+                int lo, hi_;
+                list_of(gi, lo, hi_);
+                if (loc < (hi_ - lo) * subs) break;
+                loc -= (hi_ - lo) * subs;
+                ++gi;
+            }
+        }
+        QTile t;
+        t.bhq = bh0 + gi;
+        if (MODE != (int)Mode::kSparse) {
+            t.q0 = (first + loc) * BT;
+        } else {
+            int lo, hi_;
+            list_of(gi, lo, hi_);
+            const int qb = a.t_col[lo + loc / subs];
+            t.q0 = (qb >= 0 && qb < nqb_meta) ? qb * a.block + (loc % subs) * BT : -1;
+        }
+        return t;
     };
 
     // Direct-to-LDS sources: load i of this wave fills bytes [1024 (w PER_T + i)
@@ -166,12 +209,17 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
         const int d = byte / (2 * BT), p2 = (byte % (2 * BT)) / 16;
         tr_off[i] = d * a.npad + v_swz(d, p2) * 8;
     }
-    auto issue = [&](int q0, int u) {
+    auto issue = [&](const QTile& t, int u) {
         unsigned char* dQ = u ? sQ1 : sQ0;
         unsigned char* dO = u ? sO1 : sO0;
         unsigned char* dQT = u ? sQT1 : sQT0;
         unsigned char* dOT = u ? sOT1 : sOT0;
-        q0 = max(q0, 0);
+        const int q0 = max(t.q0, 0);
+        const __bf16* Qh = static_cast<const __bf16*>(a.q) + t.bhq * (int64_t)N * D;
+        const __bf16* dOh = static_cast<const __bf16*>(a.dout) + t.bhq * (int64_t)N * D;
+        const __bf16* QTh = static_cast<const __bf16*>(a.qt) + t.bhq * (int64_t)a.npad * D;
+        const __bf16* dOTh = static_cast<const __bf16*>(a.dot) + t.bhq * (int64_t)a.npad * D;
+        const float* Sh = a.stats + t.bhq * (int64_t)(nblk + 1) * 128;
 #pragma unroll
         for (int i = 0; i < G::PER_T; ++i) {
             const int row = min(q0 + rm_row[i], N - 1);
@@ -282,13 +330,13 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
     auto step = [&](int it, int u) {
         wait_vmcnt<0>();
         barrier();
-        if (it + 1 < ntiles) issue(tile_q0(it + 1), u ^ 1);
-        const int q0 = tile_q0(it);
+        if (it + 1 < ntiles) issue(locate(it + 1), u ^ 1);
+        const int q0 = locate(it).q0;
         if (q0 < 0 || q0 >= N) return;
         if (causal && q0 + BT - 1 < kw0) return;   // the whole tile precedes this wave's keys
         compute(q0, u);
     };
-    if (ntiles > 0) issue(tile_q0(0), 0);
+    if (ntiles > 0) issue(locate(0), 0);
     for (int base = 0; base < ntiles; base += 2) {
         step(base, 0);
         if (base + 1 < ntiles) step(base + 1, 1);
@@ -296,8 +344,8 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
 
     // ---- epilogue: dK = scale * (Q^T dS)^T, dV = (dO^T P)^T ----
     if (kj < N) {
-        __bf16* dKr = static_cast<__bf16*>(a.dk) + (bh * N + kj) * (int64_t)D;
-        __bf16* dVr = static_cast<__bf16*>(a.dv) + (bh * N + kj) * (int64_t)D;
+        __bf16* dKr = static_cast<__bf16*>(a.dk) + (kvbh * N + kj) * (int64_t)D;
+        __bf16* dVr = static_cast<__bf16*>(a.dv) + (kvbh * N + kj) * (int64_t)D;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -364,9 +412,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
     const __bf16* dOh = static_cast<const __bf16*>(a.dout) + bh * (int64_t)N * D;
-    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)N * D;
-    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)N * D;
-    const __bf16* KTh = static_cast<const __bf16*>(a.kt) + bh * (int64_t)a.npad * D;
+    const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
+    const __bf16* Kh = static_cast<const __bf16*>(a.k) + kvh * (int64_t)N * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + kvh * (int64_t)N * D;
+    const __bf16* KTh = static_cast<const __bf16*>(a.kt) + kvh * (int64_t)a.npad * D;
     const float* Sh = a.stats + bh * (int64_t)(nblk + 1) * 128;
 
     // ---- schedule of 64-key tiles (the forward's) ----
@@ -378,8 +427,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     } else {
         subs = a.block / BT;
         nqb_meta = (N + a.block - 1) / a.block;
-        const int h = (int)(bh % a.H);
-        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + qt;   // BM == block for sparse launches
+        const int64_t r = meta_of(bh, a.H, a.Hkv, a.meta_heads) * nqb_meta + qt;   // BM == block for sparse launches
         int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
         lo = (int)min<int64_t>(max(lo, 0), a.nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);
@@ -533,7 +581,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 template <int D, int NW, int MODE>
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
     const int64_t nkt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE>), dim3((unsigned)(nkt * a.BH)), dim3(64 * NW), 0, stream, a);
+    const int64_t bhkv = a.BH / (a.H / a.Hkv);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE>), dim3((unsigned)(nkt * bhkv)), dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -575,22 +624,24 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
 
 }  // namespace
 
-int64_t bwd_workspace_bytes(int64_t BH, int64_t N, int64_t d) {
+int64_t bwd_workspace_bytes(int64_t BH, int64_t BHkv, int64_t N, int64_t d) {
     const int64_t npad = vt_padded_keys(N);
-    const int64_t tr = BH * d * npad * 2;                    // one transposed tensor
+    const int64_t tr = BH * d * npad * 2;                    // Q^T or dO^T
+    const int64_t trk = BHkv * d * npad * 2;                 // K^T
     const int64_t st = BH * (npad / BT + 1) * 128 * 4;       // row statistics
-    return 3 * tr + st;
+    return 2 * tr + trk + st;
 }
 
 void bwd_workspace_carve(BwdArgs& a, void* ws) {
     const int64_t npad = vt_padded_keys(a.N);
     const int64_t tr = a.BH * a.d * npad * 2;
+    const int64_t trk = a.BH / (a.H / a.Hkv) * a.d * npad * 2;
     unsigned char* p = static_cast<unsigned char*>(ws);
     a.npad = (int)npad;
     a.qt = p;
-    a.kt = p + tr;
-    a.dot = p + 2 * tr;
-    a.stats = reinterpret_cast<float*>(p + 3 * tr);
+    a.dot = p + tr;
+    a.kt = p + 2 * tr;
+    a.stats = reinterpret_cast<float*>(p + 2 * tr + trk);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream) {
@@ -605,6 +656,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream) {
     for (int i = 0; i < 3; ++i) {
         t.v = src[i];
         t.vt = dst[i];
+        t.BH = i == 1 ? a.BH / (a.H / a.Hkv) : a.BH;   // K has the key/value heads
         const hipError_t e = launch_v_transpose(t, stream);
         if (e != hipSuccess) return e;
     }

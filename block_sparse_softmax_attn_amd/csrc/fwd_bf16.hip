@@ -112,10 +112,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int qdiag = diag_of(qi);           // last key this lane's row may see
     const int wdiag = diag_of(q0w + 31);     // last key any row of this wave may see
 
+    const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
-    const __bf16* Kh = static_cast<const __bf16*>(a.k) + bh * (int64_t)NK * D;
-    const __bf16* Vth = static_cast<const __bf16*>(a.vt) + bh * (int64_t)a.npad * D;
-    const __bf16* Vh = static_cast<const __bf16*>(a.v) + bh * (int64_t)NK * D;
+    const __bf16* Kh = static_cast<const __bf16*>(a.k) + kvh * (int64_t)NK * D;
+    const __bf16* Vth = static_cast<const __bf16*>(a.vt) + kvh * (int64_t)a.npad * D;
+    const __bf16* Vh = static_cast<const __bf16*>(a.v) + kvh * (int64_t)NK * D;
 
     // ---- tile schedule ----
     int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0, kv_lo = 0, kv_hi = 0;
@@ -132,8 +133,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     } else {
         subs = a.block / BN;
         nqb_meta = (N + a.block - 1) / a.block;
-        const int h = (int)(bh % a.H);
-        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + qt;   // BM == block for sparse launches
+        const int64_t r = meta_of(bh, a.H, a.Hkv, a.meta_heads) * nqb_meta + qt;   // BM == block for sparse launches
         int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
         lo = (int)min<int64_t>(max(lo, 0), a.nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);

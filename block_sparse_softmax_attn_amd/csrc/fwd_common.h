@@ -13,8 +13,9 @@ struct FwdArgs {
     const void* v;
     void* o;
     float* lse;
-    int64_t BH;          // B * H
+    int64_t BH;          // B * H (query heads)
     int H;
+    int Hkv;             // key/value heads per batch entry; H % Hkv == 0
     int N;
     int d;
     float scale_log2;    // scale * log2(e): logits are handled in base-2 units
@@ -43,6 +44,23 @@ struct FwdArgs {
 
 enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2, kRange = 3 };
 
+// Grouped-query attention: the H / Hkv query heads h of one group share key/value
+// head h / (H / Hkv).  Index of the key/value head of query head bh = b*H + h.
+__host__ __device__ inline int64_t kv_head_of(int64_t bh, int H, int Hkv) {
+    return (bh / H) * Hkv + (bh % H) / (H / Hkv);
+}
+
+// Block-sparse pattern used by query head bh: one pattern for every head
+// (meta_heads 1), one per query head (H), one per key/value head (Hkv: the
+// query heads of a group share their key-block list), or one per (batch,
+// head) (B*H).
+__host__ __device__ inline int64_t meta_of(int64_t bh, int H, int Hkv, int meta_heads) {
+    if (meta_heads == 1) return 0;
+    if (meta_heads == H) return bh % H;
+    if (meta_heads == Hkv) return (bh % H) / (H / Hkv);
+    return bh;
+}
+
 // Merge nsplit normalised partial states (o_part, lse_part as in FwdArgs)
 // into O (bf16 when out_bf16, else fp32) and LSE.
 hipError_t launch_merge(const float* o_part, const float* lse_part, int nsplit, int64_t BH, int N, int d,
@@ -62,6 +80,7 @@ struct BwdArgs {
     void* dv;
     int64_t BH;
     int H;
+    int Hkv;
     int N;
     int d;
     float scale;
@@ -78,9 +97,9 @@ struct BwdArgs {
     int64_t t_nnz;
     int meta_heads;
     int block;
-    // workspace: Q^T, K^T, dO^T ([BH][d][npad] bf16, the transposed-tile key
-    // order) and per-row statistics ([BH][npad/64 + 1][2][64] fp32: LSE in
-    // base-2 units, then D = dO . O, for each 64-row block)
+    // workspace: Q^T, dO^T ([BH][d][npad] bf16, the transposed-tile key
+    // order), K^T ([B*Hkv][d][npad]) and per-row statistics ([BH][npad/64 +
+    // 1][2][64] fp32: LSE in base-2 units, then D = dO . O, per 64-row block)
     void* qt;
     void* kt;
     void* dot;
@@ -88,9 +107,10 @@ struct BwdArgs {
     int npad;
 };
 
-// Bytes of backward workspace for B*H heads of N rows and head dim d.
-int64_t bwd_workspace_bytes(int64_t BH, int64_t N, int64_t d);
-// Split a workspace into the BwdArgs pieces (a.BH, a.N, a.d set).
+// Bytes of backward workspace for BH query heads and BHkv key/value heads of
+// N rows and head dim d.
+int64_t bwd_workspace_bytes(int64_t BH, int64_t BHkv, int64_t N, int64_t d);
+// Split a workspace into the BwdArgs pieces (a.BH, a.H, a.Hkv, a.N, a.d set).
 void bwd_workspace_carve(BwdArgs& a, void* ws);
 // Transposes, row statistics, then the dK/dV and dQ kernels, all on `stream`.
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream);

@@ -62,8 +62,9 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdArgs a) {
     const bool wave_rows_live = 32 * w < bm;   // block 64 uses 2 of the 4 waves
 
     const float* Qh = static_cast<const float*>(a.q) + bh * (int64_t)N * D;
-    const float* Kh = static_cast<const float*>(a.k) + bh * (int64_t)N * D;
-    const float* Vh = static_cast<const float*>(a.v) + bh * (int64_t)N * D;
+    const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
+    const float* Kh = static_cast<const float*>(a.k) + kvh * (int64_t)N * D;
+    const float* Vh = static_cast<const float*>(a.v) + kvh * (int64_t)N * D;
 
     int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0;
     if (MODE == (int)Mode::kDense) {
@@ -73,8 +74,7 @@ __global__ __launch_bounds__(NT) void fwd_f32_kernel(FwdArgs a) {
     } else {
         subs = a.block / BN;
         nqb_meta = (N + a.block - 1) / a.block;
-        const int h = (int)(bh % a.H);
-        const int r = (a.meta_heads == 1 ? 0 : h) * nqb_meta + qt;
+        const int64_t r = meta_of(bh, a.H, a.Hkv, a.meta_heads) * nqb_meta + qt;
         int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
         lo = (int)min<int64_t>(max(lo, 0), a.nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);

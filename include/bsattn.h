@@ -323,6 +323,48 @@ int attn_fwd_block(const void* q, const void* k, const void* v, float* o_part, f
 int attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, int64_t B, int64_t H,
                int64_t N, int64_t d, void* o, float* lse, int out_dtype, hipStream_t stream);
 
+/*
+ * Grouped-query attention: H query heads share Hkv key/value heads (H % Hkv ==
+ * 0); query head h reads key/value head h / (H / Hkv).  Under block sparsity
+ * the query heads of a group can share one key-block list (meta_heads == Hkv),
+ * so the group loads one set of K/V blocks rather than the union of unrelated
+ * sets.  Source: "Exact Blocks, Rings, and Sparsity", section 5 ("The selector
+ * must cost less than the tiles it skips": GQA and the union of per-head
+ * selections) and the NSA remarks on query heads sharing one KV cache.
+ *
+ *   q, o, dq, dout : [B,H,N,d];  k, v, dk, dv : [B,Hkv,N,d];  lse : [B,H,N].
+ *   The other arguments are those of the non-grouped entry points; meta_heads
+ *   may also be Hkv.  Each dK, dV head is the sum of the contributions of its
+ *   group's query heads (one workgroup per key/value head sums them in a fixed
+ *   order: deterministic).
+ *   Workspaces: attn_fwd_gqa needs attn_fwd_workspace_bytes(B, Hkv, N, d, dtype)
+ *   (V^T of the key/value heads); attn_fwd_blocksparse_gqa needs none; the
+ *   backward needs attn_bwd_gqa_workspace_bytes(B, H, Hkv, N, d, dtype).
+ *   Errors: as for the non-grouped entry points; ATTN_EINVAL also when Hkv < 1,
+ *   Hkv > H or H % Hkv != 0.
+ */
+int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                 int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
+                 int64_t workspace_bytes, hipStream_t stream);
+
+int attn_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                             int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                             int64_t block, const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
+                             int64_t nnz, int64_t meta_heads, hipStream_t stream);
+
+int64_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype);
+
+int attn_bwd_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype,
+                 float scale, int causal, void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+int attn_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv,
+                             int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
+                             const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz,
+                             const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
+                             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -320,3 +320,31 @@ def test_split_and_ring_entry_points_reject_bad_arguments(m):
                                      kw.get("dt", 0), None)
     assert mg(s=0) == -1 and mg(s=2000) == -1 and mg(d=96) == -2 and mg(dt=5) == -2
     assert mg(op=None) == -1 and mg(op=FAKE + 4) == -1
+
+
+# ---------------------------------------------------------------------------
+# grouped-query attention (argument checks only)
+# ---------------------------------------------------------------------------
+
+def test_gqa_workspace_and_bad_groups(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    # Q^T and dO^T over the 8 query heads, K^T over the 2 key/value heads, statistics per query head
+    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 2, 1024, 128, 1) == 2 * 8 * 128 * 1024 * 2 + 2 * 128 * 1024 * 2 + 8 * 17 * 512
+    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 8, 1024, 128, 1) == lib.attn_bwd_workspace_bytes(1, 8, 1024, 128, 1)
+    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 3, 1024, 128, 1) == -1
+    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 0, 1024, 128, 1) == -1
+    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 16, 1024, 128, 1) == -1
+    f = ctypes.c_float(0.1)
+    for hkv in (0, 3, 16):
+        assert lib.attn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0, FAKE, 1 << 24, None) == -1
+        assert lib.attn_fwd_blocksparse_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0, 128, FAKE,
+                                            FAKE, FAKE, 4, 1, None) == -1
+        assert lib.attn_bwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0,
+                                FAKE, 1 << 26, None) == -1
+    # meta_heads must be 1, Hkv or H
+    assert lib.attn_fwd_blocksparse_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 1, f, 0, 128, FAKE, FAKE,
+                                        FAKE, 4, 4, None) == -1
+    # forward workspace is V^T of the key/value heads
+    assert lib.attn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 1, f, 0, FAKE, 2 * 64 * 256 * 2 - 16,
+                            None) == -3
