@@ -12,6 +12,7 @@ from .backward import (attention_head_bwd, attn_bwd, attn_bwd_blocksparse, proba
                        row_scalar_d, score_gradient)
 from .blockmask import canonical_blockmask
 from .gqa import attn_bwd_gqa, attn_fwd_gqa, expand_kv, expand_lists
+from .selector import block_means, meanpool_scores, meanpool_select, select_topk
 
 __all__ = [
     "attention_head", "attn_fwd", "attn_fwd_blocksparse", "merge_states", "output_stage",
@@ -19,4 +20,5 @@ __all__ = [
     "canonical_blockmask", "attention_head_bwd", "attn_bwd", "attn_bwd_blocksparse",
     "probabilities_from_lse", "row_scalar_d", "score_gradient", "attn_fwd_block", "merge_lse",
     "token_mask_offsets", "attn_fwd_gqa", "attn_bwd_gqa", "expand_kv", "expand_lists",
+    "block_means", "meanpool_scores", "meanpool_select", "select_topk",
 ]

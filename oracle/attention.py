@@ -165,13 +165,23 @@ def attn_fwd_blocksparse(q, k, v, scale: float, causal: bool, block: int, raw_ro
     block, shared by every (b,h) when meta_heads == 1, else one set per head h.
     """
     B, H, N, d = q.shape
-    if meta_heads not in (1, H):
-        raise ValueError("meta_heads must be 1 or H")
+    if meta_heads not in (1, H, B * H):
+        raise ValueError("meta_heads must be 1, H or B*H")
     rows_fn = _rows_fn(rows, N)
     mask_fn = lambda b, h, r: token_mask_block_sparse(N, causal, block, raw_row_ptr, raw_col,
-                                                      0 if meta_heads == 1 else h, r)
+                                                      meta_index(b, h, H, meta_heads), r)
     outs, lses = _run(q, k, v, scale, rows_fn, mask_fn, row_chunk)
     return _pack(outs, lses, B, H, N, d, rows)
+
+
+def meta_index(b: int, h: int, H: int, meta_heads: int) -> int:
+    """Which pattern (b, h) uses: one for every head (meta_heads 1), one per
+    head (H), or one per (batch, head) (B*H, b-major)."""
+    if meta_heads == 1:
+        return 0
+    if meta_heads == H:
+        return h
+    return b * H + h
 
 
 def _rows_fn(rows, N):

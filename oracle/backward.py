@@ -38,7 +38,8 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .attention import _as64, scores_stage, softmax_stage, output_stage, token_mask_block_sparse, token_mask_dense
+from .attention import (_as64, meta_index, output_stage, scores_stage, softmax_stage, token_mask_block_sparse,
+                        token_mask_dense)
 
 
 def probabilities_from_lse(s: np.ndarray, lse: np.ndarray) -> np.ndarray:
@@ -122,8 +123,8 @@ def attn_bwd_blocksparse(q, k, v, do, scale: float, causal: bool, block: int, ra
     """Gradients of block-sparse attention renormalised over the allowed pairs
     (raw, uncanonicalised lists; meta_heads 1 or H, as the forward oracle)."""
     B, H, N, d = q.shape
-    if meta_heads not in (1, H):
-        raise ValueError("meta_heads must be 1 or H")
+    if meta_heads not in (1, H, B * H):
+        raise ValueError("meta_heads must be 1, H or B*H")
     mask_for_head = lambda b, h: (lambda rows: token_mask_block_sparse(
-        N, causal, block, raw_row_ptr, raw_col, 0 if meta_heads == 1 else h, rows))
+        N, causal, block, raw_row_ptr, raw_col, meta_index(b, h, H, meta_heads), rows))
     return _run_bwd(q, k, v, do, scale, mask_for_head, o, lse, row_chunk)
