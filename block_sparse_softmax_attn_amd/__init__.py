@@ -35,7 +35,7 @@ from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN
 
 __all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "prepare_v", "attn_fwd_prepared",
            "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_blocksparse", "bwd_workspace_bytes",
-           "attn_fwd_splitkv", "attn_fwd_block", "attn_merge",
+           "attn_fwd_splitkv", "attn_fwd_block", "attn_merge", "select_meanpool", "DeviceBlockMask",
            "BlockMask", "AttnError", "LIB_PATH",
            "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
 
@@ -464,3 +464,99 @@ def attn_merge(o_parts, lse_parts, out_dtype=None, out=None, lse=None):
                                    lse.data_ptr(), code, _stream(o_parts.device))
     check("attn_merge", st)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# mean-pooled block selector (metadata built on the device)
+# ---------------------------------------------------------------------------
+
+class DeviceBlockMask:
+    """Canonical block-sparse metadata that lives on the device (as written by
+    the selector): one pattern per (batch, head).  Usable wherever a BlockMask
+    is; host copies and pair counts are made on first use."""
+
+    def __init__(self, N, block, causal, meta_heads, row_ptr, col, flags):
+        self.N, self.block, self.causal, self.meta_heads = int(N), int(block), bool(causal), int(meta_heads)
+        self._dev = (row_ptr, col, flags)
+        self._host = None
+        self._counts = None
+        self._t = {}
+
+    @property
+    def nnz(self) -> int:
+        return int(self._dev[1].numel())
+
+    def to_device(self, device):
+        if self._dev[0].device != device:
+            raise ValueError("the selector's metadata lives on another device")
+        return self._dev
+
+    def host(self) -> "BlockMask":
+        """A host BlockMask with the same lists (copies from the device)."""
+        if self._host is None:
+            rp, col, fl = (t.cpu().numpy() for t in self._dev)
+            counts = blockmask_build(rp, col, self.meta_heads, self.N, self.block, self.causal)
+            self._host = counts
+        return self._host
+
+    @property
+    def row_ptr(self):
+        return self.host().row_ptr
+
+    @property
+    def col(self):
+        return self.host().col
+
+    @property
+    def flags(self):
+        return self.host().flags
+
+    @property
+    def allowed_pairs(self):
+        return self.host().allowed_pairs
+
+    @property
+    def executed_tile_pairs(self):
+        return self.host().executed_tile_pairs
+
+    def transposed(self):
+        return self.host().transposed()
+
+    def transposed_to_device(self, device):
+        key = str(device)
+        if key not in self._t:
+            import torch
+            self._t[key] = tuple(torch.from_numpy(x).to(device) for x in self.transposed())
+        return self._t[key]
+
+
+def select_meanpool(q, k, block: int, topk: int, causal: bool = False, scale: Optional[float] = None,
+                    share_groups: bool = False, workspace=None) -> DeviceBlockMask:
+    """Top-k key blocks per query block by mean-pooled tile score, on the device."""
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ValueError("q must be [B, H, N, d] and k [B, Hkv, N, d]")
+    if not (q.is_contiguous() and k.is_contiguous()) or q.device != k.device or not q.is_cuda:
+        raise ValueError("q and k must be contiguous and on one GPU")
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = _get_lib()
+    nnz = int(lib.attn_select_meanpool_nnz(B, H, N, int(block), int(bool(causal)), int(topk)))
+    need = int(lib.attn_select_meanpool_workspace_bytes(B, H, Hkv, N, d, int(block)))
+    if nnz < 0 or need < 0:
+        raise ValueError("sizes, block or topk not supported by the selector")
+    nb = -(-N // int(block))
+    row_ptr = torch.empty(B * H * nb + 1, dtype=torch.int32, device=q.device)
+    col = torch.empty(max(nnz, 1), dtype=torch.int32, device=q.device)
+    flags = torch.empty(max(nnz, 1), dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        st = lib.attn_select_meanpool(q.data_ptr(), k.data_ptr(), B, H, Hkv, N, d, _dtype_code(q),
+                                      ctypes.c_float(scale), int(bool(causal)), int(block), int(topk),
+                                      int(bool(share_groups)), row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(),
+                                      nnz, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                      _stream(q.device))
+    check("attn_select_meanpool", st)
+    return DeviceBlockMask(N, block, causal, B * H, row_ptr, col[:nnz], flags[:nnz])

@@ -26,7 +26,8 @@ EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_
             "attn_bwd_workspace_bytes", "attn_bwd", "attn_blockmask_transpose", "attn_bwd_blocksparse",
             "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv", "attn_fwd_block_workspace_bytes",
             "attn_fwd_block", "attn_merge", "attn_fwd_gqa", "attn_fwd_blocksparse_gqa",
-            "attn_bwd_gqa_workspace_bytes", "attn_bwd_gqa", "attn_bwd_blocksparse_gqa")
+            "attn_bwd_gqa_workspace_bytes", "attn_bwd_gqa", "attn_bwd_blocksparse_gqa",
+            "attn_select_meanpool_nnz", "attn_select_meanpool_workspace_bytes", "attn_select_meanpool")
 
 
 class AttnError(RuntimeError):
@@ -92,6 +93,13 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_blocksparse_gqa.restype = i32
     lib.attn_bwd_blocksparse_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32,
                                              i32, i64, vp, vp, vp, i64, vp, vp, i64, vp, i64, vp]
+    lib.attn_select_meanpool_nnz.restype = i64
+    lib.attn_select_meanpool_nnz.argtypes = [i64, i64, i64, i64, i32, i64]
+    lib.attn_select_meanpool_workspace_bytes.restype = i64
+    lib.attn_select_meanpool_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.attn_select_meanpool.restype = i32
+    lib.attn_select_meanpool.argtypes = [vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, i64, i64, i32, vp, vp, vp,
+                                         i64, vp, i64, vp]
     return lib
 
 

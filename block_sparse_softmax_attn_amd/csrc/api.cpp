@@ -108,7 +108,7 @@ int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
     if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
-    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv) return ATTN_EINVAL;
+    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv && meta_heads != B * H) return ATTN_EINVAL;
     if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
     if (prepared) {
@@ -275,7 +275,7 @@ int bwd_sparse(const void* q, const void* k, const void* v, const void* o, const
                        ws_bytes);
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
-    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv) return ATTN_EINVAL;
+    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv && meta_heads != B * H) return ATTN_EINVAL;
     if (!row_ptr || !t_row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags || !t_col)) return ATTN_EINVAL;
     bsattn::BwdArgs a = make_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, scale, causal, workspace);
@@ -472,5 +472,59 @@ extern "C" int attn_merge(const float* o_parts, const float* lse_parts, int64_t 
     const hipError_t e = bsattn::launch_merge(o_parts, lse_parts, static_cast<int>(num_parts), B * H,
                                               static_cast<int>(N), static_cast<int>(d), o, lse,
                                               out_dtype == ATTN_BF16, stream);
+    return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
+}
+
+// ---------------------------------------------------------------------------
+// mean-pooled block selector
+// ---------------------------------------------------------------------------
+
+extern "C" int64_t attn_select_meanpool_nnz(int64_t B, int64_t H, int64_t N, int64_t block, int causal,
+                                            int64_t topk) {
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (block != 64 && block != 128) || (causal != 0 && causal != 1))
+        return -1;
+    if (topk < 1 || topk > bsattn::select_max_topk()) return -1;
+    const int64_t nb = (N + block - 1) / block;
+    if (nb > bsattn::select_max_blocks() || B > (int64_t(1) << 40) / H) return -1;
+    const int64_t n = bsattn::select_nnz(B * H, nb, topk, causal);
+    return n > INT32_MAX ? -1 : n;
+}
+
+extern "C" int64_t attn_select_meanpool_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                                        int64_t block) {
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128) || (block != 64 && block != 128)) return -1;
+    if (!valid_groups(H, Hkv) || B > (int64_t(1) << 40) / H) return -1;
+    const int64_t nb = (N + block - 1) / block;
+    return (B * H + B * Hkv) * nb * d * 4;
+}
+
+extern "C" int attn_select_meanpool(const void* q, const void* k, int64_t B, int64_t H, int64_t Hkv, int64_t N,
+                                    int64_t d, int dtype, float scale, int causal, int64_t block, int64_t topk,
+                                    int share_groups, int32_t* row_ptr, int32_t* col, uint8_t* flags,
+                                    int64_t capacity, void* workspace, int64_t workspace_bytes_given,
+                                    hipStream_t stream) {
+    if (!q || !k || !row_ptr || !col || !flags || !workspace) return ATTN_EINVAL;
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
+    if (d != 64 && d != 128) return ATTN_EUNSUPPORTED;
+    if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_EINVAL;
+    if (share_groups != 0 && share_groups != 1) return ATTN_EINVAL;
+    if (topk < 1 || B < 1 || H < 1 || N < 1 || N > kMaxN || (causal != 0 && causal != 1)) return ATTN_EINVAL;
+    if (topk > bsattn::select_max_topk() || (N + block - 1) / block > bsattn::select_max_blocks())
+        return ATTN_EUNSUPPORTED;
+    const int64_t nnz = attn_select_meanpool_nnz(B, H, N, block, causal, topk);
+    if (nnz < 0) return ATTN_EINVAL;
+    const int64_t need = attn_select_meanpool_workspace_bytes(B, H, Hkv, N, d, block);
+    if (need < 0) return ATTN_EINVAL;
+    if (capacity < nnz || workspace_bytes_given < need) return ATTN_ECAPACITY;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(workspace)) return ATTN_EINVAL;
+    if (B * H * N > (int64_t(1) << 40) / d) return ATTN_EINVAL;
+    const int64_t nb = (N + block - 1) / block;
+    float* qm = static_cast<float*>(workspace);
+    float* km = qm + B * H * nb * d;
+    const hipError_t e = bsattn::launch_select(q, k, dtype == ATTN_BF16, B, static_cast<int>(H),
+                                               static_cast<int>(Hkv), static_cast<int>(N), static_cast<int>(d),
+                                               scale, causal, static_cast<int>(block), static_cast<int>(topk),
+                                               share_groups, row_ptr, col, flags, qm, km, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }

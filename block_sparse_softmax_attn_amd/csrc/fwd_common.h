@@ -61,6 +61,16 @@ __host__ __device__ inline int64_t meta_of(int64_t bh, int H, int Hkv, int meta_
     return bh;
 }
 
+// Mean-pooled block selector: block means of Q and K into qm, km (fp32
+// workspace), then the canonical per-(batch, head) CSR of the top-k key blocks
+// of every query block.  select_nnz gives its entry count.
+hipError_t launch_select(const void* q, const void* k, bool bf16, int64_t B, int H, int Hkv, int N, int d,
+                         float scale, int causal, int block, int topk, int share, int32_t* row_ptr, int32_t* col,
+                         uint8_t* flags, float* qm, float* km, hipStream_t stream);
+int64_t select_nnz(int64_t BH, int64_t nb, int64_t topk, int causal);
+int64_t select_max_blocks();
+int64_t select_max_topk();
+
 // Merge nsplit normalised partial states (o_part, lse_part as in FwdArgs)
 // into O (bf16 when out_bf16, else fp32) and LSE.
 hipError_t launch_merge(const float* o_part, const float* lse_part, int nsplit, int64_t BH, int N, int d,

@@ -1,0 +1,253 @@
+// Mean-pooled block selector on the device, for gfx950.
+//
+// Source: "Exact Blocks, Rings, and Sparsity", section 5, "Fixed pooling": a
+// key block is summarised by the mean of its keys, and the mean logit of a
+// query over the block is scale q . k_bar.  The block-sparse kernel's unit is
+// a query tile, so a (query block a, key block b) pair is scored by the mean
+// logit of the whole tile, scale q_bar_a . k_bar_b (linearity), and C_a is the
+// top-k key blocks of that score (ties to the lower index; causal candidates
+// kb <= a).  With grouped-query attention the group's query heads can share
+// one choice: their scores are averaged (by averaging q_bar, the same thing
+// by linearity) and every head of the group gets the same list, so the group
+// loads one set of K/V blocks.
+//
+// Two kernels, both far off the attention's critical cost (section 5: the
+// selector must cost less than the tiles it skips):
+//   pool:   block means of Q and K in fp32, one read of each (HBM-bound);
+//   select: per head, 8 query blocks per workgroup; each thread scores the
+//           key blocks it owns against the 8 pooled queries (k_bar is read
+//           once per 8 query blocks), then one wave per query block takes the
+//           top-k by repeated wave-wide argmax and writes the canonical CSR
+//           row (ascending, unique) with its flags, straight into the
+//           metadata the block-sparse kernels read.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsattn.h"
+#include "fwd_common.h"
+#include "gfx950_util.h"
+
+namespace bsattn {
+namespace {
+
+constexpr int kRowsPerWg = 8;          // query blocks per select workgroup
+constexpr int kMaxBlocks = 2048;       // key blocks per head the select kernel holds
+constexpr int kMaxTopk = 64;
+
+template <typename T>
+__device__ __forceinline__ float to_f32(T x) {
+    return (float)x;
+}
+
+// out[h][blk][c] = mean over the rows of block blk of x[h][row][c].
+template <int D, typename T>
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, float* __restrict__ out, int N,
+                                                   int block, int nb) {
+    constexpr int RG = 256 / D;   // row groups
+    __shared__ float part[RG][D];
+    const int blk = blockIdx.x;
+    const int64_t h = blockIdx.y;
+    const int c = threadIdx.x % D, rg = threadIdx.x / D;
+    const int r0 = blk * block, r1 = min(N, r0 + block);
+    const T* src = x + h * (int64_t)N * D;
+    float acc = 0.f;
+    for (int r = r0 + rg; r < r1; r += RG) acc += to_f32(src[(int64_t)r * D + c]);
+    part[rg][c] = acc;
+    __syncthreads();
+    if (rg == 0) {
+        float s = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) s += part[g][c];
+        out[(h * nb + blk) * (int64_t)D + c] = s / (float)(r1 - r0);
+    }
+}
+
+struct SelArgs {
+    const float* qm;     // [BH][nb][D]
+    const float* km;     // [B*Hkv][nb][D]
+    int32_t* row_ptr;    // [BH*nb + 1]
+    int32_t* col;
+    uint8_t* flags;
+    int64_t BH;
+    int H, Hkv, N, block, nb, topk, causal, share;
+    float scale;
+};
+
+// entries of rows 0..qb-1 of one head
+__device__ __forceinline__ int64_t row_start(int qb, int topk, int nb, int causal) {
+    if (!causal) return (int64_t)qb * min(topk, nb);
+    if (qb <= topk) return (int64_t)qb * (qb + 1) / 2;
+    return (int64_t)topk * (topk + 1) / 2 + (int64_t)(qb - topk) * topk;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
+    __shared__ float qs[kRowsPerWg][D];
+    __shared__ float sc[kRowsPerWg][kMaxBlocks];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nwg_h = (a.nb + kRowsPerWg - 1) / kRowsPerWg;
+    const int64_t bh = blockIdx.x / nwg_h;
+    const int qb0 = (int)(blockIdx.x % nwg_h) * kRowsPerWg;
+    const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
+    const int group = a.H / a.Hkv;
+
+    // pooled queries of this workgroup's query blocks (the group mean when shared)
+    for (int i = tid; i < kRowsPerWg * D; i += 256) {
+        const int rr = i / D, c = i % D, qb = qb0 + rr;
+        float v = 0.f;
+        if (qb < a.nb) {
+            if (a.share) {
+                const int64_t h0 = (bh / a.H) * a.H + ((bh % a.H) / group) * group;
+                for (int g = 0; g < group; ++g) v += a.qm[((h0 + g) * a.nb + qb) * (int64_t)D + c];
+                v /= (float)group;
+            } else {
+                v = a.qm[(bh * a.nb + qb) * (int64_t)D + c];
+            }
+        }
+        qs[rr][c] = v * a.scale;
+    }
+    __syncthreads();
+    // scores of every candidate key block against the pooled queries
+    const int last = min(a.nb, qb0 + kRowsPerWg) - 1;
+    const int ncand_max = a.causal ? last + 1 : a.nb;
+    for (int kb = tid; kb < ncand_max; kb += 256) {
+        const float* kr = a.km + (kvh * a.nb + kb) * (int64_t)D;
+        float s[kRowsPerWg];
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerWg; ++rr) s[rr] = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < D; c += 4) {
+            const float4 kv = *reinterpret_cast<const float4*>(kr + c);
+#pragma unroll
+            for (int rr = 0; rr < kRowsPerWg; ++rr)
+                s[rr] += qs[rr][c] * kv.x + qs[rr][c + 1] * kv.y + qs[rr][c + 2] * kv.z + qs[rr][c + 3] * kv.w;
+        }
+#pragma unroll
+        for (int rr = 0; rr < kRowsPerWg; ++rr) sc[rr][kb] = s[rr];
+    }
+    __syncthreads();
+
+    // top-k per query block: one wave per row, candidates kb = lane + 64 j
+    constexpr int J = kMaxBlocks / 64;
+    const int64_t per_head = row_start(a.nb, a.topk, a.nb, a.causal);
+    for (int rr = w; rr < kRowsPerWg; rr += 4) {
+        const int qb = qb0 + rr;
+        if (qb >= a.nb) break;
+        const int ncand = a.causal ? qb + 1 : a.nb;
+        const int kk = min(a.topk, ncand);
+        float sv[J];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = lane + 64 * j;
+            sv[j] = c < ncand ? sc[rr][c] : -__builtin_inff();
+        }
+        uint32_t chosen = 0u;   // bit j: candidate lane + 64 j is selected
+        for (int round = 0; round < kk; ++round) {
+            float bv = -__builtin_inff();
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int c = lane + 64 * j;
+                if (c < ncand && !((chosen >> j) & 1u) && sv[j] > bv) {   // strict: the lower index wins ties
+                    bv = sv[j];
+                    bi = c;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (ov > bv || (ov == bv && oi < bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if ((bi & 63) == lane) chosen |= 1u << (bi >> 6);
+        }
+        // write the row in ascending order: ballot per 64-candidate slice
+        const int64_t start = bh * per_head + row_start(qb, a.topk, a.nb, a.causal);
+        const int r = (int)(bh * a.nb + qb);
+        if (lane == 0) a.row_ptr[r] = (int32_t)start;
+        if (lane == 0 && r == a.BH * a.nb - 1) a.row_ptr[r + 1] = (int32_t)(start + kk);
+        int written = 0;
+        const bool partial = (a.N % a.block) != 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const bool f = (chosen >> j) & 1u;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(f);
+            if (f) {
+                const int c = lane + 64 * j;
+                const int pos = written + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                a.col[start + pos] = c;
+                uint8_t fl = 0;
+                if (a.causal && c == qb && a.block > 1) fl |= ATTN_FLAG_DIAGONAL;
+                if (partial && c == a.nb - 1) fl |= ATTN_FLAG_PARTIAL;
+                a.flags[start + pos] = fl;
+            }
+            written += __builtin_popcountll(m);
+        }
+    }
+}
+
+}  // namespace
+
+int64_t select_nnz(int64_t BH, int64_t nb, int64_t topk, int causal) {
+    int64_t per;
+    if (!causal) per = nb * (topk < nb ? topk : nb);
+    else if (nb <= topk) per = nb * (nb + 1) / 2;
+    else per = topk * (topk + 1) / 2 + (nb - topk) * topk;
+    return BH * per;
+}
+
+int64_t select_max_blocks() { return kMaxBlocks; }
+int64_t select_max_topk() { return kMaxTopk; }
+
+hipError_t launch_select(const void* q, const void* k, bool bf16, int64_t B, int H, int Hkv, int N, int d,
+                         float scale, int causal, int block, int topk, int share, int32_t* row_ptr, int32_t* col,
+                         uint8_t* flags, float* qm, float* km, hipStream_t stream) {
+    const int nb = (N + block - 1) / block;
+    const dim3 gq((unsigned)nb, (unsigned)(B * H)), gk((unsigned)nb, (unsigned)(B * Hkv));
+    if (d == 64) {
+        if (bf16) {
+            hipLaunchKernelGGL((pool_kernel<64, __bf16>), gq, dim3(256), 0, stream, (const __bf16*)q, qm, N, block, nb);
+            hipLaunchKernelGGL((pool_kernel<64, __bf16>), gk, dim3(256), 0, stream, (const __bf16*)k, km, N, block, nb);
+        } else {
+            hipLaunchKernelGGL((pool_kernel<64, float>), gq, dim3(256), 0, stream, (const float*)q, qm, N, block, nb);
+            hipLaunchKernelGGL((pool_kernel<64, float>), gk, dim3(256), 0, stream, (const float*)k, km, N, block, nb);
+        }
+    } else {
+        if (bf16) {
+            hipLaunchKernelGGL((pool_kernel<128, __bf16>), gq, dim3(256), 0, stream, (const __bf16*)q, qm, N, block, nb);
+            hipLaunchKernelGGL((pool_kernel<128, __bf16>), gk, dim3(256), 0, stream, (const __bf16*)k, km, N, block, nb);
+        } else {
+            hipLaunchKernelGGL((pool_kernel<128, float>), gq, dim3(256), 0, stream, (const float*)q, qm, N, block, nb);
+            hipLaunchKernelGGL((pool_kernel<128, float>), gk, dim3(256), 0, stream, (const float*)k, km, N, block, nb);
+        }
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    SelArgs s;
+    s.qm = qm;
+    s.km = km;
+    s.row_ptr = row_ptr;
+    s.col = col;
+    s.flags = flags;
+    s.BH = B * H;
+    s.H = H;
+    s.Hkv = Hkv;
+    s.N = N;
+    s.block = block;
+    s.nb = nb;
+    s.topk = topk;
+    s.causal = causal;
+    s.share = share;
+    s.scale = scale;
+    const int64_t grid = (int64_t)((nb + kRowsPerWg - 1) / kRowsPerWg) * B * H;
+    if (d == 64)
+        hipLaunchKernelGGL(select_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, s);
+    else
+        hipLaunchKernelGGL(select_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, s);
+    return hipGetLastError();
+}
+
+}  // namespace bsattn

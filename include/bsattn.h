@@ -141,7 +141,8 @@ int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* raw_col,
  *   nnz        : number of entries in col/flags; offsets are clamped to it and
  *                entries outside [0, nqb) are skipped, so malformed metadata
  *                cannot make the kernel read out of bounds.
- *   meta_heads : 1 (one pattern for every (b,h)) or H (pattern h for head h).
+ *   meta_heads : 1 (one pattern for every (b,h)), H (pattern h for head h) or
+ *                B*H (pattern b*H + h, as the device selector writes).
  * No workspace: a key block is visited by only a few query blocks, so the
  * kernel transposes each V tile it loads on chip rather than in a separate
  * pass over all of V.
@@ -364,6 +365,40 @@ int attn_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const 
                              const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz,
                              const int32_t* t_row_ptr, const int32_t* t_col, int64_t meta_heads,
                              void* workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Mean-pooled block selector: builds the active key-block sets C_a on the
+ * device.  Source: "Exact Blocks, Rings, and Sparsity", section 5, "Fixed
+ * pooling: a cheap proxy, not the true block mass" (a key block is
+ * represented by the mean of its keys; ranking by the mean logit approximates
+ * ranking by block mass when the block is homogeneous) and "The selector must
+ * cost less than the tiles it skips" (GQA: heads of a group share one choice).
+ *   score(a, b) = scale * mean(Q rows of query block a) . mean(K rows of key
+ *   block b), the mean logit of the tile (means over the tokens a block holds);
+ *   C_a = the topk highest-scoring candidates (every key block, or kb <= a when
+ *   causal), ties to the lower index, written ascending.
+ *   q : device [B,H,N,d], k : device [B,Hkv,N,d] (ATTN_BF16 or ATTN_F32).
+ *   block in {64, 128}; topk in [1, 64]; ceil(N/block) <= 2048.
+ *   share_groups : 1 averages the scores of each group's H/Hkv query heads and
+ *                  gives every head of the group the same list; 0 selects per head.
+ *   row_ptr : device int32 [B*H*nb + 1], col : device int32 [capacity],
+ *   flags : device uint8 [capacity]: written; canonical metadata with one
+ *           pattern per (batch, head), b-major (pass meta_heads = B*H to the
+ *           block-sparse entry points).  nnz = attn_select_meanpool_nnz(...).
+ *   workspace : device, attn_select_meanpool_workspace_bytes(...) bytes (the
+ *               fp32 block means), 16-byte aligned.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype, d, block, too many blocks),
+ *   ATTN_ECAPACITY (capacity or workspace too small), ATTN_EHIP.
+ */
+int64_t attn_select_meanpool_nnz(int64_t B, int64_t H, int64_t N, int64_t block, int causal, int64_t topk);
+
+int64_t attn_select_meanpool_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                             int64_t block);
+
+int attn_select_meanpool(const void* q, const void* k, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                         int dtype, float scale, int causal, int64_t block, int64_t topk, int share_groups,
+                         int32_t* row_ptr, int32_t* col, uint8_t* flags, int64_t capacity, void* workspace,
+                         int64_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -348,3 +348,37 @@ def test_gqa_workspace_and_bad_groups(m):
     # forward workspace is V^T of the key/value heads
     assert lib.attn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 1, f, 0, FAKE, 2 * 64 * 256 * 2 - 16,
                             None) == -3
+
+
+# ---------------------------------------------------------------------------
+# mean-pooled selector (argument checks and closed forms only)
+# ---------------------------------------------------------------------------
+
+def test_select_nnz_and_workspace(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    # non-causal: every row keeps min(topk, nb); causal: row qb keeps min(topk, qb + 1)
+    assert lib.attn_select_meanpool_nnz(2, 3, 1000, 64, 0, 4) == 6 * 16 * 4
+    assert lib.attn_select_meanpool_nnz(1, 1, 1000, 64, 1, 4) == sum(min(4, qb + 1) for qb in range(16))
+    assert lib.attn_select_meanpool_nnz(1, 1, 100, 128, 0, 8) == 1
+    assert lib.attn_select_meanpool_nnz(1, 8, 131072, 128, 1, 16) == 8 * sum(min(16, qb + 1) for qb in range(1024))
+    assert lib.attn_select_meanpool_nnz(1, 1, 1000, 32, 0, 4) == -1        # block
+    assert lib.attn_select_meanpool_nnz(1, 1, 1000, 64, 0, 0) == -1        # topk
+    assert lib.attn_select_meanpool_nnz(1, 1, 1000, 64, 0, 65) == -1
+    assert lib.attn_select_meanpool_nnz(1, 1, 2049 * 128, 128, 0, 4) == -1  # too many blocks
+    assert lib.attn_select_meanpool_workspace_bytes(1, 8, 2, 1000, 128, 64) == (8 + 2) * 16 * 128 * 4
+    assert lib.attn_select_meanpool_workspace_bytes(1, 8, 3, 1000, 128, 64) == -1
+
+
+def test_select_rejects_bad_arguments(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    f = ctypes.c_float(0.1)
+    call = lambda **kw: lib.attn_select_meanpool(kw.get("q", FAKE), FAKE, 1, 4, kw.get("hkv", 2), 1000, kw.get("d", 64),
+                                                 kw.get("dt", 1), ctypes.c_float(kw.get("sc", 0.1)), 1,
+                                                 kw.get("blk", 64), kw.get("topk", 4), kw.get("share", 0), FAKE, FAKE,
+                                                 FAKE, kw.get("cap", 1 << 20), FAKE, kw.get("ws", 1 << 24), None)
+    assert call(q=None) == -1 and call(sc=0.0) == -1 and call(share=2) == -1 and call(hkv=3) == -1
+    assert call(d=96) == -2 and call(dt=7) == -2 and call(blk=32) == -2 and call(topk=65) == -2
+    assert call(topk=0) == -1
+    assert call(cap=10) == -3 and call(ws=100) == -3
