@@ -28,7 +28,11 @@ that measures the sustained matrix-core rate next to the published peak),
 --pmc to calibrate the byte counters), --pass bwd (time the backward instead:
 one step = one attn_bwd / attn_bwd_blocksparse call on the workload's shapes,
 10*d flops per allowed pair for the recomputed S and the dP, dV, dK, dQ
-products; its cpu_baseline is the float64 gradient oracle).
+products; its cpu_baseline is the float64 gradient oracle), --pass select
+(one step = the device mean-pooled selector, --topk blocks of 128 per query
+block, then the block-sparse forward on its output, on the workload's shapes
+with causal masking; reports the selector's cost against the dense tiles it
+lets the forward skip).
 """
 from __future__ import annotations
 
@@ -144,7 +148,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"])
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "select"])
+    ap.add_argument("--topk", type=int, default=16)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -168,6 +173,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.which == "bwd":
         bench_bwd(args, cfg, dev)
+        return
+    if args.which == "select":
+        bench_select(args, cfg, dev)
         return
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)
@@ -359,6 +367,78 @@ def bench_bwd(args, cfg, dev):
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline_bwd(cfg, q, k, v, do, mask_lists)
+    print(json.dumps(rec), flush=True)
+
+
+def _time_calls(fn, steps, warmup, stream):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps * 1e3, sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+
+
+def bench_select(args, cfg, dev):
+    """Selector + block-sparse forward against the dense causal forward on the
+    workload's shapes (block 128)."""
+    import torch
+    import block_sparse_softmax_attn_amd as attn
+
+    block, topk = 128, int(args.topk)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    q, k, v = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
+               .to(torch.bfloat16).contiguous() for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+    lib = attn._get_lib()
+    sel_ws = torch.empty(lib.attn_select_meanpool_workspace_bytes(cfg.B, cfg.H, cfg.H, cfg.N, cfg.d, block),
+                         dtype=torch.uint8, device=dev)
+    state = {}
+
+    def select():
+        state["mask"] = attn.select_meanpool(q, k, block, topk, causal=True, scale=cfg.scale, workspace=sel_ws)
+
+    def step():
+        select()
+        attn.attn_fwd_blocksparse(q, k, v, state["mask"], scale=cfg.scale, causal=True, out=o, lse=lse)
+
+    select()
+    mask = state["mask"]
+    pairs = int(mask.allowed_pairs.sum())       # one count per (batch, head) pattern
+    executed_tiles = int(mask.executed_tile_pairs.sum())
+    nb = -(-cfg.N // block)
+    dense_tiles = cfg.B * cfg.H * nb * (nb + 1) // 2
+    wall_ms, step_ms = _time_calls(step, args.steps, args.warmup, stream)
+    _, sel_ms = _time_calls(select, args.steps, args.warmup, stream)
+    ws = torch.empty(attn.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    _, dense_ms = _time_calls(lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse,
+                                                    workspace=ws), max(3, args.steps // 10), 2, stream)
+    flops = 4 * cfg.d * pairs
+    skipped = dense_tiles - executed_tiles
+    rec = {
+        "metric": "attention fwd TFLOP/s (allowed pairs of the selected pattern, selector included), 1\u00d7MI355X",
+        "value": round(flops / (wall_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.description + f", mean-pooled top-{topk} of 128-token blocks, causal",
+                   "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "block": block, "topk": topk,
+                   "allowed_pairs": pairs, "executed_tiles": executed_tiles, "dense_causal_tiles": dense_tiles,
+                   "parallelism": "single GPU"},
+        "selector": {"mean_ms": round(sel_ms, 5), "dense_causal_forward_ms": round(dense_ms, 4),
+                     "skipped_tiles": skipped,
+                     "skipped_tile_time_ms_estimate": round(dense_ms * skipped / dense_tiles, 4),
+                     "selector_cost_over_skipped_work": round(sel_ms / (dense_ms * skipped / dense_tiles), 5),
+                     "step_speedup_over_dense": round(dense_ms / step_ms, 3)},
+    }
     print(json.dumps(rec), flush=True)
 
 
