@@ -88,26 +88,37 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict
 // dK, dV: key-stationary
 // ---------------------------------------------------------------------------
 
-template <int D, int NW>
+template <int D, int NW, bool PAIRED>
 struct DkdvGeo {
     static constexpr int NT = 64 * NW;
-    static constexpr int BKV = 32 * NW;              // keys per workgroup
+    static constexpr int PAIRS = PAIRED ? NW / 2 : NW;   // 32-key slices per workgroup
+    static constexpr int BKV = 32 * PAIRS;               // keys per workgroup
     static constexpr int TB = BT * D * 2;            // bytes of a Q, dO, Q^T or dO^T tile
     static constexpr int PER_T = TB / 1024 / NW;     // 1 KiB direct-to-LDS loads per wave per tile
-    static_assert(TB % (1024 * NW) == 0, "tile must split over waves");
+    static_assert((!PAIRED || NW % 2 == 0) && TB % (1024 * NW) == 0, "tile must split over waves");
     static_assert(4 * PER_T + 1 < 64, "vmcnt range");
 };
 
-template <int D, int NW, int MODE>
-__global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdArgs a) {
-    using G = DkdvGeo<D, NW>;
+// PAIRED (d = 128): two waves share each 32-key slice: the P wave (role 0)
+// computes S = Q K^T, P and dV^T += dO^T P; the dS wave (role 1) computes
+// dP = dO V^T, reads the rounded P from LDS, forms dS = P (dP - D) and
+// dK^T += Q^T dS.  Each keeps one operand row set and one accumulator, so both
+// fit two waves per SIMD and their MFMA and VALU phases overlap; the P
+// hand-over costs one extra barrier per tile.  Single (d = 64, where one wave
+// holding K, V, dK and dV already fits two waves per SIMD): each wave does all
+// four products for its 32 keys.
+template <int D, int NW, int MODE, bool PAIRED>
+__global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
+    using G = DkdvGeo<D, NW, PAIRED>;
     __shared__ __attribute__((aligned(1024))) unsigned char sQ0[G::TB], sQ1[G::TB], sO0[G::TB], sO1[G::TB];
     __shared__ __attribute__((aligned(1024))) unsigned char sQT0[G::TB], sQT1[G::TB], sOT0[G::TB], sOT1[G::TB];
-    __shared__ __attribute__((aligned(1024))) float sS0[NW][256], sS1[NW][256];
+    __shared__ __attribute__((aligned(1024))) float sS0[256], sS1[256];
+    __shared__ __attribute__((aligned(16))) bf16x8 sP[PAIRED ? G::PAIRS : 1][2][2][64];   // [pair][block][step][lane]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
+    const int role = PAIRED ? w / G::PAIRS : 0, pw = PAIRED ? w % G::PAIRS : w;
     const int N = a.N;
     const int nkt = (N + G::BKV - 1) / G::BKV;
     // one workgroup per (key/value head, key tile); it sums the contributions
@@ -119,7 +130,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
     const int kt = (int)(ord % nkt);   // causal: the first key tiles see the most queries and start first
     const int64_t bh0 = (kvbh / a.Hkv) * a.H + (kvbh % a.Hkv) * group;   // first query head of the group
     const int kb0 = kt * G::BKV;
-    const int kw0 = kb0 + 32 * w;      // this wave's first key
+    const int kw0 = kb0 + 32 * pw;     // this wave pair's first key
     const int kj = kw0 + l32;          // this lane's key
     const int nblk = a.npad / BT;
     const bool causal = MODE == (int)Mode::kCausal || (MODE == (int)Mode::kSparse && a.causal);
@@ -230,38 +241,147 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
             dma16(dOTh + q0 + tr_off[i], dOT + off);
         }
         // row statistics of this block (lanes 0-31) and of the next (32-63)
-        dma16(Sh + (q0 / BT) * 128 + lane * 4, u ? sS1[w] : sS0[w]);
+        if (w == 0) dma16(Sh + (q0 / BT) * 128 + lane * 4, u ? sS1 : sS0);
     };
 
-    // this lane's key and value rows: B operands of S = Q K^T and dP = dO V^T
-    bf16x8 kf[D / 16], vf[D / 16];
-    {
+    // ---- operands, accumulators and one tile's math for each design ----
+    bf16x8 kvf[D / 16];          // paired: K (P wave) or V (dS wave) rows
+    f32x16 acc[D / 32];          // paired: dV^T (P wave) or dK^T (dS wave)
+    bf16x8 kf[PAIRED ? 1 : D / 16], vf[PAIRED ? 1 : D / 16];
+    f32x16 dkacc[PAIRED ? 1 : D / 32], dvacc[PAIRED ? 1 : D / 32];
+    if constexpr (PAIRED) {
+        // this lane's key row (P wave: B operand of S = Q K^T) or value row
+        // (dS wave: B operand of dP = dO V^T)
+        const int row = min(kj, N - 1);
+        const __bf16* src = (role == 0 ? Kh : Vh) + (int64_t)row * D + 8 * hi;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) kvf[k] = *reinterpret_cast<const bf16x8*>(src + 16 * k);
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
+    } else {
+        // this lane's key and value rows: B operands of S = Q K^T and dP = dO V^T
         const int row = min(kj, N - 1);
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) {
             kf[k] = *reinterpret_cast<const bf16x8*>(Kh + (int64_t)row * D + 16 * k + 8 * hi);
             vf[k] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)row * D + 16 * k + 8 * hi);
         }
+#pragma unroll
+        for (int i = 0; i < D / 32; ++i) {
+            dkacc[i] = f32x16{};
+            dvacc[i] = f32x16{};
+        }
     }
     wait_vmcnt<0>();
-
-    f32x16 dkacc[D / 32], dvacc[D / 32];
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-        dkacc[i] = f32x16{};
-        dvacc[i] = f32x16{};
-    }
     const float sl2 = a.scale_log2;
 
-    // One 64-query tile for this wave, as two 32-query blocks.  Each phase
-    // loads all of its LDS operands first, then issues its MFMAs, so the
-    // matrix pipe is not stalled by one LDS round trip per product.
-    auto compute = [&](int q0, int u) {
+    // One 64-query tile, as two 32-query blocks.  Phase 1: S (P wave) or dP
+    // (dS wave) for both blocks; the P wave writes the rounded P to LDS.
+    // Barrier.  Phase 2: dV (P wave, P still in registers) or dS and dK (dS
+    // wave).  Every wave reaches the barrier, also when the causal mask leaves
+    // it nothing to do.
+    auto compute_paired = [&](int q0, int u) {
         const unsigned char* bQ = u ? sQ1 : sQ0;
         const unsigned char* bO = u ? sO1 : sO0;
         const unsigned char* bQT = u ? sQT1 : sQT0;
         const unsigned char* bOT = u ? sOT1 : sOT0;
-        const float* st = u ? sS1[w] : sS0[w];
+        const float* st = u ? sS1 : sS0;
+        bool live[2];
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) live[qc] = !(causal && q0 + 32 * qc + 31 < kw0);
+        // ---- phase 1: queries as rows, lane (l32, hi) gets query
+        // q0 + 32qc + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
+        f32x16 pr[2];
+        bf16x8 pb[2][2];
+        const unsigned char* bA = role == 0 ? bQ : bO;
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+            pr[qc] = f32x16{};
+            if (!live[qc]) continue;
+            const int r = 32 * qc + l32;
+            bf16x8 fa[D / 16];
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k)
+                fa[k] = *reinterpret_cast<const bf16x8*>(bA + r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16);
+            __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+            for (int k = 0; k < D / 16; ++k) pr[qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], kvf[k], pr[qc], 0, 0, 0);
+        }
+        if (role == 0) {
+#pragma unroll
+            for (int qc = 0; qc < 2; ++qc) {
+                if (!live[qc]) continue;
+                const int qb0 = q0 + 32 * qc;
+                const bool cmask = causal && qb0 < kw0 + 31;
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const float4 l4 = *reinterpret_cast<const float4*>(st + 32 * qc + 8 * g4 + 4 * hi);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 4 * g4 + e;
+                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pr[qc][v], sl2, -lv[e]));
+                        if (cmask && kj > qb0 + 8 * g4 + 4 * hi + e) p = 0.f;
+                        pb[qc][v >> 3][v & 7] = (__bf16)p;
+                    }
+                }
+                sP[pw][qc][0][lane] = pb[qc][0];
+                sP[pw][qc][1][lane] = pb[qc][1];
+            }
+        }
+        barrier();
+        // ---- phase 2 ----
+#pragma unroll
+        for (int qc = 0; qc < 2; ++qc) {
+            if (!live[qc]) continue;
+            bf16x8 op[2];
+            if (role == 0) {
+                op[0] = pb[qc][0];
+                op[1] = pb[qc][1];
+            } else {
+                // dS = P (dP - D) from the rounded P, rounded to bf16
+                const bf16x8 p0 = sP[pw][qc][0][lane], p1 = sP[pw][qc][1][lane];
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 32 * qc + 8 * g4 + 4 * hi);
+                    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int v = 4 * g4 + e;
+                        const float p = (float)((v >> 3) ? p1[v & 7] : p0[v & 7]);
+                        op[v >> 3][v & 7] = (__bf16)(p * (pr[qc][v] - dv[e]));
+                    }
+                }
+            }
+            // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave) over two 16-query steps
+            const unsigned char* bT = role == 0 ? bOT : bQT;
+            bf16x8 ta[2][D / 32];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const int d = 32 * db + l32;
+                    ta[t][db] = *reinterpret_cast<const bf16x8*>(bT + d * (2 * BT) + v_swz(d, 2 * (2 * qc + t) + hi) * 16);
+                }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[t][db], op[t], acc[db], 0, 0, 0);
+        }
+    };
+
+
+
+    // One 64-query tile for this wave, as two 32-query blocks.  Each phase
+    // loads all of its LDS operands first, then issues its MFMAs, so the
+    // matrix pipe is not stalled by one LDS round trip per product.
+    auto compute_single = [&](int q0, int u) {
+        const unsigned char* bQ = u ? sQ1 : sQ0;
+        const unsigned char* bO = u ? sO1 : sO0;
+        const unsigned char* bQT = u ? sQT1 : sQT0;
+        const unsigned char* bOT = u ? sOT1 : sOT0;
+        const float* st = u ? sS1 : sS0;
 #pragma unroll
         for (int qc = 0; qc < BT / 32; ++qc) {
             const int qb0 = q0 + 32 * qc;
@@ -324,16 +444,25 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
         }
     };
 
+    auto compute = [&](int q0, int u) {
+        if constexpr (PAIRED) {
+            compute_paired(q0, u);
+        } else {
+            if (causal && q0 + BT - 1 < kw0) return;   // the whole tile precedes this wave's keys
+            compute_single(q0, u);
+        }
+    };
+
     // Tile it sits in buffer it & 1: wait for its loads, barrier (every wave's
-    // loads have landed, every wave is done with tile it-1), refill the other
-    // buffer with tile it+1, compute.
+    // loads have landed, every wave is done with tile it-1 and with its P),
+    // refill the other buffer with tile it+1, compute.
     auto step = [&](int it, int u) {
         wait_vmcnt<0>();
         barrier();
         if (it + 1 < ntiles) issue(locate(it + 1), u ^ 1);
         const int q0 = locate(it).q0;
-        if (q0 < 0 || q0 >= N) return;
-        if (causal && q0 + BT - 1 < kw0) return;   // the whole tile precedes this wave's keys
+        if (q0 < 0 || q0 >= N) return;                  // the same for every wave
+        if (causal && q0 + BT - 1 < kb0) return;         // the whole tile precedes every key of the workgroup
         compute(q0, u);
     };
     if (ntiles > 0) issue(locate(0), 0);
@@ -342,7 +471,7 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
         if (base + 1 < ntiles) step(base + 1, 1);
     }
 
-    // ---- epilogue: dK = scale * (Q^T dS)^T, dV = (dO^T P)^T ----
+    // ---- epilogue: dV = (dO^T P)^T, dK = scale * (Q^T dS)^T ----
     if (kj < N) {
         __bf16* dKr = static_cast<__bf16*>(a.dk) + (kvbh * N + kj) * (int64_t)D;
         __bf16* dVr = static_cast<__bf16*>(a.dv) + (kvbh * N + kj) * (int64_t)D;
@@ -350,14 +479,22 @@ __global__ __launch_bounds__(64 * NW, NW >= 8 ? 2 : 1) void bwd_dkdv_kernel(BwdA
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                const int c = 32 * db + 8 * j + 4 * hi;
                 bf16x4 kv, vv;
+                if constexpr (PAIRED) {
+                    const float f = role == 0 ? 1.0f : a.scale;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    kv[i] = (__bf16)(dkacc[db][4 * j + i] * a.scale);
-                    vv[i] = (__bf16)dvacc[db][4 * j + i];
+                    for (int i = 0; i < 4; ++i) kv[i] = (__bf16)(acc[db][4 * j + i] * f);
+                    *reinterpret_cast<bf16x4*>((role == 0 ? dVr : dKr) + c) = kv;
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        kv[i] = (__bf16)(dkacc[db][4 * j + i] * a.scale);
+                        vv[i] = (__bf16)dvacc[db][4 * j + i];
+                    }
+                    *reinterpret_cast<bf16x4*>(dKr + c) = kv;
+                    *reinterpret_cast<bf16x4*>(dVr + c) = vv;
                 }
-                *reinterpret_cast<bf16x4*>(dKr + 32 * db + 8 * j + 4 * hi) = kv;
-                *reinterpret_cast<bf16x4*>(dVr + 32 * db + 8 * j + 4 * hi) = vv;
             }
     }
 }
@@ -578,11 +715,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 // launchers
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int MODE>
+template <int D, int NW, int MODE, bool PAIRED = (D == 128)>
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
-    const int64_t nkt = (a.N + 32 * NW - 1) / (32 * NW);
+    const int64_t nkt = (a.N + DkdvGeo<D, NW, PAIRED>::BKV - 1) / DkdvGeo<D, NW, PAIRED>::BKV;
     const int64_t bhkv = a.BH / (a.H / a.Hkv);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE>), dim3((unsigned)(nkt * bhkv)), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE, PAIRED>), dim3((unsigned)(nkt * bhkv)), dim3(64 * NW), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
@@ -600,22 +738,23 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
                        static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), a.lse, a.stats, a.N, nblk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // dK/dV: 4 waves x 32 keys per workgroup (one key block of a sparse
-    // pattern); dQ: the forward's shapes (8 waves and 3 stages dense/causal,
+    // dK/dV: 128 keys per workgroup (one key block of a sparse pattern; 64 for
+    // 64-key blocks): 4 wave pairs for d = 128, 4 single waves for d = 64;
+    // dQ: the forward's shapes (8 waves and 3 stages dense/causal,
     // one query block and 2 stages block-sparse).
     switch (mode) {
         case Mode::kDense:
-            e = launch_dkdv<D, 4, (int)Mode::kDense>(a, stream);
+            e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kDense>(a, stream);
             return e != hipSuccess ? e : launch_dq<D, 8, 3, (int)Mode::kDense>(a, stream);
         case Mode::kCausal:
-            e = launch_dkdv<D, 4, (int)Mode::kCausal>(a, stream);
+            e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kCausal>(a, stream);
             return e != hipSuccess ? e : launch_dq<D, 8, 3, (int)Mode::kCausal>(a, stream);
         case Mode::kSparse:
             if (a.block == 128) {
-                e = launch_dkdv<D, 4, (int)Mode::kSparse>(a, stream);
+                e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kSparse>(a, stream);
                 return e != hipSuccess ? e : launch_dq<D, 4, 2, (int)Mode::kSparse>(a, stream);
             }
-            e = launch_dkdv<D, 2, (int)Mode::kSparse>(a, stream);
+            e = launch_dkdv<D, D == 64 ? 2 : 4, (int)Mode::kSparse>(a, stream);
             return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse>(a, stream);
         case Mode::kRange: break;   // no backward for key-range launches
     }
