@@ -3,11 +3,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
 A step is one pass of the hot path over one batch of synthetic N(0,1) bf16
-input already resident in HBM.  Dense and causal: host validation and launch
-of the V transpose into the workspace, then of the fused kernel (exactly the
-two launches attn_fwd makes, issued through the two-step entry points so each
-is timed).  Block-sparse: the single launch attn_fwd_blocksparse makes (its
-kernel transposes the V tiles it visits itself).  The default workload is the
+input already resident in HBM: one attn_fwd (dense, causal) or
+attn_fwd_blocksparse call, i.e. host validation and the single launch of the
+fused kernel, which reads Q, K and V in place.  The default workload is the
 dense non-causal d=128 case (B=1 H=32 N=8192), the one the throughput target
 is stated on.  Prints ONE JSON line:
 
@@ -183,13 +181,9 @@ def main():
                .to(torch.bfloat16).contiguous() for _ in range(3))
     o = torch.empty_like(q)
     lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
-    ws = None if cfg.sparse else torch.empty(attn.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, torch.bfloat16),
-                                             dtype=torch.uint8, device=dev)
 
-    # One step = the bf16 hot path as the one-call entry point runs it: dense
-    # and causal launch the V transpose into the workspace, then the fused
-    # kernel; block-sparse launches only the fused kernel.  Each launch is
-    # timed with HIP events on the launch stream.
+    # One step = one call of the one-call entry point: a single launch of the
+    # fused kernel, timed with HIP events on the launch stream.
     if cfg.sparse:
         rp, col = workloads.config_block_lists(cfg)
         t0 = time.perf_counter()
@@ -200,34 +194,28 @@ def main():
         mask.to_device(dev)
         fused = lambda: attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal,
                                                   out=o, lse=lse)
-        prepare = lambda: None
     else:
         build_ms = None
         pairs = allowed_pairs_dense(cfg)
         executed = None
-        fused = lambda: attn.attn_fwd_prepared(q, k, ws, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
-        prepare = lambda: attn.prepare_v(v, workspace=ws)
+        fused = lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
     flops = 4 * cfg.d * pairs
 
     for _ in range(args.warmup):
-        prepare()
         fused()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        prepare()
-        ev[i][1].record(stream)
         fused()
-        ev[i][2].record(stream)
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    mean_launch_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+    mean_launch_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
 
     value = flops * args.steps / wall / 1e12
     achieved = flops / (mean_launch_ms * 1e-3) / 1e12
@@ -262,7 +250,6 @@ def main():
             "traffic": read_traffic(args.workload),
             "kernel": "fwd_bf16_kernel",
             "mean_launch_ms": round(mean_launch_ms, 5),
-            "v_transpose_mean_ms": None if cfg.sparse else round(prep_ms, 5),
         },
     }
     if executed is not None:
@@ -419,9 +406,8 @@ def bench_select(args, cfg, dev):
     dense_tiles = cfg.B * cfg.H * nb * (nb + 1) // 2
     wall_ms, step_ms = _time_calls(step, args.steps, args.warmup, stream)
     _, sel_ms = _time_calls(select, args.steps, args.warmup, stream)
-    ws = torch.empty(attn.workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, torch.bfloat16), dtype=torch.uint8, device=dev)
-    _, dense_ms = _time_calls(lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse,
-                                                    workspace=ws), max(3, args.steps // 10), 2, stream)
+    _, dense_ms = _time_calls(lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse),
+                              max(3, args.steps // 10), 2, stream)
     flops = 4 * cfg.d * pairs
     skipped = dense_tiles - executed_tiles
     rec = {

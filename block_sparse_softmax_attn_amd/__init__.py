@@ -33,7 +33,7 @@ import numpy as np
 from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN_FLAG_PARTIAL, ATTN_OK,
                    AttnError, LIB_PATH, check, get as _get_lib, status_string)
 
-__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "workspace_bytes", "prepare_v", "attn_fwd_prepared",
+__all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "prepared_v_bytes", "prepare_v", "attn_fwd_prepared",
            "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_blocksparse", "bwd_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_block", "attn_merge", "select_meanpool", "DeviceBlockMask",
            "BlockMask", "AttnError", "LIB_PATH",
@@ -78,27 +78,24 @@ def _outputs(q, out, lse):
     return out, lse
 
 
-def workspace_bytes(B: int, H: int, N: int, d: int, dtype) -> int:
-    """Device workspace (bytes) the forward needs for these sizes."""
-    code = dtype if isinstance(dtype, int) else (ATTN_BF16 if str(dtype).endswith("bfloat16") else ATTN_F32)
-    n = int(_get_lib().attn_fwd_workspace_bytes(int(B), int(H), int(N), int(d), code))
+def prepared_v_bytes(B: int, H: int, N: int, d: int) -> int:
+    """Bytes of the V^T buffer prepare_v writes (bf16) for these sizes."""
+    n = int(_get_lib().attn_prepared_v_bytes(int(B), int(H), int(N), int(d), ATTN_BF16))
     if n < 0:
-        raise ValueError("sizes or dtype not supported")
+        raise ValueError("sizes not supported")
     return n
 
 
-def _workspace(kv, workspace):
-    """The forward's V^T workspace, sized by the key/value heads of ``kv``."""
+def _vt_buffer(B, H, N, d, dev, vt):
+    """A V^T buffer for B*H heads (allocated from torch's caching allocator
+    when ``vt`` is None)."""
     import torch
-    B, H, N, d = kv.shape
-    need = workspace_bytes(B, H, N, d, _dtype_code(kv))
-    if need == 0:
-        return None, 0
-    if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=kv.device)
-    if workspace.device != kv.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
-        raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on the inputs' device")
-    return workspace, workspace.numel() * workspace.element_size()
+    need = prepared_v_bytes(B, H, N, d)
+    if vt is None:
+        vt = torch.empty(need, dtype=torch.uint8, device=dev)
+    if vt.device != dev or not vt.is_contiguous() or vt.numel() * vt.element_size() < need:
+        raise ValueError(f"the V^T buffer must be a contiguous buffer of at least {need} bytes on the inputs' device")
+    return vt, vt.numel() * vt.element_size()
 
 
 def _stream(dev):
@@ -106,28 +103,23 @@ def _stream(dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, lse=None, workspace=None):
-    """Dense or causal attention forward; returns (O in q's dtype, LSE fp32 [B,H,N]).
-
-    ``workspace``: optional device buffer of at least ``workspace_bytes(...)``
-    bytes (allocated per call from torch's caching allocator when omitted)."""
+def attn_fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, out=None, lse=None):
+    """Dense or causal attention forward; returns (O in q's dtype, LSE fp32 [B,H,N])."""
     import torch
     _check_qkv(q, k, v)
     B, H, N, d = q.shape
     Hkv = k.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
-    ws, ws_bytes = _workspace(k, workspace)
-    wsp = ws.data_ptr() if ws is not None else None
     with torch.cuda.device(q.device):
         if Hkv == H:
             st = _get_lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                      B, H, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
-                                     wsp, ws_bytes, _stream(q.device))
+                                     _stream(q.device))
         else:
             st = _get_lib().attn_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                          B, H, Hkv, N, d, _dtype_code(q), ctypes.c_float(scale), int(bool(causal)),
-                                         wsp, ws_bytes, _stream(q.device))
+                                         _stream(q.device))
     check("attn_fwd", st)
     return out, lse
 
@@ -238,39 +230,39 @@ def attn_fwd_blocksparse(q, k, v, mask: BlockMask, scale: Optional[float] = None
     return out, lse
 
 
-def prepare_v(v, workspace=None):
-    """bf16 only: V transposed into a workspace for attn_fwd_prepared /
-    attn_fwd_blocksparse_prepared (returns the workspace)."""
+def prepare_v(v, vt=None):
+    """bf16 only: V transposed into a V^T buffer for attn_fwd_prepared /
+    attn_fwd_blocksparse_prepared (returns the buffer)."""
     import torch
     if v.dim() != 4 or not v.is_cuda or not v.is_contiguous() or v.dtype != torch.bfloat16:
         raise ValueError("v must be a contiguous bfloat16 [B, H, N, d] tensor on a GPU")
     B, H, N, d = v.shape
-    ws, ws_bytes = _workspace(v, workspace)
+    vt, vt_bytes = _vt_buffer(B, H, N, d, v.device, vt)
     with torch.cuda.device(v.device):
-        st = _get_lib().attn_prepare_v(v.data_ptr(), B, H, N, d, ATTN_BF16, ws.data_ptr(), ws_bytes, _stream(v.device))
+        st = _get_lib().attn_prepare_v(v.data_ptr(), B, H, N, d, ATTN_BF16, vt.data_ptr(), vt_bytes, _stream(v.device))
     check("attn_prepare_v", st)
-    return ws
+    return vt
 
 
-def attn_fwd_prepared(q, k, workspace, scale: Optional[float] = None, causal: bool = False, out=None, lse=None):
-    """attn_fwd with V taken from a workspace filled by prepare_v (bf16)."""
+def attn_fwd_prepared(q, k, vt, scale: Optional[float] = None, causal: bool = False, out=None, lse=None):
+    """attn_fwd with V^T taken from a buffer filled by prepare_v (bf16)."""
     import torch
     _check_qkv(q, k, k)
     B, H, N, d = q.shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
-    ws, ws_bytes = _workspace(q, workspace)
+    vt, vt_bytes = _vt_buffer(B, H, N, d, q.device, vt)
     with torch.cuda.device(q.device):
         st = _get_lib().attn_fwd_prepared(q.data_ptr(), k.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d,
-                                          _dtype_code(q), ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(),
-                                          ws_bytes, _stream(q.device))
+                                          _dtype_code(q), ctypes.c_float(scale), int(bool(causal)), vt.data_ptr(),
+                                          vt_bytes, _stream(q.device))
     check("attn_fwd_prepared", st)
     return out, lse
 
 
-def attn_fwd_blocksparse_prepared(q, k, workspace, mask: BlockMask, scale: Optional[float] = None,
+def attn_fwd_blocksparse_prepared(q, k, vt, mask: BlockMask, scale: Optional[float] = None,
                                   causal: Optional[bool] = None, out=None, lse=None):
-    """attn_fwd_blocksparse with V taken from a workspace filled by prepare_v (bf16)."""
+    """attn_fwd_blocksparse with V^T taken from a buffer filled by prepare_v (bf16)."""
     import torch
     _check_qkv(q, k, k)
     B, H, N, d = q.shape
@@ -280,12 +272,12 @@ def attn_fwd_blocksparse_prepared(q, k, workspace, mask: BlockMask, scale: Optio
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out, lse = _outputs(q, out, lse)
     row_ptr, col, flags = mask.to_device(q.device)
-    ws, ws_bytes = _workspace(q, workspace)
+    vt, vt_bytes = _vt_buffer(B, H, N, d, q.device, vt)
     with torch.cuda.device(q.device):
         st = _get_lib().attn_fwd_blocksparse_prepared(
             q.data_ptr(), k.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, N, d, _dtype_code(q),
             ctypes.c_float(scale), int(causal), mask.block, row_ptr.data_ptr(), col.data_ptr(), flags.data_ptr(),
-            mask.nnz, mask.meta_heads, ws.data_ptr(), ws_bytes, _stream(q.device))
+            mask.nnz, mask.meta_heads, vt.data_ptr(), vt_bytes, _stream(q.device))
     check("attn_fwd_blocksparse_prepared", st)
     return out, lse
 
@@ -411,7 +403,7 @@ def attn_fwd_splitkv(q, k, v, scale: Optional[float] = None, causal: bool = Fals
 
 
 def attn_fwd_block(q, k, v, scale: Optional[float] = None, causal: bool = False, q_offset: int = 0,
-                   k_offset: int = 0, o_part=None, lse_part=None, workspace=None):
+                   k_offset: int = 0, o_part=None, lse_part=None):
     """One ring step: fp32 partial state (O_b, LSE_b) of the rows of ``q``
     (global positions q_offset + i) against the key/value block ``k``, ``v``
     (global positions k_offset + j)."""
@@ -429,15 +421,10 @@ def attn_fwd_block(q, k, v, scale: Optional[float] = None, causal: bool = False,
         o_part = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
     if lse_part is None:
         lse_part = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    need = int(_get_lib().attn_fwd_block_workspace_bytes(B, H, Nk, d, ATTN_BF16))
-    if need < 0:
-        raise ValueError("sizes not supported")
-    ws, ws_bytes = _ws_buffer(q.device, need, workspace, align=16)
     with torch.cuda.device(q.device):
         st = _get_lib().attn_fwd_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
                                        lse_part.data_ptr(), B, H, Nq, Nk, d, ATTN_BF16, ctypes.c_float(scale),
-                                       int(bool(causal)), int(q_offset), int(k_offset), ws.data_ptr(), ws_bytes,
-                                       _stream(q.device))
+                                       int(bool(causal)), int(q_offset), int(k_offset), _stream(q.device))
     check("attn_fwd_block", st)
     return o_part, lse_part
 

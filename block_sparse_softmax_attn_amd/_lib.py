@@ -21,11 +21,10 @@ ATTN_BF16 = 1
 ATTN_FLAG_DIAGONAL = 1
 ATTN_FLAG_PARTIAL = 2
 
-EXPORTED = ("attn_status_string", "attn_fwd_workspace_bytes", "attn_fwd", "attn_blockmask_build",
+EXPORTED = ("attn_status_string", "attn_prepared_v_bytes", "attn_fwd", "attn_blockmask_build",
             "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared",
             "attn_bwd_workspace_bytes", "attn_bwd", "attn_blockmask_transpose", "attn_bwd_blocksparse",
-            "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv", "attn_fwd_block_workspace_bytes",
-            "attn_fwd_block", "attn_merge", "attn_fwd_gqa", "attn_fwd_blocksparse_gqa",
+            "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv", "attn_fwd_block", "attn_merge", "attn_fwd_gqa", "attn_fwd_blocksparse_gqa",
             "attn_bwd_gqa_workspace_bytes", "attn_bwd_gqa", "attn_bwd_blocksparse_gqa",
             "attn_select_meanpool_nnz", "attn_select_meanpool_workspace_bytes", "attn_select_meanpool")
 
@@ -44,10 +43,10 @@ def _load() -> ctypes.CDLL:
     i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i32]
-    lib.attn_fwd_workspace_bytes.restype = i64
-    lib.attn_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+    lib.attn_prepared_v_bytes.restype = i64
+    lib.attn_prepared_v_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.attn_blockmask_build.restype = i32
     lib.attn_blockmask_build.argtypes = [vp, vp, i64, i64, i64, i32, vp, vp, vp, i64, vp, vp, vp]
     lib.attn_fwd_blocksparse.restype = i32
@@ -73,15 +72,12 @@ def _load() -> ctypes.CDLL:
     lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i64]
     lib.attn_fwd_splitkv.restype = i32
     lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, i64, vp, i64, vp]
-    lib.attn_fwd_block_workspace_bytes.restype = i64
-    lib.attn_fwd_block_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_fwd_block.restype = i32
-    lib.attn_fwd_block.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, i64, i64, vp, i64,
-                                   vp]
+    lib.attn_fwd_block.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, i64, i64, vp]
     lib.attn_merge.restype = i32
     lib.attn_merge.argtypes = [vp, vp, i64, i64, i64, i64, i64, vp, vp, i32, vp]
     lib.attn_fwd_gqa.restype = i32
-    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
+    lib.attn_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.attn_fwd_blocksparse_gqa.restype = i32
     lib.attn_fwd_blocksparse_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i32, f32, i32, i64,
                                              vp, vp, vp, i64, i64, vp]

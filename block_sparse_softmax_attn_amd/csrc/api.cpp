@@ -51,60 +51,53 @@ bsattn::FwdArgs make_args(const void* q, const void* k, const void* v, void* o, 
 
 bool valid_groups(int64_t H, int64_t Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
 
-int64_t workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-    if (dtype != ATTN_BF16) return 0;
-    return B * H * d * bsattn::vt_padded_keys(N) * 2;
-}
+// V^T of B*H heads, as attn_prepare_v writes it
+int64_t vt_bytes(int64_t B, int64_t H, int64_t N, int64_t d) { return B * H * d * bsattn::vt_padded_keys(N) * 2; }
 
-int check_workspace(void* ws, int64_t ws_bytes, int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-    const int64_t need = workspace_bytes(B, H, N, d, dtype);
-    if (need == 0) return ATTN_OK;
-    if (ws_bytes < need) return ATTN_ECAPACITY;
-    if (!ws || !aligned16(ws)) return ATTN_EINVAL;
+int check_vt(const void* vt, int64_t given, int64_t B, int64_t H, int64_t N, int64_t d) {
+    if (given < vt_bytes(B, H, N, d)) return ATTN_ECAPACITY;
+    if (!vt || !aligned16(vt)) return ATTN_EINVAL;
     return ATTN_OK;
 }
 
-// bf16 dense/causal: V^T into the workspace (unless the caller prepared it),
-// then the fused kernel, both on `stream`.  bf16 block-sparse: the fused kernel
-// alone, reading V^T from the workspace only when the caller prepared it.
-int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, void* ws, bool prepared, hipStream_t stream) {
+// One launch of the fused kernel on `stream`.  bf16 reads V in place, or V^T
+// when the caller prepared it (vt != nullptr).
+int run(bsattn::FwdArgs& a, int dtype, bsattn::Mode mode, const void* vt, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (dtype == ATTN_BF16) {
-        a.vt = ws;
+        a.vt = const_cast<void*>(vt);   // read only by the forward kernel
         a.npad = static_cast<int>(bsattn::vt_padded_keys(a.N));
-        if (mode == bsattn::Mode::kSparse && !prepared) {
-            a.vt = nullptr;   // the sparse kernel transposes the V tiles it loads itself
-        } else if (!prepared) {
-            bsattn::FwdArgs t = a;
-            t.BH = a.BH / (a.H / a.Hkv);   // V has the key/value heads
-            e = bsattn::launch_v_transpose(t, stream);
-        }
-        if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, mode, stream);
+        e = bsattn::launch_fwd_bf16(a, mode, stream);
     } else {
         e = bsattn::launch_fwd_f32(a, mode, stream);
     }
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
+// v == nullptr: the prepared form, V^T in vt (vt_given bytes)
 int fwd_dense(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H, int64_t Hkv,
-              int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace, int64_t ws_bytes,
-              bool prepared, hipStream_t stream) {
-    int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
+              int64_t N, int64_t d, int dtype, float scale, int causal, const void* vt, int64_t vt_given,
+              hipStream_t stream) {
+    const bool prepared = v == nullptr;
+    int st = check_common(q, k, prepared ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
-    st = check_workspace(workspace, ws_bytes, B, Hkv, N, d, dtype);
-    if (st != ATTN_OK) return st;
+    if (prepared) {
+        st = check_vt(vt, vt_given, B, Hkv, N, d);
+        if (st != ATTN_OK) return st;
+    }
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
     a.Hkv = static_cast<int>(Hkv);
-    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, workspace, prepared, stream);
+    return run(a, dtype, causal ? bsattn::Mode::kCausal : bsattn::Mode::kDense, prepared ? vt : nullptr, stream);
 }
 
 int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
                int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
                const int32_t* row_ptr, const int32_t* col, const uint8_t* flags, int64_t nnz, int64_t meta_heads,
-               void* workspace, int64_t ws_bytes, bool prepared, hipStream_t stream) {
-    // only the prepared form reads a workspace (V^T written by attn_prepare_v)
-    int st = check_common(q, k, prepared && dtype == ATTN_BF16 ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
+               const void* vt, int64_t vt_given, hipStream_t stream) {
+    // v == nullptr: the prepared form, V^T in vt (written by attn_prepare_v)
+    const bool prepared = v == nullptr;
+    int st = check_common(q, k, prepared ? q : v, o, lse, B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
     if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
@@ -112,7 +105,7 @@ int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
     if (!row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags)) return ATTN_EINVAL;
     if (prepared) {
-        st = check_workspace(workspace, ws_bytes, B, Hkv, N, d, dtype);
+        st = check_vt(vt, vt_given, B, Hkv, N, d);
         if (st != ATTN_OK) return st;
     }
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
@@ -123,7 +116,7 @@ int fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
     a.nnz = nnz;
     a.meta_heads = static_cast<int>(meta_heads);
     a.block = static_cast<int>(block);
-    return run(a, dtype, bsattn::Mode::kSparse, workspace, prepared, stream);
+    return run(a, dtype, bsattn::Mode::kSparse, prepared ? vt : nullptr, stream);
 }
 
 }  // namespace
@@ -139,40 +132,39 @@ extern "C" const char* attn_status_string(int status) {
     }
 }
 
-extern "C" int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
-    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128)) return -1;
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return -1;
+extern "C" int64_t attn_prepared_v_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128) || dtype != ATTN_BF16) return -1;
     if (B > (int64_t(1) << 62) / H || B * H > (int64_t(1) << 62) / (2 * d * bsattn::vt_padded_keys(N))) return -1;
-    return workspace_bytes(B, H, N, d, dtype);
+    return vt_bytes(B, H, N, d);
 }
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                        int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
-                        int64_t workspace_bytes_given, hipStream_t stream) {
-    return fwd_dense(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, workspace, workspace_bytes_given, false,
-                     stream);
+                        int64_t N, int64_t d, int dtype, float scale, int causal, hipStream_t stream) {
+    if (!v) return ATTN_EINVAL;
+    return fwd_dense(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, nullptr, 0, stream);
 }
 
 extern "C" int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                     int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
                                     int64_t block, const int32_t* row_ptr, const int32_t* col,
                                     const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
+    if (!v) return ATTN_EINVAL;
     return fwd_sparse(q, k, v, o, lse, B, H, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
-                      meta_heads, nullptr, 0, false, stream);
+                      meta_heads, nullptr, 0, stream);
 }
 
-extern "C" int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* workspace,
-                              int64_t workspace_bytes_given, hipStream_t stream) {
+extern "C" int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype, void* vt,
+                              int64_t vt_bytes_given, hipStream_t stream) {
     if (!v) return ATTN_EINVAL;
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    const int64_t need = attn_fwd_workspace_bytes(B, H, N, d, dtype);
+    const int64_t need = attn_prepared_v_bytes(B, H, N, d, dtype);
     if (need < 0) return (d != 64 && d != 128) ? ATTN_EUNSUPPORTED : ATTN_EINVAL;
     if (!aligned16(v)) return ATTN_EINVAL;
-    const int st = check_workspace(workspace, workspace_bytes_given, B, H, N, d, dtype);
+    const int st = check_vt(vt, vt_bytes_given, B, H, N, d);
     if (st != ATTN_OK) return st;
     bsattn::FwdArgs a{};
     a.v = v;
-    a.vt = workspace;
+    a.vt = vt;
     a.BH = B * H;
     a.N = static_cast<int>(N);
     a.d = static_cast<int>(d);
@@ -181,21 +173,20 @@ extern "C" int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, in
 }
 
 extern "C" int attn_fwd_prepared(const void* q, const void* k, void* o, float* lse, int64_t B, int64_t H, int64_t N,
-                                 int64_t d, int dtype, float scale, int causal, const void* workspace,
-                                 int64_t workspace_bytes_given, hipStream_t stream) {
+                                 int64_t d, int dtype, float scale, int causal, const void* vt,
+                                 int64_t vt_bytes_given, hipStream_t stream) {
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
-    return fwd_dense(q, k, nullptr, o, lse, B, H, H, N, d, dtype, scale, causal, const_cast<void*>(workspace),
-                     workspace_bytes_given, true, stream);
+    return fwd_dense(q, k, nullptr, o, lse, B, H, H, N, d, dtype, scale, causal, vt, vt_bytes_given, stream);
 }
 
 extern "C" int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* lse, int64_t B, int64_t H,
                                              int64_t N, int64_t d, int dtype, float scale, int causal, int64_t block,
                                              const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
-                                             int64_t nnz, int64_t meta_heads, const void* workspace,
-                                             int64_t workspace_bytes_given, hipStream_t stream) {
+                                             int64_t nnz, int64_t meta_heads, const void* vt,
+                                             int64_t vt_bytes_given, hipStream_t stream) {
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
     return fwd_sparse(q, k, nullptr, o, lse, B, H, H, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
-                      meta_heads, const_cast<void*>(workspace), workspace_bytes_given, true, stream);
+                      meta_heads, vt, vt_bytes_given, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -321,18 +312,19 @@ extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v,
 // ---------------------------------------------------------------------------
 
 extern "C" int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                            int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
-                            int64_t workspace_bytes_given, hipStream_t stream) {
-    return fwd_dense(q, k, v, o, lse, B, H, Hkv, N, d, dtype, scale, causal, workspace, workspace_bytes_given, false,
-                     stream);
+                            int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal,
+                            hipStream_t stream) {
+    if (!v) return ATTN_EINVAL;
+    return fwd_dense(q, k, v, o, lse, B, H, Hkv, N, d, dtype, scale, causal, nullptr, 0, stream);
 }
 
 extern "C" int attn_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                                         int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype, float scale,
                                         int causal, int64_t block, const int32_t* row_ptr, const int32_t* col,
                                         const uint8_t* flags, int64_t nnz, int64_t meta_heads, hipStream_t stream) {
+    if (!v) return ATTN_EINVAL;
     return fwd_sparse(q, k, v, o, lse, B, H, Hkv, N, d, dtype, scale, causal, block, row_ptr, col, flags, nnz,
-                      meta_heads, nullptr, 0, false, stream);
+                      meta_heads, nullptr, 0, stream);
 }
 
 extern "C" int64_t attn_bwd_gqa_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
@@ -384,10 +376,10 @@ int64_t partial_bytes(int64_t BH, int64_t N, int64_t d, int64_t splits) {
 extern "C" int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
                                                     int64_t num_splits) {
     if (dtype != ATTN_BF16 || num_splits < 1 || num_splits > kMaxSplits) return -1;
-    const int64_t vt = attn_fwd_workspace_bytes(B, H, N, d, dtype);
-    if (vt < 0 || B * H > (int64_t(1) << 56) / (N * (d + 1) * 4 * num_splits)) return -1;
+    if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128)) return -1;
+    if (B > (int64_t(1) << 40) / H || B * H > (int64_t(1) << 56) / (N * (d + 1) * 4 * num_splits)) return -1;
     const int64_t splits = (N + split_chunk(N, num_splits) - 1) / split_chunk(N, num_splits);
-    return align256(vt) + partial_bytes(B * H, N, d, splits);
+    return partial_bytes(B * H, N, d, splits);
 }
 
 extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -406,30 +398,22 @@ extern "C" int attn_fwd_splitkv(const void* q, const void* k, const void* v, voi
     const int64_t splits = (N + chunk - 1) / chunk;
     bsattn::FwdArgs a = make_args(q, k, v, o, lse, B, H, N, d, scale, causal);
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    a.vt = ws;
-    a.npad = static_cast<int>(bsattn::vt_padded_keys(N));
+    a.vt = nullptr;   // V read in place
     a.Nk = static_cast<int>(N);
     a.kv_chunk = static_cast<int>(chunk);
     a.nsplit = static_cast<int>(splits);
-    a.o_part = reinterpret_cast<float*>(ws + align256(workspace_bytes(B, H, N, d, dtype)));
+    a.o_part = reinterpret_cast<float*>(ws);
     a.lse_part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(a.o_part) + align256(splits * B * H * N * d * 4));
     if ((int64_t)((N + 255) / 256) * B * H * splits > INT32_MAX) return ATTN_EINVAL;
-    hipError_t e = bsattn::launch_v_transpose(a, stream);
-    if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, bsattn::Mode::kRange, stream);
+    hipError_t e = bsattn::launch_fwd_bf16(a, bsattn::Mode::kRange, stream);
     if (e == hipSuccess)
         e = bsattn::launch_merge(a.o_part, a.lse_part, a.nsplit, a.BH, a.N, a.d, o, lse, true, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 
-extern "C" int64_t attn_fwd_block_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, int dtype) {
-    if (dtype != ATTN_BF16) return -1;
-    return attn_fwd_workspace_bytes(B, H, Nk, d, dtype);
-}
-
 extern "C" int attn_fwd_block(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
                               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype, float scale,
-                              int causal, int64_t q_offset, int64_t k_offset, void* workspace,
-                              int64_t workspace_bytes_given, hipStream_t stream) {
+                              int causal, int64_t q_offset, int64_t k_offset, hipStream_t stream) {
     // shapes: Q [B,H,Nq,d]; K, V [B,H,Nk,d]; both sides pass the common checks
     int st = check_common(q, k, v, o_part, lse_part, B, H, Nq, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
@@ -438,13 +422,8 @@ extern "C" int attn_fwd_block(const void* q, const void* k, const void* v, float
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
     if (q_offset < 0 || k_offset < 0 || q_offset > (int64_t(1) << 40) || k_offset > (int64_t(1) << 40))
         return ATTN_EINVAL;
-    const int64_t need = attn_fwd_block_workspace_bytes(B, H, Nk, d, dtype);
-    if (need < 0) return ATTN_EINVAL;
-    if (workspace_bytes_given < need) return ATTN_ECAPACITY;
-    if (!workspace || !aligned16(workspace)) return ATTN_EINVAL;
     bsattn::FwdArgs a = make_args(q, k, v, o_part, lse_part, B, H, Nq, d, scale, causal);
-    a.vt = workspace;
-    a.npad = static_cast<int>(bsattn::vt_padded_keys(Nk));
+    a.vt = nullptr;   // V read in place
     a.Nk = static_cast<int>(Nk);
     a.q_off = q_offset;
     a.k_off = k_offset;
@@ -452,11 +431,7 @@ extern "C" int attn_fwd_block(const void* q, const void* k, const void* v, float
     a.nsplit = 1;
     a.o_part = o_part;
     a.lse_part = lse_part;
-    // the transpose pass reads V with Nk rows
-    bsattn::FwdArgs t = a;
-    t.N = static_cast<int>(Nk);
-    hipError_t e = bsattn::launch_v_transpose(t, stream);
-    if (e == hipSuccess) e = bsattn::launch_fwd_bf16(a, bsattn::Mode::kRange, stream);
+    const hipError_t e = bsattn::launch_fwd_bf16(a, bsattn::Mode::kRange, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
 

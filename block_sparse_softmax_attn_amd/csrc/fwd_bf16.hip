@@ -15,12 +15,16 @@
 //     exchange with lane l^32 (v_permlane32_swap), no LDS reductions.
 //   * The S^T accumulator converts in place to the B operand of O^T += V^T P^T.
 //     The key order inside each 16-key MFMA step is permuted to the keys a lane
-//     already holds; V^T is prepared once per call in that order (a transpose
-//     pass into a workspace), so both K and V^T tiles are plain 16-byte rows.
-//   * K and V^T tiles go from global memory straight into LDS
+//     already holds.  The V^T operand is read from a row-major V tile with the
+//     gfx950 transposing LDS load (ds_read_b64_tr_b16: two per operand, each
+//     giving a lane 4 consecutive keys of its dimension), so V is used in
+//     place and no transpose pass over V is needed.  A caller that reuses V
+//     can also prepare V^T once in the permuted order and have the kernel read
+//     plain 16-byte V^T rows instead.
+//   * K and V tiles go from global memory straight into LDS
 //     (global_load_lds_dwordx4: no VGPR staging, no LDS store instructions),
 //     NSTAGE tiles in flight, 16-byte chunks XOR-swizzled per row so the
-//     fragment reads (one ds_read_b128 per lane) are bank-conflict free.
+//     fragment reads are bank-conflict free.
 //   * Logits are handled in base-2 units (scale * log2 e folded into one FMA
 //     before v_exp_f32).  The running max is only raised when a row's new max
 //     exceeds it by more than 8 (a factor 256): exact, since A and l share the
@@ -42,22 +46,43 @@ constexpr int BN = 64;                 // keys per tile step
 constexpr float kSlack = 8.0f;         // lazy-rescale headroom, base-2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
-template <int D, int NW, int NS, bool VREG>
+// Where the V operand of a tile comes from:
+//   kVsTr: the V tile copied straight into LDS row-major, like K, and read
+//          with the transposing LDS load ds_read_b64_tr_b16 (V in place);
+//   kVsT:  a V^T tile (written beforehand by the transpose pass) copied
+//          straight into LDS and read with plain 16-byte LDS loads.
+enum VSrc : int { kVsTr = 0, kVsT = 1 };
+
+// Row r, logical 16-byte chunk c of a row-major V tile -> physical chunk.  A
+// transposing read of one MFMA operand touches 8 consecutive rows and 4
+// consecutive chunks of each; this XOR spreads them over a 256-byte bank window.
+template <int D>
+__device__ __forceinline__ int vtr_swz(int r, int c) {
+    return D == 128 ? (c ^ (4 * (r & 3))) : (c ^ (4 * ((r >> 1) & 1)));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane L supplies the
+// address of 4 consecutive 16-bit values; lane j receives element j % 4 of the
+// values read by lanes 4e + j / 4, for e = 0..3.  Read with lane L pointing at
+// row e = L / 4, columns 4 (L % 4) .. +3 of a 4 x 16 block, lane j gets column
+// j, rows 0..3.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
+    typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int D, int NW, int NS, int VSRC>
 struct Geo {
     static constexpr int NT = 64 * NW;               // threads per workgroup
     static constexpr int BM = 32 * NW;               // query rows per workgroup
     static constexpr int K_BYTES = BN * D * 2;       // K tile: BN rows of D bf16
-    static constexpr int V_BYTES = D * BN * 2;       // V^T tile: D rows of BN bf16
+    static constexpr int V_BYTES = D * BN * 2;       // V^T tile (D rows of BN) or V tile (BN rows of D)
     static constexpr int K_PER_W = K_BYTES / 1024 / NW;   // 1 KiB direct-to-LDS loads per wave
-    static constexpr int V_PER_W = VREG ? 0 : V_BYTES / 1024 / NW;
+    static constexpr int V_PER_W = V_BYTES / 1024 / NW;
     static constexpr int PER_W = K_PER_W + V_PER_W;
-    // V staged through registers (VREG): each thread moves 4 keys x 8 dims and
-    // writes them transposed into a padded V^T tile.
-    static constexpr int VS = BN + 8;                     // padded V^T row, bf16
-    static constexpr int V_PAIRS = (BN / 4) * (D / 8);
-    static constexpr int V_PER_T = (V_PAIRS + NT - 1) / NT;
     static_assert(K_BYTES % (1024 * NW) == 0 && V_BYTES % (1024 * NW) == 0, "tile must split over waves");
-    static_assert(!VREG || NS == 2, "register-staged V runs two stages");
     static_assert(NS >= 2 && NS <= 4, "2 to 4 stages");
     static_assert((NS - 2) * PER_W < 64, "vmcnt range");
 };
@@ -70,18 +95,16 @@ struct TileDesc {
     int masked;    // any element mask needed (uniform over the workgroup)
 };
 
-template <int D, int NW, int NS, int MODE, bool VREG>
+template <int D, int NW, int NS, int MODE, int VSRC>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
-    using G = Geo<D, NW, NS, VREG>;
+    using G = Geo<D, NW, NS, VSRC>;
+    constexpr bool VTR = VSRC == kVsTr;
     // One array per stage: distinct objects let the compiler see that a tile in
     // flight never aliases the tile being read.
     constexpr int KB2 = NS > 2 ? G::K_BYTES : 16, KB3 = NS > 3 ? G::K_BYTES : 16;
-    constexpr int VB0 = VREG ? 16 : G::V_BYTES;
-    constexpr int VB2 = (NS > 2 && !VREG) ? G::V_BYTES : 16, VB3 = (NS > 3 && !VREG) ? G::V_BYTES : 16;
+    constexpr int VB2 = NS > 2 ? G::V_BYTES : 16, VB3 = NS > 3 ? G::V_BYTES : 16;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[G::K_BYTES], sK1[G::K_BYTES], sK2[KB2], sK3[KB3];
-    __shared__ __attribute__((aligned(1024))) unsigned char sV0[VB0], sV1[VB0], sV2[VB2], sV3[VB3];
-    // register-staged V: two padded V^T tiles
-    __shared__ __attribute__((aligned(16))) __bf16 sVt[VREG ? 2 : 1][VREG ? D * G::VS : 8];
+    __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::V_BYTES], sV1[G::V_BYTES], sV2[VB2], sV3[VB3];
     unsigned char* const kbuf[4] = {sK0, sK1, sK2, sK3};
     unsigned char* const vbuf[4] = {sV0, sV1, sV2, sV3};
 
@@ -115,8 +138,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * D;
     const __bf16* Kh = static_cast<const __bf16*>(a.k) + kvh * (int64_t)NK * D;
-    const __bf16* Vth = static_cast<const __bf16*>(a.vt) + kvh * (int64_t)a.npad * D;
-    const __bf16* Vh = static_cast<const __bf16*>(a.v) + kvh * (int64_t)NK * D;
+    const __bf16* Vth = VTR ? nullptr : static_cast<const __bf16*>(a.vt) + kvh * (int64_t)a.npad * D;
+    const __bf16* Vh = VTR ? static_cast<const __bf16*>(a.v) + kvh * (int64_t)NK * D : nullptr;
 
     // ---- tile schedule ----
     int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0, kv_lo = 0, kv_hi = 0;
@@ -168,6 +191,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // bytes [1024 g + 16 i, +16) of the tile, i.e. row r, physical chunk p,
     // with logical chunk swz(r, p) of that row.
     int k_row[G::K_PER_W], k_col[G::K_PER_W], v_off[G::V_PER_W > 0 ? G::V_PER_W : 1];
+    int v_row[VTR ? G::V_PER_W : 1];
 #pragma unroll
     for (int i = 0; i < G::K_PER_W; ++i) {
         const int byte = (w * G::K_PER_W + i) * 1024 + lane * 16;
@@ -178,8 +202,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < G::V_PER_W; ++i) {
         const int byte = (w * G::V_PER_W + i) * 1024 + lane * 16;
-        const int d = byte / (2 * BN), p = (byte % (2 * BN)) / 16;
-        v_off[i] = d * a.npad + v_swz(d, p) * 8;
+        if constexpr (VTR) {   // row-major V tile: offset of the key row's chunk; the row goes in v_row
+            const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
+            v_row[i] = r;
+            v_off[i] = vtr_swz<D>(r, p) * 8;
+        } else {
+            const int d = byte / (2 * BN), p = (byte % (2 * BN)) / 16;
+            v_off[i] = d * a.npad + v_swz(d, p) * 8;
+        }
     }
     auto issue_tile = [&](int kb0, unsigned char* dK, unsigned char* dV) {
 #pragma unroll
@@ -188,42 +218,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             dma16(Kh + (int64_t)key * D + k_col[i], dK + (w * G::K_PER_W + i) * 1024);
         }
 #pragma unroll
-        for (int i = 0; i < G::V_PER_W; ++i)
-            dma16(Vth + (int64_t)kb0 + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
-    };
-    u32x4 vreg[VREG ? G::V_PER_T : 1][4];
-    auto load_v = [&](int kb0) {   // VREG: 4 keys x 8 dims per thread into registers
-#pragma unroll
-        for (int u2 = 0; u2 < G::V_PER_T; ++u2) {
-            const int pr = min(tid + u2 * G::NT, G::V_PAIRS - 1);
-            const int kq = pr % (BN / 4), dq = pr / (BN / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int key = min(kb0 + 4 * kq + r, NK - 1);
-                vreg[u2][r] = *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + dq * 8);
+        for (int i = 0; i < G::V_PER_W; ++i) {
+            if constexpr (VTR) {
+                const int key = min(kb0 + v_row[i], NK - 1);
+                dma16(Vh + (int64_t)key * D + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
+            } else {
+                dma16(Vth + (int64_t)kb0 + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
             }
         }
     };
-    auto store_v = [&](__bf16* sV) {   // VREG: per dim, the 4 keys as one 8-byte piece of V^T
-#pragma unroll
-        for (int u2 = 0; u2 < G::V_PER_T; ++u2) {
-            const int pr = tid + u2 * G::NT;
-            if (pr < G::V_PAIRS) {
-                const int kq = pr % (BN / 4), dq = pr / (BN / 4);
-                const int pos = vt_pos_of_quad(kq);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int ww = e >> 1;
-                    const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                    u32x2 pk;
-                    pk[0] = __builtin_amdgcn_perm(vreg[u2][1][ww], vreg[u2][0][ww], sel);
-                    pk[1] = __builtin_amdgcn_perm(vreg[u2][3][ww], vreg[u2][2][ww], sel);
-                    *reinterpret_cast<u32x2*>(sV + (dq * 8 + e) * G::VS + pos) = pk;
-                }
-            }
-        }
-    };
-
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
@@ -246,13 +249,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
             if (s < ntiles) issue_tile(describe(s).kb0, kbuf[s], vbuf[s]);
-        if constexpr (VREG) {
-            load_v(describe(0).kb0);
-            store_v(sVt[0]);
-        }
 
         // One tile's math for this wave: scores, masks, online softmax, PV.
-        auto compute = [&](const TileDesc& t, const unsigned char* bK, const unsigned char* bV, const __bf16* bVt) {
+        auto compute = [&](const TileDesc& t, const unsigned char* bK, const unsigned char* bV) {
             // ---- S^T: lane (l32, hi) gets, in s[c][v], the score of query l32
             // and key kb0 + 32c + 8(v>>2) + 4hi + (v&3) ----
             f32x16 s[BN / 32];
@@ -315,10 +314,21 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                 for (int db = 0; db < D / 32; ++db) {
                     const int d = 32 * db + l32;
                     bf16x8 vf;
-                    if constexpr (VREG)
-                        vf = *reinterpret_cast<const bf16x8*>(bVt + d * G::VS + 16 * g + 8 * hi);
-                    else
+                    if constexpr (VTR) {
+                        // operand element i of lane (d, hi) is key 16g + 8(i>>2) + 4hi + (i&3):
+                        // two transposing reads of 4 keys; lane L of a 16-lane group
+                        // points at key row 4hi + L/4 (+8 for the second), dims
+                        // 32db + 16((lane>>4)&1) + 4(L%4) .. +3
+                        const int row = 16 * g + 4 * hi + ((lane >> 2) & 3);
+                        const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+                        const int half = 8 * (lane & 1);
+                        const bf16x4 lo4 = lds_read_tr(bV + row * (2 * D) + vtr_swz<D>(row, ch) * 16 + half);
+                        const bf16x4 hi4 =
+                            lds_read_tr(bV + (row + 8) * (2 * D) + vtr_swz<D>(row + 8, ch) * 16 + half);
+                        vf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                    } else {
                         vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz(d, 2 * g + hi) * 16);
+                    }
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g], oacc[db], 0, 0, 0);
                 }
         };
@@ -331,16 +341,12 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             if (ahead >= 2) wait_vmcnt<2 * G::PER_W>();
             else if (ahead == 1) wait_vmcnt<G::PER_W>();
             else wait_vmcnt<0>();
-            if constexpr (VREG) __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): V^T stores done
             barrier();
             const int un = (u + NS - 1) % NS;
-            const bool vnext = VREG && it + 1 < ntiles;
-            if (vnext) load_v(describe(it + 1).kb0);
             if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, kbuf[un], vbuf[un]);
             const TileDesc t = describe(it);
-            // a wave whose rows all precede the tile skips it (still stages V)
-            if (!(t.causal && t.kb0 > wdiag)) compute(t, kbuf[u], vbuf[u], sVt[VREG ? (it & 1) : 0]);
-            if (vnext) store_v(sVt[(it + 1) & 1]);
+            // a wave whose rows all precede the tile skips its math
+            if (!(t.causal && t.kb0 > wdiag)) compute(t, kbuf[u], vbuf[u]);
         };
 
         for (int base = 0; base < ntiles; base += NS) {
@@ -424,25 +430,28 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const __bf16* __restri
     }
 }
 
-template <int D, int NW, int NS, int MODE, bool VREG = false>
+template <int D, int NW, int NS, int MODE, int VSRC>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    using G = Geo<D, NW, NS, VREG>;
+    using G = Geo<D, NW, NS, VSRC>;
     const int64_t nqt = (a.N + G::BM - 1) / G::BM;
     const int64_t grid = nqt * a.BH * (MODE == (int)Mode::kRange ? a.nsplit : 1);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VREG>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VSRC>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
     return hipGetLastError();
+}
+
+// V^T from the caller's workspace when a.vt is set, else V read in place.
+template <int D, int NW, int NS, int MODE>
+hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
+    if (a.vt != nullptr) return launch<D, NW, NS, MODE, kVsT>(a, stream);
+    return launch<D, NW, NS, MODE, kVsTr>(a, stream);
 }
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     // dense and causal: 8 waves (256 query rows) share each K/V tile, one
-    // workgroup per CU, 3 tiles in flight, V^T from the workspace (4 waves on
-    // small grids, below).  Block-
-    // sparse: the workgroup is one query block, two workgroups per CU, 2 tiles
-    // in flight; each V block is reused by only a few query blocks, so unless
-    // the caller prepared V^T (a.vt set) the kernel transposes V tiles itself
-    // instead of paying a transpose pass over all of V.
-    const bool vreg = a.vt == nullptr;
+    // workgroup per CU, 3 tiles in flight (4 waves and 2 tiles on small grids,
+    // below).  Block-sparse: the workgroup is one query block, two workgroups
+    // per CU, 2 tiles in flight.
     // Fewer than 4 rounds of 256-row workgroups over the 256 CUs: 128-row
     // workgroups (two per CU, 2 tiles in flight) fill the chip better (B=4
     // H=16 N=2048 causal: 343 -> 410 TFLOP/s); larger grids keep 256 rows,
@@ -450,18 +459,15 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     const bool small_grid = (int64_t)((a.N + 255) / 256) * a.BH < 1024;
     switch (mode) {
         case Mode::kDense:
-            if (small_grid) return launch<D, 4, 2, (int)Mode::kDense>(a, stream);
-            return launch<D, 8, 3, (int)Mode::kDense>(a, stream);
+            if (small_grid) return launch_v<D, 4, 2, (int)Mode::kDense>(a, stream);
+            return launch_v<D, 8, 3, (int)Mode::kDense>(a, stream);
         case Mode::kCausal:
-            if (small_grid) return launch<D, 4, 2, (int)Mode::kCausal>(a, stream);
-            return launch<D, 8, 3, (int)Mode::kCausal>(a, stream);
-        case Mode::kRange: return launch<D, 8, 3, (int)Mode::kRange>(a, stream);
+            if (small_grid) return launch_v<D, 4, 2, (int)Mode::kCausal>(a, stream);
+            return launch_v<D, 8, 3, (int)Mode::kCausal>(a, stream);
+        case Mode::kRange: return launch_v<D, 8, 3, (int)Mode::kRange>(a, stream);
         case Mode::kSparse:
-            if (a.block == 128)
-                return vreg ? launch<D, 4, 2, (int)Mode::kSparse, true>(a, stream)
-                            : launch<D, 4, 2, (int)Mode::kSparse>(a, stream);
-            return vreg ? launch<D, 2, 2, (int)Mode::kSparse, true>(a, stream)
-                        : launch<D, 2, 2, (int)Mode::kSparse>(a, stream);
+            if (a.block == 128) return launch_v<D, 4, 2, (int)Mode::kSparse>(a, stream);
+            return launch_v<D, 2, 2, (int)Mode::kSparse>(a, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -24,9 +24,9 @@
  *   - Tensors are dense and contiguous: Q, K, V, O are [B, H, N, d] with row
  *     stride d; LSE is [B, H, N] fp32.  Q, K, V, O have the same dtype.
  *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
- *     aligned to 16 bytes.  The caller owns every buffer, including the
- *     workspace the bf16 path needs (attn_fwd_workspace_bytes); the library
- *     never allocates device memory and keeps no pointer after a call returns.
+ *     aligned to 16 bytes.  The caller owns every buffer, including any
+ *     workspace an entry point takes; the library never allocates device
+ *     memory and keeps no pointer after a call returns.
  *   - Calls are asynchronous on `stream` (0 = the null stream): the inputs
  *     must stay alive and unmodified until the stream has run the work.
  *   - Allowed pairs: causal keeps j <= i.  A query row with no allowed key
@@ -65,15 +65,6 @@ enum {
 const char* attn_status_string(int status);
 
 /*
- * attn_fwd_workspace_bytes - bytes of device workspace that attn_fwd and
- * attn_prepare_v need for these sizes: B*H*d*ceil(N/128)*128*2 for ATTN_BF16
- * (V transposed per head, in the key order the kernel reads), 0 for ATTN_F32.
- * attn_fwd_blocksparse needs none.  Returns -1 for sizes or a dtype the
- * kernels do not accept.
- */
-int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
-
-/*
  * attn_fwd - dense or causal attention forward.
  *   q, k, v : device, [B,H,N,d] of `dtype` (ATTN_BF16 or ATTN_F32), read only.
  *   o       : device, [B,H,N,d] of `dtype`, written (O in the input dtype).
@@ -83,18 +74,15 @@ int64_t attn_fwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int
  *   scale   : finite and > 0 (e.g. 1/sqrt(d)); logits are scale * q.k.
  *   causal  : 0 or 1 (1 keeps j <= i; tiles wholly in the future are skipped,
  *             the diagonal tile gets the triangular element mask).
- *   workspace, workspace_bytes : device scratch of at least
- *             attn_fwd_workspace_bytes(...) bytes (may be NULL when that is 0);
- *             overwritten by the call, must not overlap any tensor argument.
+ * One kernel launch, no workspace: K and V tiles are read in place.
  * Source: "Exact Blocks, Rings, and Sparsity", section 2, forward kernel
  * ("What the forward kernel keeps on chip"): the host wrapper takes q, k, v
  * and a causal flag and returns O and the per-row LSE.
- * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY (workspace too
- * small), ATTN_EHIP.
+ * Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
-             void* workspace, int64_t workspace_bytes, hipStream_t stream);
+             hipStream_t stream);
 
 /*
  * attn_blockmask_build - HOST-side canonicaliser of block-sparse metadata.
@@ -143,9 +131,7 @@ int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* raw_col,
  *                cannot make the kernel read out of bounds.
  *   meta_heads : 1 (one pattern for every (b,h)), H (pattern h for head h) or
  *                B*H (pattern b*H + h, as the device selector writes).
- * No workspace: a key block is visited by only a few query blocks, so the
- * kernel transposes each V tile it loads on chip rather than in a separate
- * pass over all of V.
+ * One kernel launch, no workspace.
  * Source: "Exact Blocks, Rings, and Sparsity", section 5 (the outer loop runs
  * over b in C_a; skipped tiles skip their loads and both products) and
  * section 6 (drop-and-renormalize); "block-sparse attention patterns"
@@ -159,38 +145,45 @@ int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, f
                          int64_t nnz, int64_t meta_heads, hipStream_t stream);
 
 /*
- * Two-step form of the bf16 path, for callers that run several forwards
- * against the same V (or that time the fused kernel on its own):
+ * Two-step form of the bf16 path, for callers that run many forwards against
+ * the same V: V is transposed once, and the fused kernel then reads V^T tiles
+ * with plain 16-byte LDS reads instead of transposing LDS reads (about 1 %
+ * less kernel time at B=1 H=32 N=8192 d=128).
  *
- * attn_prepare_v - write V transposed per head into `workspace` (the layout
- *   the fused kernel reads: [B*H][d][ceil(N/128)*128] bf16, keys permuted
- *   inside each 16-key group, keys >= N zero).
- *   v : device [B,H,N,d] bf16.  workspace : as for attn_fwd.
+ * attn_prepared_v_bytes - bytes of the V^T buffer for these sizes:
+ *   B*H*d*ceil(N/128)*128*2 (ATTN_BF16 only); -1 for sizes or a dtype the
+ *   kernels do not accept.
+ *
+ * attn_prepare_v - write V transposed per head into `vt` (the layout the
+ *   fused kernel reads: [B*H][d][ceil(N/128)*128] bf16, keys permuted inside
+ *   each 16-key group, keys >= N zero).
+ *   v : device [B,H,N,d] bf16.  vt : device, vt_bytes >=
+ *   attn_prepared_v_bytes(...), 16-byte aligned, must not overlap v.
  *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype other than ATTN_BF16, d),
  *   ATTN_ECAPACITY, ATTN_EHIP.
  *
  * attn_fwd_prepared / attn_fwd_blocksparse_prepared - attn_fwd /
- *   attn_fwd_blocksparse without the V argument: V is read from a workspace
- *   that attn_prepare_v filled for the same B, H, N, d (ATTN_BF16 only).
- *   attn_fwd(...) is attn_prepare_v(...) followed by attn_fwd_prepared(...)
- *   on the same stream; attn_fwd_blocksparse_prepared gives results bitwise
- *   equal to attn_fwd_blocksparse (same arithmetic in the same order), and
- *   pays off when several sparse forwards share one V.
+ *   attn_fwd_blocksparse without the V argument: V^T is read from `vt`, which
+ *   attn_prepare_v filled for the same B, H, N, d (ATTN_BF16 only).  Results
+ *   are bitwise equal to attn_fwd / attn_fwd_blocksparse (same arithmetic in
+ *   the same order).
  * Source: as for attn_fwd and attn_fwd_blocksparse.
  */
+int64_t attn_prepared_v_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype);
+
 int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
-                   void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                   void* vt, int64_t vt_bytes, hipStream_t stream);
 
 int attn_fwd_prepared(const void* q, const void* k, void* o, float* lse,
                       int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale, int causal,
-                      const void* workspace, int64_t workspace_bytes, hipStream_t stream);
+                      const void* vt, int64_t vt_bytes, hipStream_t stream);
 
 int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* lse,
                                   int64_t B, int64_t H, int64_t N, int64_t d, int dtype, float scale,
                                   int causal, int64_t block,
                                   const int32_t* row_ptr, const int32_t* col, const uint8_t* flags,
-                                  int64_t nnz, int64_t meta_heads, const void* workspace,
-                                  int64_t workspace_bytes, hipStream_t stream);
+                                  int64_t nnz, int64_t meta_heads, const void* vt,
+                                  int64_t vt_bytes, hipStream_t stream);
 
 /*
  * Backward pass (gradients of the forward above; ATTN_BF16 only).
@@ -281,7 +274,7 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
  *   GPU), then merged: same arguments as attn_fwd plus num_splits in [1, 64]
  *   (key ranges of whole 64-key tiles; fewer ranges when N is small).
  *   workspace : at least attn_fwd_splitkv_workspace_bytes(...) bytes, aligned
- *   to 256 bytes (V^T, then the fp32 partial states).
+ *   to 256 bytes (the fp32 partial states of every range).
  *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype, d), ATTN_ECAPACITY, ATTN_EHIP.
  */
 int64_t attn_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype,
@@ -300,16 +293,12 @@ int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float
  *   lse_part : device [B,H,Nq] fp32, written: LSE_s (-inf for rows that see no key).
  *   causal   : 1 keeps the pairs with k_offset + j <= q_offset + i.
  *   q_offset, k_offset : in [0, 2^40].
- *   workspace : device, attn_fwd_block_workspace_bytes(B, H, Nk, d, dtype)
- *              bytes (V^T of the block), 16-byte aligned.
- *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY, ATTN_EHIP.
+ *   One kernel launch, no workspace.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP.
  */
-int64_t attn_fwd_block_workspace_bytes(int64_t B, int64_t H, int64_t Nk, int64_t d, int dtype);
-
 int attn_fwd_block(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int64_t B,
                    int64_t H, int64_t Nq, int64_t Nk, int64_t d, int dtype, float scale, int causal,
-                   int64_t q_offset, int64_t k_offset, void* workspace, int64_t workspace_bytes,
-                   hipStream_t stream);
+                   int64_t q_offset, int64_t k_offset, hipStream_t stream);
 
 /*
  * attn_merge - merge num_parts partial states over disjoint key sets.
@@ -338,15 +327,13 @@ int attn_merge(const float* o_parts, const float* lse_parts, int64_t num_parts, 
  *   may also be Hkv.  Each dK, dV head is the sum of the contributions of its
  *   group's query heads (one workgroup per key/value head sums them in a fixed
  *   order: deterministic).
- *   Workspaces: attn_fwd_gqa needs attn_fwd_workspace_bytes(B, Hkv, N, d, dtype)
- *   (V^T of the key/value heads); attn_fwd_blocksparse_gqa needs none; the
- *   backward needs attn_bwd_gqa_workspace_bytes(B, H, Hkv, N, d, dtype).
+ *   Workspaces: the forwards need none; the backward needs
+ *   attn_bwd_gqa_workspace_bytes(B, H, Hkv, N, d, dtype).
  *   Errors: as for the non-grouped entry points; ATTN_EINVAL also when Hkv < 1,
  *   Hkv > H or H % Hkv != 0.
  */
 int attn_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
-                 int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, void* workspace,
-                 int64_t workspace_bytes, hipStream_t stream);
+                 int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal, hipStream_t stream);
 
 int attn_fwd_blocksparse_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                              int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype, float scale, int causal,

@@ -55,16 +55,15 @@ FAKE = 1 << 20   # 16-aligned, never dereferenced: every call below fails valida
     (dict(causal=2), -1),
     (dict(q=FAKE + 2), -1),
     (dict(N=1 << 31), -1),
-    (dict(ws_bytes=100), -3), (dict(ws=0), -1), (dict(ws=FAKE + 8), -1),
+    (dict(v=0), -1), (dict(v=FAKE + 8), -1),
 ])
 def test_attn_fwd_rejects_bad_arguments(m, args, expect):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
-    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, dtype=1, scale=0.125, causal=0,
-             ws=FAKE, ws_bytes=1 << 20)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=16, d=64, dtype=1, scale=0.125, causal=0)
     a.update(args)
-    st = lib.attn_fwd(a["q"] or None, a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
-                      a["dtype"], ctypes.c_float(a["scale"]), a["causal"], a["ws"] or None, a["ws_bytes"], None)
+    st = lib.attn_fwd(a["q"] or None, a["k"], a["v"] or None, a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["dtype"], ctypes.c_float(a["scale"]), a["causal"], None)
     assert st == expect
 
 
@@ -88,14 +87,14 @@ def test_prepared_entry_points_reject_bad_arguments(m):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
     f = ctypes.c_float(0.125)
-    # prepare: fp32 has no V^T workspace, null v, bad d, small or misaligned workspace
+    # prepare: fp32 has no V^T form, null v, bad d, small or misaligned V^T buffer
     assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 0, FAKE, 1 << 20, None) == -2
     assert lib.attn_prepare_v(None, 1, 2, 100, 64, 1, FAKE, 1 << 20, None) == -1
     assert lib.attn_prepare_v(FAKE, 1, 2, 100, 96, 1, FAKE, 1 << 20, None) == -2
     assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 1, FAKE, 100, None) == -3
     assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 1, FAKE + 4, 1 << 20, None) == -1
     assert lib.attn_prepare_v(FAKE, 0, 2, 100, 64, 1, FAKE, 1 << 20, None) == -1
-    # prepared forwards: bf16 only, workspace required
+    # prepared forwards: bf16 only, V^T buffer required
     assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0, f, 0, FAKE, 1 << 20, None) == -2
     assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 0, None, 1 << 20, None) == -1
     assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 0, FAKE, 64, None) == -3
@@ -106,16 +105,16 @@ def test_prepared_entry_points_reject_bad_arguments(m):
                                              4, 1, FAKE, 1 << 20, None) == -1
 
 
-def test_workspace_bytes(m):
+def test_prepared_v_bytes(m):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
-    assert lib.attn_fwd_workspace_bytes(1, 32, 8192, 128, 1) == 32 * 128 * 8192 * 2
-    assert lib.attn_fwd_workspace_bytes(1, 16, 16300, 128, 1) == 16 * 128 * 16384 * 2
-    assert lib.attn_fwd_workspace_bytes(2, 3, 1, 64, 1) == 6 * 64 * 128 * 2
-    assert lib.attn_fwd_workspace_bytes(1, 1, 256, 64, 0) == 0
-    assert lib.attn_fwd_workspace_bytes(1, 1, 256, 96, 1) == -1
-    assert lib.attn_fwd_workspace_bytes(0, 1, 256, 64, 1) == -1
-    assert m.workspace_bytes(1, 2, 300, 128, 1) == 2 * 128 * 384 * 2
+    assert lib.attn_prepared_v_bytes(1, 32, 8192, 128, 1) == 32 * 128 * 8192 * 2
+    assert lib.attn_prepared_v_bytes(1, 16, 16300, 128, 1) == 16 * 128 * 16384 * 2
+    assert lib.attn_prepared_v_bytes(2, 3, 1, 64, 1) == 6 * 64 * 128 * 2
+    assert lib.attn_prepared_v_bytes(1, 1, 256, 64, 0) == -1     # bf16 only
+    assert lib.attn_prepared_v_bytes(1, 1, 256, 96, 1) == -1
+    assert lib.attn_prepared_v_bytes(0, 1, 256, 64, 1) == -1
+    assert m.prepared_v_bytes(1, 2, 300, 128) == 2 * 128 * 384 * 2
 
 
 def _check_builder(m, rows, meta_heads, N, block, causal):
@@ -287,16 +286,14 @@ def test_splitkv_workspace_bytes(m):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
     a256 = lambda x: (x + 255) // 256 * 256
-    # B1 H4 N8192 d128, 4 splits of 2048 keys: V^T + fp32 partials
-    vt = 4 * 128 * 8192 * 2
-    assert lib.attn_fwd_splitkv_workspace_bytes(1, 4, 8192, 128, 1, 4) == a256(vt) + a256(4 * 4 * 8192 * 128 * 4) + a256(4 * 4 * 8192 * 4)
+    # B1 H4 N8192 d128, 4 splits of 2048 keys: the fp32 partial states
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 4, 8192, 128, 1, 4) == a256(4 * 4 * 8192 * 128 * 4) + a256(4 * 4 * 8192 * 4)
     # N = 100 holds two 64-key tiles: at most two ranges
-    vt = 128 * 64 * 2
-    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 8) == a256(vt) + a256(2 * 100 * 64 * 4) + a256(2 * 100 * 4)
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 8) == a256(2 * 100 * 64 * 4) + a256(2 * 100 * 4)
     assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 0, 2) == -1     # bf16 only
     assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 0) == -1
     assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 64, 1, 65) == -1
-    assert lib.attn_fwd_block_workspace_bytes(2, 3, 300, 128, 1) == 6 * 128 * 384 * 2
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 1, 100, 96, 1, 2) == -1
 
 
 def test_split_and_ring_entry_points_reject_bad_arguments(m):
@@ -309,12 +306,12 @@ def test_split_and_ring_entry_points_reject_bad_arguments(m):
     assert lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 2, FAKE, 100, None) == -3
     assert lib.attn_fwd_splitkv(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 2, FAKE + 16, 1 << 24, None) == -1
     assert lib.attn_fwd_splitkv(None, FAKE, FAKE, FAKE, FAKE, 1, 2, 256, 64, 1, f, 0, 2, FAKE, 1 << 24, None) == -1
-    # ring step: negative offsets, zero keys, fp32, small workspace
-    blk = lambda **kw: lib.attn_fwd_block(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, kw.get("nq", 64), kw.get("nk", 128), 64,
-                                          kw.get("dt", 1), f, 1, kw.get("qo", 0), kw.get("ko", 0), FAKE,
-                                          kw.get("ws", 1 << 24), None)
+    # ring step: negative offsets, zero keys, fp32, null or misaligned V
+    blk = lambda **kw: lib.attn_fwd_block(FAKE, FAKE, kw.get("v", FAKE), FAKE, FAKE, 1, 2, kw.get("nq", 64),
+                                          kw.get("nk", 128), 64, kw.get("dt", 1), f, 1, kw.get("qo", 0),
+                                          kw.get("ko", 0), None)
     assert blk(qo=-1) == -1 and blk(ko=-5) == -1 and blk(nk=0) == -1 and blk(nq=0) == -1
-    assert blk(dt=0) == -2 and blk(ws=10) == -3
+    assert blk(dt=0) == -2 and blk(v=None) == -1 and blk(v=FAKE + 4) == -1
     # merge: parts, d, dtype, alignment
     mg = lambda **kw: lib.attn_merge(kw.get("op", FAKE), FAKE, kw.get("s", 2), 1, 2, 64, kw.get("d", 64), FAKE, FAKE,
                                      kw.get("dt", 0), None)
@@ -337,7 +334,7 @@ def test_gqa_workspace_and_bad_groups(m):
     assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 16, 1024, 128, 1) == -1
     f = ctypes.c_float(0.1)
     for hkv in (0, 3, 16):
-        assert lib.attn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0, FAKE, 1 << 24, None) == -1
+        assert lib.attn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0, None) == -1
         assert lib.attn_fwd_blocksparse_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0, 128, FAKE,
                                             FAKE, FAKE, 4, 1, None) == -1
         assert lib.attn_bwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, hkv, 256, 64, 1, f, 0,
@@ -345,9 +342,8 @@ def test_gqa_workspace_and_bad_groups(m):
     # meta_heads must be 1, Hkv or H
     assert lib.attn_fwd_blocksparse_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 1, f, 0, 128, FAKE, FAKE,
                                         FAKE, 4, 4, None) == -1
-    # forward workspace is V^T of the key/value heads
-    assert lib.attn_fwd_gqa(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 256, 64, 1, f, 0, FAKE, 2 * 64 * 256 * 2 - 16,
-                            None) == -3
+    # null V
+    assert lib.attn_fwd_gqa(FAKE, FAKE, None, FAKE, FAKE, 1, 8, 2, 256, 64, 1, f, 0, None) == -1
 
 
 # ---------------------------------------------------------------------------

@@ -241,8 +241,10 @@ def test_prepared_v_path_is_bitwise_equal(lib):
     assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
 
 
-def test_workspace_too_small_is_rejected(lib):
+def test_prepared_v_buffer_too_small_is_rejected(lib):
     q, k, v = (t.cuda() for t in inputs(1, 1, 64, 64, "bf16", 86))
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(ValueError):
-        lib.attn_fwd(q, k, v, workspace=small)
+        lib.attn_fwd_prepared(q, k, small)
+    with pytest.raises(ValueError):
+        lib.prepare_v(v, small)
