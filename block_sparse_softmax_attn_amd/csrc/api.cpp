@@ -204,7 +204,7 @@ int check_bwd(const void* q, const void* k, const void* v, const void* o, const 
     if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
     if (!dout || !dq || !dk || !dv) return ATTN_EINVAL;
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_EINVAL;
-    if (ws_bytes < bsattn::bwd_workspace_bytes(B * H, B * Hkv, N, d)) return ATTN_ECAPACITY;
+    if (ws_bytes < bsattn::bwd_workspace_bytes(B * H, N)) return ATTN_ECAPACITY;
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ATTN_EINVAL;
     return ATTN_OK;
 }
@@ -242,7 +242,7 @@ int64_t bwd_ws(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtyp
     if (B < 1 || H < 1 || N < 1 || N > kMaxN || (d != 64 && d != 128) || dtype != ATTN_BF16) return -1;
     if (!valid_groups(H, Hkv)) return -1;
     if (B > (int64_t(1) << 62) / H || B * H > (int64_t(1) << 58) / (8 * d * bsattn::vt_padded_keys(N))) return -1;
-    return bsattn::bwd_workspace_bytes(B * H, B * Hkv, N, d);
+    return bsattn::bwd_workspace_bytes(B * H, N);
 }
 
 int bwd_dense(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -9,27 +9,27 @@
 // keys) are split over two kernels, without atomics, the two-traversal choice
 // that section describes:
 //   * dK/dV: a workgroup owns a block of keys (32 per wave, kept in registers
-//     together with their V rows) and streams 64-query tiles of Q, dO, Q^T,
-//     dO^T and the row statistics through LDS;
+//     together with their V rows) and streams 64-query tiles of Q, dO and the
+//     row statistics through LDS;
 //   * dQ: a workgroup owns a block of queries (as in the forward) and streams
-//     64-key tiles of K, V and K^T.
+//     64-key tiles of K and V.
 // Both recompute S and dP for their tiles.
 //
 // gfx950 mapping (ours, not the pages'):
 //   * dK/dV computes S = Q K^T and dP = dO V^T with the keys as the MFMA
 //     columns: a lane holds 16 queries of ONE key, and those registers (P and
 //     dS rounded to bf16) are directly the B operand of dV^T += dO^T P and
-//     dK^T += Q^T dS.  The query order inside each 16-query MFMA step is the
-//     order the transposed tiles are stored in, so every A operand is one
-//     16-byte LDS read.
+//     dK^T += Q^T dS.  The A operands dO^T and Q^T come from the same
+//     row-major dO and Q tiles through the transposing LDS load
+//     (ds_read_b64_tr_b16), in the query order the P and dS registers hold.
 //   * dQ computes S^T = K Q^T and dP^T = V dO^T (a lane holds keys of ONE query,
 //     the forward's layout): LSE_i and D_i are lane scalars, and dS^T is the B
-//     operand of dQ^T += K^T dS^T.
-//   * Q^T, K^T and dO^T are written once per call by the forward's V^T
-//     transpose pass (same 16-token permutation).
+//     operand of dQ^T += K^T dS^T, whose A operand K^T is read transposed from
+//     the K tile.
 //   * Every tile goes from global memory straight into LDS
-//     (global_load_lds_dwordx4) with the forward's XOR swizzles; two tiles in
-//     flight for dK/dV, up to three for dQ.
+//     (global_load_lds_dwordx4), XOR-swizzled so that both the plain and the
+//     transposing reads spread over the banks; two tiles in flight for dK/dV,
+//     up to three for dQ.  No transposed copy of any input is made.
 //   * Rows without allowed keys, and rows past N, get LSE = +inf in the row
 //     statistics, so exp2(s - lse) = 0 and they contribute nothing.
 #include <hip/hip_runtime.h>
@@ -93,10 +93,10 @@ struct DkdvGeo {
     static constexpr int NT = 64 * NW;
     static constexpr int PAIRS = PAIRED ? NW / 2 : NW;   // 32-key slices per workgroup
     static constexpr int BKV = 32 * PAIRS;               // keys per workgroup
-    static constexpr int TB = BT * D * 2;            // bytes of a Q, dO, Q^T or dO^T tile
+    static constexpr int TB = BT * D * 2;            // bytes of a Q or dO tile
     static constexpr int PER_T = TB / 1024 / NW;     // 1 KiB direct-to-LDS loads per wave per tile
     static_assert((!PAIRED || NW % 2 == 0) && TB % (1024 * NW) == 0, "tile must split over waves");
-    static_assert(4 * PER_T + 1 < 64, "vmcnt range");
+    static_assert(2 * PER_T + 1 < 64, "vmcnt range");
 };
 
 // PAIRED (d = 128): two waves share each 32-key slice: the P wave (role 0)
@@ -111,7 +111,6 @@ template <int D, int NW, int MODE, bool PAIRED>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     using G = DkdvGeo<D, NW, PAIRED>;
     __shared__ __attribute__((aligned(1024))) unsigned char sQ0[G::TB], sQ1[G::TB], sO0[G::TB], sO1[G::TB];
-    __shared__ __attribute__((aligned(1024))) unsigned char sQT0[G::TB], sQT1[G::TB], sOT0[G::TB], sOT1[G::TB];
     __shared__ __attribute__((aligned(1024))) float sS0[256], sS1[256];
     __shared__ __attribute__((aligned(16))) bf16x8 sP[PAIRED ? G::PAIRS : 1][2][2][64];   // [pair][block][step][lane]
 
@@ -119,6 +118,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
     const int role = PAIRED ? w / G::PAIRS : 0, pw = PAIRED ? w % G::PAIRS : w;
+    const TrLane<D> trl = tr_lane<D>(lane);   // transposing-read offsets of dO^T / Q^T
     const int N = a.N;
     const int nkt = (N + G::BKV - 1) / G::BKV;
     // one workgroup per (key/value head, key tile); it sums the contributions
@@ -207,29 +207,22 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     };
 
     // Direct-to-LDS sources: load i of this wave fills bytes [1024 (w PER_T + i)
-    // + 16 lane, +16) of a tile.  Row-major tiles: row r, physical chunk p
-    // holds logical chunk k_swz(r, p); transposed tiles: row d (128 bytes),
-    // physical chunk p holds logical chunk v_swz(d, p).
-    int rm_row[G::PER_T], rm_col[G::PER_T], tr_off[G::PER_T];
+    // + 16 lane, +16) of a tile: row r, physical chunk p, holding logical chunk
+    // rt_swz(r, p) of that row.
+    int rm_row[G::PER_T], rm_col[G::PER_T];
 #pragma unroll
     for (int i = 0; i < G::PER_T; ++i) {
         const int byte = (w * G::PER_T + i) * 1024 + lane * 16;
         const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
         rm_row[i] = r;
-        rm_col[i] = k_swz<D>(r, p) * 8;
-        const int d = byte / (2 * BT), p2 = (byte % (2 * BT)) / 16;
-        tr_off[i] = d * a.npad + v_swz(d, p2) * 8;
+        rm_col[i] = rt_swz<D>(r, p) * 8;
     }
     auto issue = [&](const QTile& t, int u) {
         unsigned char* dQ = u ? sQ1 : sQ0;
         unsigned char* dO = u ? sO1 : sO0;
-        unsigned char* dQT = u ? sQT1 : sQT0;
-        unsigned char* dOT = u ? sOT1 : sOT0;
         const int q0 = max(t.q0, 0);
         const __bf16* Qh = static_cast<const __bf16*>(a.q) + t.bhq * (int64_t)N * D;
         const __bf16* dOh = static_cast<const __bf16*>(a.dout) + t.bhq * (int64_t)N * D;
-        const __bf16* QTh = static_cast<const __bf16*>(a.qt) + t.bhq * (int64_t)a.npad * D;
-        const __bf16* dOTh = static_cast<const __bf16*>(a.dot) + t.bhq * (int64_t)a.npad * D;
         const float* Sh = a.stats + t.bhq * (int64_t)(nblk + 1) * 128;
 #pragma unroll
         for (int i = 0; i < G::PER_T; ++i) {
@@ -237,8 +230,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             const int off = (w * G::PER_T + i) * 1024;
             dma16(Qh + (int64_t)row * D + rm_col[i], dQ + off);
             dma16(dOh + (int64_t)row * D + rm_col[i], dO + off);
-            dma16(QTh + q0 + tr_off[i], dQT + off);
-            dma16(dOTh + q0 + tr_off[i], dOT + off);
         }
         // row statistics of this block (lanes 0-31) and of the next (32-63)
         if (w == 0) dma16(Sh + (q0 / BT) * 128 + lane * 4, u ? sS1 : sS0);
@@ -283,8 +274,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     auto compute_paired = [&](int q0, int u) {
         const unsigned char* bQ = u ? sQ1 : sQ0;
         const unsigned char* bO = u ? sO1 : sO0;
-        const unsigned char* bQT = u ? sQT1 : sQT0;
-        const unsigned char* bOT = u ? sOT1 : sOT0;
         const float* st = u ? sS1 : sS0;
         bool live[2];
 #pragma unroll
@@ -302,7 +291,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             bf16x8 fa[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k)
-                fa[k] = *reinterpret_cast<const bf16x8*>(bA + r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16);
+                fa[k] = *reinterpret_cast<const bf16x8*>(bA + r * (2 * D) + rt_swz<D>(r, 2 * k + hi) * 16);
             __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) pr[qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], kvf[k], pr[qc], 0, 0, 0);
@@ -354,15 +343,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
                 }
             }
             // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave) over two 16-query steps
-            const unsigned char* bT = role == 0 ? bOT : bQT;
+            const unsigned char* bT = role == 0 ? bO : bQ;
             bf16x8 ta[2][D / 32];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const int d = 32 * db + l32;
-                    ta[t][db] = *reinterpret_cast<const bf16x8*>(bT + d * (2 * BT) + v_swz(d, 2 * (2 * qc + t) + hi) * 16);
-                }
+                for (int db = 0; db < D / 32; ++db) ta[t][db] = tr_operand<D>(bT, trl, 2 * qc + t, db);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -379,8 +365,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     auto compute_single = [&](int q0, int u) {
         const unsigned char* bQ = u ? sQ1 : sQ0;
         const unsigned char* bO = u ? sO1 : sO0;
-        const unsigned char* bQT = u ? sQT1 : sQT0;
-        const unsigned char* bOT = u ? sOT1 : sOT0;
         const float* st = u ? sS1 : sS0;
 #pragma unroll
         for (int qc = 0; qc < BT / 32; ++qc) {
@@ -393,7 +377,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             bf16x8 fa[D / 16], fb[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) {
-                const int off = r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16;
+                const int off = r * (2 * D) + rt_swz<D>(r, 2 * k + hi) * 16;
                 fa[k] = *reinterpret_cast<const bf16x8*>(bQ + off);
                 fb[k] = *reinterpret_cast<const bf16x8*>(bO + off);
             }
@@ -410,10 +394,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int d = 32 * db + l32;
-                    const int off = d * (2 * BT) + v_swz(d, 2 * (2 * qc + t) + hi) * 16;
-                    ta[t][db] = *reinterpret_cast<const bf16x8*>(bOT + off);
-                    tb[t][db] = *reinterpret_cast<const bf16x8*>(bQT + off);
+                    ta[t][db] = tr_operand<D>(bO, trl, 2 * qc + t, db);
+                    tb[t][db] = tr_operand<D>(bQ, trl, 2 * qc + t, db);
                 }
             // ---- P = exp2(s * scale log2 e - lse2) and dS = P (dP - D), bf16 ----
             bf16x8 pb[2], dsb[2];
@@ -507,9 +489,9 @@ template <int D, int NW, int NS>
 struct DqGeo {
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;               // queries per workgroup
-    static constexpr int TB = BT * D * 2;            // bytes of a K, V or K^T tile
+    static constexpr int TB = BT * D * 2;            // bytes of a K or V tile
     static constexpr int PER_T = TB / 1024 / NW;
-    static constexpr int PER_W = 3 * PER_T;
+    static constexpr int PER_W = 2 * PER_T;
     static_assert(TB % (1024 * NW) == 0, "tile must split over waves");
     static_assert(NS == 2 || NS == 3, "2 or 3 stages");
     static_assert((NS - 2) * PER_W < 64, "vmcnt range");
@@ -528,14 +510,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     constexpr int T2 = NS > 2 ? G::TB : 16;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[G::TB], sK1[G::TB], sK2[T2];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::TB], sV1[G::TB], sV2[T2];
-    __shared__ __attribute__((aligned(1024))) unsigned char sKT0[G::TB], sKT1[G::TB], sKT2[T2];
     unsigned char* const kbuf[3] = {sK0, sK1, sK2};
     unsigned char* const vbuf[3] = {sV0, sV1, sV2};
-    unsigned char* const tbuf[3] = {sKT0, sKT1, sKT2};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
+    const TrLane<D> trl = tr_lane<D>(lane);   // transposing-read offsets of K^T
     const int N = a.N;
     const int nqt = (N + G::BM - 1) / G::BM;
     const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nqt * a.BH);
@@ -552,7 +533,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
     const __bf16* Kh = static_cast<const __bf16*>(a.k) + kvh * (int64_t)N * D;
     const __bf16* Vh = static_cast<const __bf16*>(a.v) + kvh * (int64_t)N * D;
-    const __bf16* KTh = static_cast<const __bf16*>(a.kt) + kvh * (int64_t)a.npad * D;
     const float* Sh = a.stats + bh * (int64_t)(nblk + 1) * 128;
 
     // ---- schedule of 64-key tiles (the forward's) ----
@@ -589,15 +569,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
         return t;
     };
 
-    int k_row[G::PER_T], k_col[G::PER_T], t_off[G::PER_T];
+    int k_row[G::PER_T], k_col[G::PER_T];
 #pragma unroll
     for (int i = 0; i < G::PER_T; ++i) {
         const int byte = (w * G::PER_T + i) * 1024 + lane * 16;
         const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
         k_row[i] = r;
-        k_col[i] = k_swz<D>(r, p) * 8;
-        const int d = byte / (2 * BT), p2 = (byte % (2 * BT)) / 16;
-        t_off[i] = d * a.npad + v_swz(d, p2) * 8;
+        k_col[i] = rt_swz<D>(r, p) * 8;
     }
     auto issue = [&](int kb0, int u) {
 #pragma unroll
@@ -606,7 +584,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
             const int off = (w * G::PER_T + i) * 1024;
             dma16(Kh + (int64_t)key * D + k_col[i], kbuf[u] + off);
             dma16(Vh + (int64_t)key * D + k_col[i], vbuf[u] + off);
-            dma16(KTh + kb0 + t_off[i], tbuf[u] + off);
         }
     };
 
@@ -639,7 +616,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
         auto compute = [&](const KeyTile& t, int u) {
             const unsigned char* bK = kbuf[u];
             const unsigned char* bV = vbuf[u];
-            const unsigned char* bT = tbuf[u];
 #pragma unroll
             for (int c = 0; c < BT / 32; ++c) {
                 // ---- S^T and dP^T: lane (l32, hi) gets key
@@ -648,7 +624,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
                 const int r = 32 * c + l32;
 #pragma unroll
                 for (int k = 0; k < D / 16; ++k) {
-                    const int off = r * (2 * D) + k_swz<D>(r, 2 * k + hi) * 16;
+                    const int off = r * (2 * D) + rt_swz<D>(r, 2 * k + hi) * 16;
                     const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(bK + off);
                     const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(bV + off);
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[k], s, 0, 0, 0);
@@ -670,9 +646,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
                     const int g = 2 * c + tt;
 #pragma unroll
                     for (int db = 0; db < D / 32; ++db) {
-                        const int d = 32 * db + l32;
-                        const bf16x8 ka =
-                            *reinterpret_cast<const bf16x8*>(bT + d * (2 * BT) + v_swz(d, 2 * g + hi) * 16);
+                        const bf16x8 ka = tr_operand<D>(bK, trl, g, db);   // K^T, keys in dsb's order
                         dqacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, dsb[tt], dqacc[db], 0, 0, 0);
                     }
                 }
@@ -763,42 +737,17 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
 
 }  // namespace
 
-int64_t bwd_workspace_bytes(int64_t BH, int64_t BHkv, int64_t N, int64_t d) {
+int64_t bwd_workspace_bytes(int64_t BH, int64_t N) {
     const int64_t npad = vt_padded_keys(N);
-    const int64_t tr = BH * d * npad * 2;                    // Q^T or dO^T
-    const int64_t trk = BHkv * d * npad * 2;                 // K^T
-    const int64_t st = BH * (npad / BT + 1) * 128 * 4;       // row statistics
-    return 2 * tr + trk + st;
+    return BH * (npad / BT + 1) * 128 * 4;   // row statistics
 }
 
 void bwd_workspace_carve(BwdArgs& a, void* ws) {
-    const int64_t npad = vt_padded_keys(a.N);
-    const int64_t tr = a.BH * a.d * npad * 2;
-    const int64_t trk = a.BH / (a.H / a.Hkv) * a.d * npad * 2;
-    unsigned char* p = static_cast<unsigned char*>(ws);
-    a.npad = (int)npad;
-    a.qt = p;
-    a.dot = p + tr;
-    a.kt = p + 2 * tr;
-    a.stats = reinterpret_cast<float*>(p + 2 * tr + trk);
+    a.npad = (int)vt_padded_keys(a.N);
+    a.stats = static_cast<float*>(ws);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream) {
-    // Q^T, K^T, dO^T through the forward's transpose pass
-    FwdArgs t{};
-    t.BH = a.BH;
-    t.N = a.N;
-    t.d = a.d;
-    t.npad = a.npad;
-    const void* src[3] = {a.q, a.k, a.dout};
-    void* dst[3] = {a.qt, a.kt, a.dot};
-    for (int i = 0; i < 3; ++i) {
-        t.v = src[i];
-        t.vt = dst[i];
-        t.BH = i == 1 ? a.BH / (a.H / a.Hkv) : a.BH;   // K has the key/value heads
-        const hipError_t e = launch_v_transpose(t, stream);
-        if (e != hipSuccess) return e;
-    }
     if (a.d == 64) return launch_d<64>(a, mode, stream);
     return launch_d<128>(a, mode, stream);
 }

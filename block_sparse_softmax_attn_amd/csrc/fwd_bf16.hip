@@ -53,26 +53,6 @@ constexpr float kLn2 = 0.69314718055994530942f;
 //          straight into LDS and read with plain 16-byte LDS loads.
 enum VSrc : int { kVsTr = 0, kVsT = 1 };
 
-// Row r, logical 16-byte chunk c of a row-major V tile -> physical chunk.  A
-// transposing read of one MFMA operand touches 8 consecutive rows and 4
-// consecutive chunks of each; this XOR spreads them over a 256-byte bank window.
-template <int D>
-__device__ __forceinline__ int vtr_swz(int r, int c) {
-    return D == 128 ? (c ^ (4 * (r & 3))) : (c ^ (4 * ((r >> 1) & 1)));
-}
-
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane L supplies the
-// address of 4 consecutive 16-bit values; lane j receives element j % 4 of the
-// values read by lanes 4e + j / 4, for e = 0..3.  Read with lane L pointing at
-// row e = L / 4, columns 4 (L % 4) .. +3 of a 4 x 16 block, lane j gets column
-// j, rows 0..3.
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
-    typedef __attribute__((address_space(3))) v4s_t lds_v4s;
-    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
 template <int D, int NW, int NS, int VSRC>
 struct Geo {
     static constexpr int NT = 64 * NW;               // threads per workgroup
@@ -111,6 +91,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
+    const TrLane<D> trl = tr_lane<D>(lane);   // transposing-read offsets of the V^T operand
     constexpr bool RANGE = MODE == (int)Mode::kRange;
     const int N = a.N;                   // query rows
     const int NK = RANGE ? a.Nk : N;     // keys
@@ -205,7 +186,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         if constexpr (VTR) {   // row-major V tile: offset of the key row's chunk; the row goes in v_row
             const int r = byte / (2 * D), p = (byte % (2 * D)) / 16;
             v_row[i] = r;
-            v_off[i] = vtr_swz<D>(r, p) * 8;
+            v_off[i] = rt_swz<D>(r, p) * 8;
         } else {
             const int d = byte / (2 * BN), p = (byte % (2 * BN)) / 16;
             v_off[i] = d * a.npad + v_swz(d, p) * 8;
@@ -315,17 +296,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                     const int d = 32 * db + l32;
                     bf16x8 vf;
                     if constexpr (VTR) {
-                        // operand element i of lane (d, hi) is key 16g + 8(i>>2) + 4hi + (i&3):
-                        // two transposing reads of 4 keys; lane L of a 16-lane group
-                        // points at key row 4hi + L/4 (+8 for the second), dims
-                        // 32db + 16((lane>>4)&1) + 4(L%4) .. +3
-                        const int row = 16 * g + 4 * hi + ((lane >> 2) & 3);
-                        const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
-                        const int half = 8 * (lane & 1);
-                        const bf16x4 lo4 = lds_read_tr(bV + row * (2 * D) + vtr_swz<D>(row, ch) * 16 + half);
-                        const bf16x4 hi4 =
-                            lds_read_tr(bV + (row + 8) * (2 * D) + vtr_swz<D>(row + 8, ch) * 16 + half);
-                        vf = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+                        vf = tr_operand<D>(bV, trl, g, db);   // keys in the order pf[g] holds them
                     } else {
                         vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz(d, 2 * g + hi) * 16);
                     }

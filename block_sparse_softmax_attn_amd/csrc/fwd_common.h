@@ -107,22 +107,17 @@ struct BwdArgs {
     int64_t t_nnz;
     int meta_heads;
     int block;
-    // workspace: Q^T, dO^T ([BH][d][npad] bf16, the transposed-tile key
-    // order), K^T ([B*Hkv][d][npad]) and per-row statistics ([BH][npad/64 +
-    // 1][2][64] fp32: LSE in base-2 units, then D = dO . O, per 64-row block)
-    void* qt;
-    void* kt;
-    void* dot;
+    // workspace: per-row statistics ([BH][npad/64 + 1][2][64] fp32: LSE in
+    // base-2 units, then D = dO . O, per 64-row block)
     float* stats;
     int npad;
 };
 
-// Bytes of backward workspace for BH query heads and BHkv key/value heads of
-// N rows and head dim d.
-int64_t bwd_workspace_bytes(int64_t BH, int64_t BHkv, int64_t N, int64_t d);
-// Split a workspace into the BwdArgs pieces (a.BH, a.H, a.Hkv, a.N, a.d set).
+// Bytes of backward workspace for BH query heads of N rows.
+int64_t bwd_workspace_bytes(int64_t BH, int64_t N);
+// Point the BwdArgs at their workspace pieces (a.BH, a.N set).
 void bwd_workspace_carve(BwdArgs& a, void* ws);
-// Transposes, row statistics, then the dK/dV and dQ kernels, all on `stream`.
+// Row statistics, then the dK/dV and dQ kernels, all on `stream`.
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream);
 
 // Launchers: return hipSuccess or the launch error.

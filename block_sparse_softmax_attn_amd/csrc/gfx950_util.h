@@ -52,12 +52,64 @@ static __device__ __forceinline__ int k_swz(int r, int c) {
 // Transposed tiles (V^T, Q^T, ...) hold 64 tokens per row: 128-byte rows, 8 chunks.
 static __device__ __forceinline__ int v_swz(int d, int c) { return c ^ ((d >> 1) & 7); }
 
-// Slot of the first key of quad kq (keys 4kq..4kq+3 of a tile) in a V^T row:
-// inside each 16-key group, keys {4h..4h+3, 8+4h..8+4h+3} (the ones lane half
-// h holds in its S^T registers) take slots 8h..8h+7.  Same order as the
-// transpose pass writes.
-static __device__ __forceinline__ int vt_pos_of_quad(int kq) {
-    return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
+// Row r, logical chunk c of a row-major tile that is read both with plain
+// 16-byte loads (16 consecutive rows at one chunk) and with transposing loads
+// (tr_operand below: 4 consecutive rows x 4 consecutive chunks per 32 lanes):
+// the XOR mask is a bijection of the row's low bits (plain reads hit 16
+// distinct slots of a 256-byte bank window) that also moves each of 4
+// consecutive rows to a different 4-chunk quad (transposing reads do too).
+template <int D>
+static __device__ __forceinline__ int rt_swz(int r, int c) {
+    if (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    const int x = (r >> 1) & 7;
+    return c ^ (((x & 1) << 2) | (x >> 1));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane L supplies the
+// address of 4 consecutive 16-bit values; lane j receives element j % 4 of the
+// values read by lanes 4e + j / 4, for e = 0..3.  Read with lane L pointing at
+// row e = L / 4, columns 4 (L % 4) .. +3 of a 4 x 16 block, lane j gets column
+// j, rows 0..3.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+static __device__ __forceinline__ bf16x4 lds_read_tr(const unsigned char* p) {
+    typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+    const v4s_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+// A operand of one v_mfma_f32_32x32x16_bf16 step taken from a row-major
+// [tokens][D] LDS tile (rt_swz layout): lane l holds dim 32 db + l % 32 of the
+// 16 tokens 16g..16g+15, element i of lane half h being token
+// 16g + 8 (i >> 2) + 4h + (i & 3), the order in which the S^T (or S)
+// accumulator registers hold tokens.  Two transposing reads of 4 tokens each;
+// lane L of a 16-lane group points at token 4h + L / 4 (+8 for the second
+// read), dims 32 db + 16 ((l >> 4) & 1) + 4 (L % 4) .. +3.  rt_swz depends on
+// the low 4 bits of the row only, so the byte offsets for g = 0 (TrLane, per
+// lane, computed once) plus 32 D g address every step.
+template <int D>
+struct TrLane {
+    int off[2][D / 32];
+};
+
+template <int D>
+static __device__ __forceinline__ TrLane<D> tr_lane(int lane) {
+    TrLane<D> t;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+            const int row = 8 * a + 4 * (lane >> 5) + ((lane >> 2) & 3);
+            const int ch = 4 * db + 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+            t.off[a][db] = row * (2 * D) + rt_swz<D>(row, ch) * 16 + 8 * (lane & 1);
+        }
+    return t;
+}
+
+template <int D>
+static __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, const TrLane<D>& t, int g, int db) {
+    const bf16x4 lo = lds_read_tr(tile + t.off[0][db] + 32 * D * g);
+    const bf16x4 hi = lds_read_tr(tile + t.off[1][db] + 32 * D * g);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
 static __device__ __forceinline__ float xor32_max(float x) {

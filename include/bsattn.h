@@ -198,12 +198,12 @@ int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* 
  * reconstruction of P, the two traversals that own dK/dV and dQ); FlashAttention
  * notes, section 5.3 (backward recomputation).  Rows without allowed keys
  * (LSE = -inf) get dQ = 0 and contribute nothing.  The launch sequence is:
- * transposes of Q, K, dO into the workspace, the row statistics (LSE in base 2
- * and D), the dK/dV kernel, the dQ kernel, all on `stream`; results are
- * deterministic (no atomics).
+ * the row statistics (LSE in base 2 and D) into the workspace, the dK/dV
+ * kernel, the dQ kernel, all on `stream`; results are deterministic (no
+ * atomics).
  *
  * attn_bwd_workspace_bytes - device workspace attn_bwd and attn_bwd_blocksparse
- *   need: 3*B*H*d*ceil(N/128)*128*2 + B*H*(ceil(N/128)*2 + 1)*512 bytes.
+ *   need (the row statistics): B*H*(ceil(N/128)*2 + 1)*512 bytes.
  *   Returns -1 for sizes or a dtype the kernels do not accept.
  *
  * attn_bwd - gradients of attn_fwd.

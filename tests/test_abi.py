@@ -187,13 +187,14 @@ def test_bwd_workspace_bytes(m):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
     # three transposed tensors [BH][d][npad] bf16 + row statistics [BH][npad/64 + 1][128] fp32
-    assert lib.attn_bwd_workspace_bytes(1, 32, 8192, 128, 1) == 3 * 32 * 128 * 8192 * 2 + 32 * 129 * 512
-    assert lib.attn_bwd_workspace_bytes(1, 16, 16300, 128, 1) == 3 * 16 * 128 * 16384 * 2 + 16 * 257 * 512
-    assert lib.attn_bwd_workspace_bytes(2, 3, 1, 64, 1) == 3 * 6 * 64 * 128 * 2 + 6 * 3 * 512
+    # row statistics only: per head, ceil(N/128)*2 + 1 blocks of 64 rows x (LSE, D) fp32
+    assert lib.attn_bwd_workspace_bytes(1, 32, 8192, 128, 1) == 32 * 129 * 512
+    assert lib.attn_bwd_workspace_bytes(1, 16, 16300, 128, 1) == 16 * 257 * 512
+    assert lib.attn_bwd_workspace_bytes(2, 3, 1, 64, 1) == 6 * 3 * 512
     assert lib.attn_bwd_workspace_bytes(1, 1, 256, 64, 0) == -1          # fp32 backward not provided
     assert lib.attn_bwd_workspace_bytes(1, 1, 256, 96, 1) == -1
     assert lib.attn_bwd_workspace_bytes(1, 0, 256, 64, 1) == -1
-    assert m.bwd_workspace_bytes(1, 2, 300, 128) == 3 * 2 * 128 * 384 * 2 + 2 * 7 * 512
+    assert m.bwd_workspace_bytes(1, 2, 300, 128) == 2 * 7 * 512
 
 
 @pytest.mark.parametrize("args,expect", [
@@ -326,8 +327,8 @@ def test_split_and_ring_entry_points_reject_bad_arguments(m):
 def test_gqa_workspace_and_bad_groups(m):
     from block_sparse_softmax_attn_amd._lib import get
     lib = get()
-    # Q^T and dO^T over the 8 query heads, K^T over the 2 key/value heads, statistics per query head
-    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 2, 1024, 128, 1) == 2 * 8 * 128 * 1024 * 2 + 2 * 128 * 1024 * 2 + 8 * 17 * 512
+    # statistics per query head
+    assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 2, 1024, 128, 1) == 8 * 17 * 512
     assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 8, 1024, 128, 1) == lib.attn_bwd_workspace_bytes(1, 8, 1024, 128, 1)
     assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 3, 1024, 128, 1) == -1
     assert lib.attn_bwd_gqa_workspace_bytes(1, 8, 0, 1024, 128, 1) == -1
