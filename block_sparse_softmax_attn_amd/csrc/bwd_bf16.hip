@@ -154,8 +154,8 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // entries [lo, hi) of the transposed list of query head bh0 + gi (BKV == block)
     auto list_of = [&](int gi, int& lo, int& hi_) {
         const int64_t r = meta_of(bh0 + gi, a.H, a.Hkv, a.meta_heads) * nqb_meta + kt;
-        lo = a.t_row_ptr[r];
-        hi_ = a.t_row_ptr[r + 1];
+        lo = ld_meta(a.t_row_ptr, r);
+        hi_ = ld_meta(a.t_row_ptr, r + 1);
         lo = (int)min<int64_t>(max(lo, 0), a.t_nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.t_nnz);
     };
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         } else {
             int lo, hi_;
             list_of(gi, lo, hi_);
-            const int qb = a.t_col[lo + loc / subs];
+            const int qb = ld_meta(a.t_col, lo + loc / subs);
             t.q0 = (qb >= 0 && qb < nqb_meta) ? qb * a.block + (loc % subs) * BT : -1;
         }
         return t;
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
         subs = a.block / BT;
         nqb_meta = (N + a.block - 1) / a.block;
         const int64_t r = meta_of(bh, a.H, a.Hkv, a.meta_heads) * nqb_meta + qt;   // BM == block for sparse launches
-        int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
+        int lo = ld_meta(a.row_ptr, r), hi_ = ld_meta(a.row_ptr, r + 1);
         lo = (int)min<int64_t>(max(lo, 0), a.nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);
         e0 = lo;
@@ -555,11 +555,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
         KeyTile t;
         if (MODE == (int)Mode::kSparse) {
             const int e = e0 + it / subs;
-            const int kb = a.col[e];
+            const int kb = ld_meta(a.col, e);
             const bool valid = kb >= 0 && kb < nqb_meta;
             t.kb0 = valid ? kb * a.block + (it % subs) * BT : 0;
             t.nlim = valid ? N : 0;
-            t.causal = ((a.flags[e] & 1) != 0) || (a.causal && t.kb0 + BT - 1 > q0);
+            t.causal = ((ld_meta_byte(a.flags, e) & 1) != 0) || (a.causal && t.kb0 + BT - 1 > q0);
         } else {
             t.kb0 = it * BT;
             t.nlim = N;

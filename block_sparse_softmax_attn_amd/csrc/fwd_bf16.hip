@@ -138,7 +138,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         subs = a.block / BN;
         nqb_meta = (N + a.block - 1) / a.block;
         const int64_t r = meta_of(bh, a.H, a.Hkv, a.meta_heads) * nqb_meta + qt;   // BM == block for sparse launches
-        int lo = a.row_ptr[r], hi_ = a.row_ptr[r + 1];
+        int lo = ld_meta(a.row_ptr, r), hi_ = ld_meta(a.row_ptr, r + 1);
         lo = (int)min<int64_t>(max(lo, 0), a.nnz);
         hi_ = (int)min<int64_t>(max(hi_, lo), a.nnz);
         e0 = lo;
@@ -148,13 +148,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         TileDesc t;
         if (MODE == (int)Mode::kSparse) {
             const int e = e0 + it / subs;
-            const int kb = a.col[e];
+            const int kb = ld_meta(a.col, e);
             const bool valid = kb >= 0 && kb < nqb_meta;
             t.kb0 = valid ? kb * a.block + (it % subs) * BN : 0;
             t.nlim = valid ? N : 0;
             // the flag comes from canonical metadata; the geometric test keeps a
             // causal launch correct even for lists that were not pruned
-            t.causal = ((a.flags[e] & 1) != 0) || (a.causal && t.kb0 + BN - 1 > q0);
+            t.causal = ((ld_meta_byte(a.flags, e) & 1) != 0) || (a.causal && t.kb0 + BN - 1 > q0);
         } else if (RANGE) {
             t.kb0 = kv_lo + it * BN;
             t.nlim = kv_hi;
@@ -224,9 +224,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             for (int k = 0; k < D / 16; ++k)
                 qf[k] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * D + 16 * k + 8 * hi);
         }
-        // Q has landed before any tile load is issued: the vmcnt accounting
-        // below then only ever counts tile loads.
-        wait_vmcnt<0>();
+        // The first tiles' loads are issued behind the Q loads, so the two
+        // latencies overlap.  Loads complete in issue order: the wait for tile
+        // 0 below (at most the later tiles' loads outstanding) also covers Q.
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
             if (s < ntiles) issue_tile(describe(s).kb0, kbuf[s], vbuf[s]);

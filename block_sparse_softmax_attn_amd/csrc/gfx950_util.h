@@ -112,6 +112,25 @@ static __device__ __forceinline__ bf16x8 tr_operand(const unsigned char* tile, c
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Read of block-sparse metadata, which an earlier launch (or the host) wrote
+// and nothing changes during this one, through the constant address space: a
+// uniform index compiles to a scalar load, counted by lgkmcnt, so reading the
+// next tile's key block never waits for the direct-to-LDS tile loads in flight
+// (a vector load would need vmcnt(0), which waits for them too).
+template <typename T>
+static __device__ __forceinline__ T ld_meta(const T* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+// One byte of metadata the same way: the scalar unit reads aligned 32-bit
+// words, so the word holding the byte is read (an aligned word never crosses
+// a page, so it is mapped whenever the byte is) and the byte extracted.
+static __device__ __forceinline__ unsigned ld_meta_byte(const uint8_t* p, int64_t i) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(p) + static_cast<uintptr_t>(i);
+    const uint32_t word = *((const __attribute__((address_space(4))) uint32_t*)(addr & ~uintptr_t(3)));
+    return (word >> (8 * (addr & 3))) & 0xffu;
+}
+
 static __device__ __forceinline__ float xor32_max(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
