@@ -125,9 +125,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // of every query head of the key/value head's group
     const int group = a.H / a.Hkv;
     const int64_t BHkv = a.BH / group;
-    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nkt * BHkv);
-    const int64_t kvbh = ord / nkt;
-    const int kt = (int)(ord % nkt);   // causal: the first key tiles see the most queries and start first
+    int64_t kvbh;
+    int kt;   // causal: the first key tiles see the most queries and start first
+    if (MODE == (int)Mode::kDense) {
+        const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nkt * BHkv);
+        kvbh = ord / nkt;
+        kt = (int)(ord % nkt);
+    } else {
+        rank_major_order(blockIdx.x, (int64_t)nkt * BHkv, nkt, kvbh, kt);
+    }
     const int64_t bh0 = (kvbh / a.Hkv) * a.H + (kvbh % a.Hkv) * group;   // first query head of the group
     const int kb0 = kt * G::BKV;
     const int kw0 = kb0 + 32 * pw;     // this wave pair's first key
@@ -519,10 +525,16 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     const TrLane<D> trl = tr_lane<D>(lane);   // transposing-read offsets of K^T
     const int N = a.N;
     const int nqt = (N + G::BM - 1) / G::BM;
-    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nqt * a.BH);
-    const int64_t bh = ord / nqt;
-    int qt = (int)(ord % nqt);
-    if (MODE != (int)Mode::kDense) qt = nqt - 1 - qt;   // heaviest query tiles first
+    int64_t bh;
+    int qt;
+    if (MODE == (int)Mode::kDense) {
+        const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nqt * a.BH);
+        bh = ord / nqt;
+        qt = (int)(ord % nqt);
+    } else {
+        rank_major_order(blockIdx.x, (int64_t)nqt * a.BH, nqt, bh, qt);
+        qt = nqt - 1 - qt;   // heaviest query tiles first
+    }
     const int q0 = qt * G::BM;
     const int q0w = q0 + 32 * w;
     const int qi = q0w + l32;

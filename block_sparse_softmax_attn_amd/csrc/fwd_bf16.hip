@@ -98,14 +98,23 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const int nqt = (N + G::BM - 1) / G::BM;
     const int nsplit = RANGE ? a.nsplit : 1;
     const int64_t total = (int64_t)nqt * a.BH * nsplit;
-    const int64_t ord = xcd_tile_order(blockIdx.x, total);
-    // the query tiles of one (head, split) are consecutive: they share its K/V
-    const int64_t rest = ord / nqt;
+    // The query tiles of one (head, split) run on one XCD: they share its K/V.
+    // Causal tiles differ in cost by up to N / BM times: the costliest tiles
+    // of all the XCD's heads go first.  Block-sparse tiles cost about the same
+    // (a few blocks each): head by head, which keeps one head's K/V hot in L2.
+    int64_t rest;
+    int qt;
+    if (MODE == (int)Mode::kCausal || (RANGE && a.causal)) {
+        rank_major_order(blockIdx.x, total, nqt, rest, qt);
+        qt = nqt - 1 - qt;
+    } else {
+        const int64_t ord = xcd_tile_order(blockIdx.x, total);
+        rest = ord / nqt;
+        qt = (int)(ord % nqt);
+        if (MODE == (int)Mode::kSparse) qt = nqt - 1 - qt;
+    }
     const int split = (int)(rest % nsplit);
     const int64_t bh = rest / nsplit;
-    int qt = (int)(ord % nqt);
-    if (MODE == (int)Mode::kCausal || MODE == (int)Mode::kSparse || (RANGE && a.causal))
-        qt = nqt - 1 - qt;   // heaviest query tiles first
     const int q0 = qt * G::BM;
     const int q0w = q0 + 32 * w;
     const int qi = q0w + l32;  // this lane's query row

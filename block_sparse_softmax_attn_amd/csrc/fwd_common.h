@@ -139,4 +139,27 @@ __device__ __forceinline__ int64_t xcd_tile_order(int64_t wg, int64_t total) {
     return (wg % kXcds) * per + wg / kXcds;
 }
 
+// Item order for launches whose items differ in cost (causal, block-sparse):
+// `total` items are `per_head` tiles of each of several heads.  Each XCD still
+// gets a contiguous range of whole heads (xcd_tile_order), but inside it the
+// items are dispatched rank-major, head-minor, so the costliest tiles of every
+// head of the XCD start first instead of one head at a time.  Returns the head
+// and the tile's rank within it; when the ranges do not hold whole heads the
+// order is head-major.
+__device__ __forceinline__ void rank_major_order(int64_t wg, int64_t total, int per_head, int64_t& head,
+                                                 int& rank) {
+    constexpr int kXcds = 8;
+    const int64_t per = total / kXcds;
+    if (wg < per * kXcds && per % per_head == 0) {
+        const int64_t hx = per / per_head;   // heads per XCD
+        const int64_t x = wg % kXcds, local = wg / kXcds;
+        head = x * hx + local % hx;
+        rank = (int)(local / hx);
+    } else {
+        const int64_t ord = xcd_tile_order(wg, total);
+        head = ord / per_head;
+        rank = (int)(ord % per_head);
+    }
+}
+
 }  // namespace bsattn
