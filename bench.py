@@ -349,7 +349,7 @@ def bench_bwd(args, cfg, dev):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_bwd call: Q/K/dO transposes, row statistics, dK/dV kernel, dQ kernel",
+                     "kernel": "attn_bwd call: row statistics, dK/dV kernel, dQ kernel",
                      "mean_call_ms": round(mean_ms, 5)},
     }
     if not args.no_cpu_baseline:
