@@ -131,6 +131,17 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     const __bf16* Vth = VTR ? nullptr : static_cast<const __bf16*>(a.vt) + kvh * (int64_t)a.npad * D;
     const __bf16* Vh = VTR ? static_cast<const __bf16*>(a.v) + kvh * (int64_t)NK * D : nullptr;
 
+    // Query fragments (B operand of S^T = K Q^T): dims 16k+8hi..+7 of row qi,
+    // loaded before the block-sparse schedule is read so the two latencies
+    // overlap.
+    bf16x8 qf[D / 16];
+    {
+        const int qrow = min(qi, N - 1);
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k)
+            qf[k] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * D + 16 * k + 8 * hi);
+    }
+
     // ---- tile schedule ----
     int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0, kv_lo = 0, kv_hi = 0;
     if (MODE == (int)Mode::kDense) {
@@ -224,15 +235,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     float ell = 0.f;                   // this lane's share of the denominator
     const float sl2 = a.scale_log2;
 
+    if (ntiles == 0) wait_vmcnt<0>();   // nothing to compute: let the query loads land
     if (ntiles > 0) {
-        // Query fragments (B operand of S^T = K Q^T): dims 16k+8hi..+7 of row qi.
-        bf16x8 qf[D / 16];
-        {
-            const int qrow = min(qi, N - 1);
-#pragma unroll
-            for (int k = 0; k < D / 16; ++k)
-                qf[k] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * D + 16 * k + 8 * hi);
-        }
         // The first tiles' loads are issued behind the Q loads, so the two
         // latencies overlap.  Loads complete in issue order: the wait for tile
         // 0 below (at most the later tiles' loads outstanding) also covers Q.
