@@ -119,6 +119,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int l32 = lane & 31, hi = lane >> 5;
     const int role = PAIRED ? w / G::PAIRS : 0, pw = PAIRED ? w % G::PAIRS : w;
     const TrLane<D> trl = tr_lane<D>(lane);   // transposing-read offsets of dO^T / Q^T
+    const RtLane<D> rtl = rt_lane<D>(lane);   // plain fragment offsets of Q / dO
     const int N = a.N;
     const int nkt = (N + G::BKV - 1) / G::BKV;
     // one workgroup per (key/value head, key tile); it sums the contributions
@@ -293,11 +294,10 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         for (int qc = 0; qc < 2; ++qc) {
             pr[qc] = f32x16{};
             if (!live[qc]) continue;
-            const int r = 32 * qc + l32;
             bf16x8 fa[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k)
-                fa[k] = *reinterpret_cast<const bf16x8*>(bA + r * (2 * D) + rt_swz<D>(r, 2 * k + hi) * 16);
+                fa[k] = *reinterpret_cast<const bf16x8*>(bA + rtl.off[k] + 32 * qc * (2 * D));
             __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) pr[qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], kvf[k], pr[qc], 0, 0, 0);
@@ -377,13 +377,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             const int qb0 = q0 + 32 * qc;
             if (causal && qb0 + 31 < kw0) continue;   // all 32 queries precede all keys of this wave
             const bool cmask = causal && qb0 < kw0 + 31;
-            const int r = 32 * qc + l32;
             // ---- S = Q K^T and dP = dO V^T, queries as rows: lane (l32, hi)
             // gets query qb0 + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
             bf16x8 fa[D / 16], fb[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) {
-                const int off = r * (2 * D) + rt_swz<D>(r, 2 * k + hi) * 16;
+                const int off = rtl.off[k] + 32 * qc * (2 * D);
                 fa[k] = *reinterpret_cast<const bf16x8*>(bQ + off);
                 fb[k] = *reinterpret_cast<const bf16x8*>(bO + off);
             }
@@ -523,6 +522,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     const int lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hi = lane >> 5;
     const TrLane<D> trl = tr_lane<D>(lane);   // transposing-read offsets of K^T
+    const RtLane<D> rtl = rt_lane<D>(lane);   // plain fragment offsets of K / V
     const int N = a.N;
     const int nqt = (N + G::BM - 1) / G::BM;
     int64_t bh;
@@ -633,10 +633,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
                 // ---- S^T and dP^T: lane (l32, hi) gets key
                 // kb0 + 32c + 8(v>>2) + 4hi + (v&3) of query qi in element v ----
                 f32x16 s = f32x16{}, dp = f32x16{};
-                const int r = 32 * c + l32;
 #pragma unroll
                 for (int k = 0; k < D / 16; ++k) {
-                    const int off = r * (2 * D) + rt_swz<D>(r, 2 * k + hi) * 16;
+                    const int off = rtl.off[k] + 32 * c * (2 * D);
                     const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(bK + off);
                     const bf16x8 vfr = *reinterpret_cast<const bf16x8*>(bV + off);
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[k], s, 0, 0, 0);

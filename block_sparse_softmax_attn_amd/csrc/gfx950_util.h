@@ -65,6 +65,25 @@ static __device__ __forceinline__ int rt_swz(int r, int c) {
     return c ^ (((x & 1) << 2) | (x >> 1));
 }
 
+// Byte offsets of lane (l32, hi)'s plain 16-byte fragments (row l32, chunk
+// 2k + hi, k < D / 16) in a row-major rt_swz tile.  rt_swz depends on the low
+// 4 row bits only, so row 32c + l32 is at off[k] + 64 D c: with the tile inside
+// the 64 KiB the LDS offset field reaches, each read is a register plus an
+// immediate.
+template <int D>
+struct RtLane {
+    int off[D / 16];
+};
+
+template <int D>
+static __device__ __forceinline__ RtLane<D> rt_lane(int lane) {
+    RtLane<D> t;
+    const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) t.off[k] = l32 * (2 * D) + rt_swz<D>(l32, 2 * k + hi) * 16;
+    return t;
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane L supplies the
 // address of 4 consecutive 16-bit values; lane j receives element j % 4 of the
 // values read by lanes 4e + j / 4, for e = 0..3.  Read with lane L pointing at
