@@ -304,16 +304,18 @@ def bench_bwd(args, cfg, dev):
     q, k, v, do = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
                    .to(torch.bfloat16).contiguous() for _ in range(4))
     dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws = torch.empty(attn.bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.uint8, device=dev)
     if cfg.sparse:
         rp, col = workloads.config_block_lists(cfg)
         mask = attn.blockmask_build(rp, col, 1, cfg.N, cfg.block, cfg.causal)
+        ws = torch.empty(attn.bwd_blocksparse_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, mask), dtype=torch.uint8,
+                         device=dev)
         pairs_head = int(mask.allowed_pairs[0])
         o, lse = attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal)
         step = lambda: attn.attn_bwd_blocksparse(q, k, v, o, lse, do, mask, scale=cfg.scale, causal=cfg.causal,
                                                  dq=dq, dk=dk, dv=dv, workspace=ws)
         mask_lists = (rp, col, pairs_head)
     else:
+        ws = torch.empty(attn.bwd_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d), dtype=torch.uint8, device=dev)
         pairs_head = cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.N
         o, lse = attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal)
         step = lambda: attn.attn_bwd(q, k, v, o, lse, do, scale=cfg.scale, causal=cfg.causal,

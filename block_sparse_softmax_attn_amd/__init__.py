@@ -35,6 +35,7 @@ from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN
 
 __all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "prepared_v_bytes", "prepare_v", "attn_fwd_prepared",
            "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_blocksparse", "bwd_workspace_bytes",
+           "bwd_blocksparse_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_block", "attn_merge", "select_meanpool", "DeviceBlockMask",
            "BlockMask", "AttnError", "LIB_PATH",
            "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
@@ -296,7 +297,9 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int, Hkv: Optional[int] = Non
     return n
 
 
-def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace):
+def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace, need=None, alloc=None):
+    """Checked gradient outputs and workspace: a given workspace needs ``need``
+    bytes; one is allocated (``alloc`` bytes, default ``need``) when none is given."""
     import torch
     _check_qkv(q, k, v)
     if q.dtype != torch.bfloat16:
@@ -313,12 +316,12 @@ def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace):
         if g.shape != like.shape or g.dtype != q.dtype or not g.is_contiguous() or g.device != q.device:
             raise ValueError("gradient outputs must match q (dq) or k, v (dk, dv) and be contiguous")
         grads.append(g)
-    n = int(_get_lib().attn_bwd_gqa_workspace_bytes(B, H, k.shape[1], N, d, ATTN_BF16))
-    if n < 0:
+    if need is None:
+        need = int(_get_lib().attn_bwd_gqa_workspace_bytes(B, H, k.shape[1], N, d, ATTN_BF16))
+    if need < 0:
         raise ValueError("sizes not supported by the backward")
-    need = n
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, alloc or 0), dtype=torch.uint8, device=q.device)
     if workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace must be a contiguous buffer of at least {need} bytes on the inputs' device")
     return grads, workspace, workspace.numel() * workspace.element_size()
@@ -345,6 +348,19 @@ def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool 
     return dq, dk, dv
 
 
+def bwd_blocksparse_workspace_bytes(B: int, H: int, N: int, d: int, mask, Hkv: Optional[int] = None) -> int:
+    """Device workspace (bytes) the bf16 block-sparse backward uses for this
+    mask, including the partial sums of split key-block lists."""
+    Hkv = H if Hkv is None else int(Hkv)
+    t_row_ptr = np.ascontiguousarray(mask.transposed()[0], dtype=np.int32)
+    n = int(_get_lib().attn_bwd_blocksparse_workspace_bytes(int(B), int(H), Hkv, int(N), int(d), ATTN_BF16,
+                                                           int(mask.block), t_row_ptr.ctypes.data_as(ctypes.c_void_p),
+                                                           int(mask.meta_heads)))
+    if n < 0:
+        raise ValueError("sizes or metadata not supported by the block-sparse backward")
+    return n
+
+
 def attn_bwd_blocksparse(q, k, v, o, lse, dout, mask: BlockMask, scale: Optional[float] = None,
                          causal: Optional[bool] = None, dq=None, dk=None, dv=None, workspace=None):
     """Gradients of attn_fwd_blocksparse (bf16)."""
@@ -352,7 +368,12 @@ def attn_bwd_blocksparse(q, k, v, o, lse, dout, mask: BlockMask, scale: Optional
     B, H, N, d = q.shape
     if mask.N != N:
         raise ValueError(f"mask was built for N={mask.N}, inputs have N={N}")
-    (dq, dk, dv), ws, ws_bytes = _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    # a smaller workspace than the full size (down to the minimum) turns the
+    # split of long key-block lists off
+    full = bwd_blocksparse_workspace_bytes(B, H, N, d, mask, Hkv=k.shape[1])
+    least = int(_get_lib().attn_bwd_blocksparse_workspace_bytes(B, H, k.shape[1], N, d, ATTN_BF16, int(mask.block),
+                                                               None, int(mask.meta_heads)))
+    (dq, dk, dv), ws, ws_bytes = _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace, least, full)
     causal = mask.causal if causal is None else bool(causal)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     row_ptr, col, flags = mask.to_device(q.device)

@@ -197,14 +197,16 @@ namespace {
 
 int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
               void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype,
-              float scale, int causal, void* ws, int64_t ws_bytes) {
+              float scale, int causal, void* ws, int64_t ws_bytes, int64_t block = 0) {
     int st = check_common(q, k, v, const_cast<void*>(o), const_cast<float*>(lse), B, H, N, d, dtype, scale, causal);
     if (st != ATTN_OK) return st;
     if (dtype != ATTN_BF16) return ATTN_EUNSUPPORTED;
     if (!valid_groups(H, Hkv)) return ATTN_EINVAL;
     if (!dout || !dq || !dk || !dv) return ATTN_EINVAL;
     if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv)) return ATTN_EINVAL;
-    if (ws_bytes < bsattn::bwd_workspace_bytes(B * H, N)) return ATTN_ECAPACITY;
+    const int64_t need = block ? bsattn::bwd_sparse_workspace_base(B * H, B * Hkv, N, block)
+                               : bsattn::bwd_workspace_bytes(B * H, N);
+    if (ws_bytes < need) return ATTN_ECAPACITY;
     if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return ATTN_EINVAL;
     return ATTN_OK;
 }
@@ -262,10 +264,14 @@ int bwd_sparse(const void* q, const void* k, const void* v, const void* o, const
                float scale, int causal, int64_t block, const int32_t* row_ptr, const int32_t* col,
                const uint8_t* flags, int64_t nnz, const int32_t* t_row_ptr, const int32_t* t_col,
                int64_t meta_heads, void* workspace, int64_t ws_bytes, hipStream_t stream) {
+    if (block != 64 && block != 128) {
+        const int st0 = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, dtype, scale, causal,
+                                  workspace, ws_bytes);
+        return st0 != ATTN_OK ? st0 : ATTN_EUNSUPPORTED;
+    }
     int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, Hkv, N, d, dtype, scale, causal, workspace,
-                       ws_bytes);
+                       ws_bytes, block);
     if (st != ATTN_OK) return st;
-    if (block != 64 && block != 128) return ATTN_EUNSUPPORTED;
     if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv && meta_heads != B * H) return ATTN_EINVAL;
     if (!row_ptr || !t_row_ptr || nnz < 0 || nnz > INT32_MAX) return ATTN_EINVAL;
     if (nnz > 0 && (!col || !flags || !t_col)) return ATTN_EINVAL;
@@ -279,6 +285,7 @@ int bwd_sparse(const void* q, const void* k, const void* v, const void* o, const
     a.t_nnz = nnz;
     a.meta_heads = static_cast<int>(meta_heads);
     a.block = static_cast<int>(block);
+    bsattn::bwd_sparse_workspace_carve(a, workspace, ws_bytes);
     const hipError_t e = bsattn::launch_bwd_bf16(a, bsattn::Mode::kSparse, stream);
     return e == hipSuccess ? ATTN_OK : ATTN_EHIP;
 }
@@ -287,6 +294,20 @@ int bwd_sparse(const void* q, const void* k, const void* v, const void* o, const
 
 extern "C" int64_t attn_bwd_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int dtype) {
     return bwd_ws(B, H, H, N, d, dtype);
+}
+
+extern "C" int64_t attn_bwd_blocksparse_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d,
+                                                        int dtype, int64_t block, const int32_t* t_row_ptr,
+                                                        int64_t meta_heads) {
+    if (bwd_ws(B, H, Hkv, N, d, dtype) < 0 || (block != 64 && block != 128)) return -1;
+    if (meta_heads != 1 && meta_heads != H && meta_heads != Hkv && meta_heads != B * H) return -1;
+    const int64_t base = bsattn::bwd_sparse_workspace_base(B * H, B * Hkv, N, block);
+    if (!t_row_ptr) return base;
+    const int64_t slots = bsattn::bwd_sparse_slots(t_row_ptr, B, H, Hkv, N, block, meta_heads);
+    if (slots == 0) return base;
+    const int64_t per_slot = bsattn::bwd_sparse_slot_bytes(block, d) + 8;   // partials + extra-list entry
+    if (slots > (int64_t(1) << 40) / per_slot) return -1;
+    return base + 256 + slots * per_slot;
 }
 
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fwd_common.h"
 #include "gfx950_util.h"
 
@@ -43,6 +45,40 @@ namespace {
 
 constexpr int BT = 64;   // tokens per streamed tile: queries (dK/dV) or keys (dQ)
 constexpr float kLog2e = 1.4426950408889634f;
+
+// Block-sparse dK/dV: a key block whose list holds more than kPieceTiles query
+// tiles is split into up to kMaxPieces pieces, each a workgroup of its own
+// (a globally listed key block would otherwise run its whole list in one
+// workgroup while the rest of the GPU idles).
+constexpr int kPieceTiles = 32;
+constexpr int kMaxPieces = 8;
+
+__host__ __device__ inline int pieces_of(int ntiles) {
+    if (ntiles <= kPieceTiles) return 1;
+    return min(kMaxPieces, (ntiles + kPieceTiles - 1) / kPieceTiles);
+}
+
+// Entry idx of the split plan, written by the plan launch (scalar loads).
+__device__ inline int2 plan_at(const BwdArgs& a, int64_t idx) {
+    const int32_t* p = reinterpret_cast<const int32_t*>(a.plan);
+    return make_int2(ld_meta(p, 2 * idx), ld_meta(p, 2 * idx + 1));
+}
+
+// Query tiles the key tile kt of key/value head kvbh visits, over the query
+// heads of its group, in a block-sparse launch (BKV == block).
+__device__ inline int sparse_key_tiles(const BwdArgs& a, int64_t kvbh, int kt, int nqb_meta, int subs) {
+    const int group = a.H / a.Hkv;
+    const int64_t bh0 = (kvbh / a.Hkv) * a.H + (kvbh % a.Hkv) * group;
+    int n = 0;
+    for (int gi = 0; gi < group; ++gi) {
+        const int64_t r = meta_of(bh0 + gi, a.H, a.Hkv, a.meta_heads) * nqb_meta + kt;
+        int lo = ld_meta(a.t_row_ptr, r), hi_ = ld_meta(a.t_row_ptr, r + 1);
+        lo = (int)min<int64_t>(max(lo, 0), a.t_nnz);
+        hi_ = (int)min<int64_t>(max(hi_, lo), a.t_nnz);
+        n += (hi_ - lo) * subs;
+    }
+    return n;
+}
 
 // ---------------------------------------------------------------------------
 // row statistics: one workgroup per 64-row block (plus one padding block)
@@ -128,7 +164,17 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int64_t BHkv = a.BH / group;
     int64_t kvbh;
     int kt;   // causal: the first key tiles see the most queries and start first
-    if (MODE == (int)Mode::kDense) {
+    // block-sparse: the main launch runs piece 0 of every key tile, the extra
+    // launch the other pieces of split key tiles from the plan's list
+    int piece = 0;
+    if (MODE == (int)Mode::kSparse && a.extra_pass) {
+        const int32_t* ex = reinterpret_cast<const int32_t*>(a.extra);
+        const int64_t item = ld_meta(ex, 2 * (int64_t)blockIdx.x);
+        piece = ld_meta(ex, 2 * (int64_t)blockIdx.x + 1);
+        if (item < 0 || piece < 1) return;   // uniform: before any barrier
+        kvbh = item / nkt;
+        kt = (int)(item % nkt);
+    } else if (MODE == (int)Mode::kDense) {
         const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nkt * BHkv);
         kvbh = ord / nkt;
         kt = (int)(ord % nkt);
@@ -181,6 +227,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             ntiles += (hi_ - lo) * subs;
         }
     }
+    // this workgroup's piece of the tile list (the plan's choice: a split the
+    // workspace cannot hold was turned off there)
+    const int npieces = MODE == (int)Mode::kSparse ? plan_at(a, kvbh * nkt + kt).y : 1;
+    if (piece >= npieces) return;   // uniform: before any barrier
+    const int psize = (ntiles + npieces - 1) / npieces;
+    const int t_lo = piece * psize, t_hi = min(ntiles, t_lo + psize);
     // Tile it: its query head and first query (-1 for an out-of-range entry).
     struct QTile {
         int64_t bhq;
@@ -446,16 +498,38 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     auto step = [&](int it, int u) {
         wait_vmcnt<0>();
         barrier();
-        if (it + 1 < ntiles) issue(locate(it + 1), u ^ 1);
+        if (it + 1 < t_hi) issue(locate(it + 1), u ^ 1);
         const int q0 = locate(it).q0;
         if (q0 < 0 || q0 >= N) return;                  // the same for every wave
         if (causal && q0 + BT - 1 < kb0) return;         // the whole tile precedes every key of the workgroup
         compute(q0, u);
     };
-    if (ntiles > 0) issue(locate(0), 0);
-    for (int base = 0; base < ntiles; base += 2) {
+    if (t_lo < t_hi) issue(locate(t_lo), 0);
+    for (int base = t_lo; base < t_hi; base += 2) {
         step(base, 0);
-        if (base + 1 < ntiles) step(base + 1, 1);
+        if (base + 1 < t_hi) step(base + 1, 1);
+    }
+
+    if (npieces > 1) {   // fp32 partial sums of this piece: reduced in piece order afterwards
+        const int slot = plan_at(a, kvbh * nkt + kt).x + piece;
+        float* pK = a.part + (int64_t)slot * (2 * G::BKV * D) + (int64_t)(kj - kb0) * D;
+        float* pV = pK + G::BKV * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int c = 32 * db + 8 * j + 4 * hi;
+                if constexpr (PAIRED) {
+                    const float4 x = {acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
+                    *reinterpret_cast<float4*>((role == 0 ? pV : pK) + c) = x;
+                } else {
+                    const float4 xk = {dkacc[db][4 * j], dkacc[db][4 * j + 1], dkacc[db][4 * j + 2], dkacc[db][4 * j + 3]};
+                    const float4 xv = {dvacc[db][4 * j], dvacc[db][4 * j + 1], dvacc[db][4 * j + 2], dvacc[db][4 * j + 3]};
+                    *reinterpret_cast<float4*>(pK + c) = xk;
+                    *reinterpret_cast<float4*>(pV + c) = xv;
+                }
+            }
+        return;
     }
 
     // ---- epilogue: dV = (dO^T P)^T, dK = scale * (Q^T dS)^T ----
@@ -697,6 +771,98 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// block-sparse dK/dV split: plan and ordered reduction
+// ---------------------------------------------------------------------------
+
+// One workgroup: for every (key/value head, key tile) in order, its number of
+// pieces and the first of its partial slots (an exclusive scan over the split
+// items; unsplit items get slot -1).
+template <int BKV>
+__global__ __launch_bounds__(256) void bwd_plan_kernel(BwdArgs a, int nkt, int64_t items) {
+    __shared__ int warp_tot[4];
+    __shared__ int carry;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nqb_meta = (a.N + a.block - 1) / a.block, subs = a.block / BT;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < items; base += 256) {
+        const int64_t it = base + tid;
+        int np = 0;
+        if (it < items) np = pieces_of(sparse_key_tiles(a, it / nkt, (int)(it % nkt), nqb_meta, subs));
+        const int need = np > 1 ? np : 0;
+        // inclusive scan inside the wave, then across the 4 waves
+        int x = need;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) warp_tot[w] = x;
+        __syncthreads();
+        int before = carry;
+        for (int i = 0; i < w; ++i) before += warp_tot[i];
+        if (it < items) a.plan[it] = make_int2(need ? before + x - need : -1, max(np, 1));
+        __syncthreads();
+        if (tid == 255) carry = before + x;
+        __syncthreads();
+    }
+    const int used = carry;
+    __syncthreads();
+    if (used > a.part_slots) {   // the workspace holds fewer slots: no key tile is split
+        for (int64_t it = tid; it < items; it += 256) a.plan[it] = make_int2(-1, 1);
+        for (int64_t w2 = tid; w2 < a.part_slots; w2 += 256) a.extra[w2] = make_int2(-1, -1);
+        return;
+    }
+    // the extra-piece list, indexed by slot: slot base + p holds (item, p)
+    for (int64_t w2 = used + tid; w2 < a.part_slots; w2 += 256) a.extra[w2] = make_int2(-1, -1);
+    for (int64_t it = tid; it < items; it += 256) {
+        const int2 pl = a.plan[it];
+        for (int p = 0; p < pl.y && pl.x >= 0; ++p) a.extra[pl.x + p] = make_int2((int)it, p);
+    }
+}
+
+// One workgroup per (key/value head, key tile): dK = scale * sum of the pieces'
+// partials, dV = sum, in piece order (deterministic), for split key tiles.
+// Each thread owns E float4 of dK and of dV and adds the pieces one after the
+// other, so each piece is E independent loads in flight per thread.
+template <int D, int BKV>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int nkt) {
+    constexpr int E = BKV * D / (256 * 4);
+    const int64_t item = blockIdx.x;
+    const int2 pl = plan_at(a, item);
+    if (pl.y <= 1) return;
+    const int64_t kvbh = item / nkt;
+    const int kb0 = (int)(item % nkt) * BKV;
+    const float* base = a.part + (int64_t)pl.x * (2 * BKV * D);
+    float4 sk[E], sv[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) sk[i] = sv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = 0; p < pl.y; ++p) {
+        const float* pk = base + (int64_t)p * (2 * BKV * D);
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+            const int e = (threadIdx.x + 256 * i) * 4;
+            const float4 xk = *reinterpret_cast<const float4*>(pk + e);
+            const float4 xv = *reinterpret_cast<const float4*>(pk + BKV * D + e);
+            sk[i].x += xk.x; sk[i].y += xk.y; sk[i].z += xk.z; sk[i].w += xk.w;
+            sv[i].x += xv.x; sv[i].y += xv.y; sv[i].z += xv.z; sv[i].w += xv.w;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const int e = (threadIdx.x + 256 * i) * 4;
+        const int key = e / D, c = e % D;
+        if (kb0 + key >= a.N) continue;
+        const int64_t row = (kvbh * a.N + kb0 + key) * (int64_t)D + c;
+        const bf16x4 ok = {(__bf16)(sk[i].x * a.scale), (__bf16)(sk[i].y * a.scale), (__bf16)(sk[i].z * a.scale),
+                           (__bf16)(sk[i].w * a.scale)};
+        const bf16x4 ov = {(__bf16)sv[i].x, (__bf16)sv[i].y, (__bf16)sv[i].z, (__bf16)sv[i].w};
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dk) + row) = ok;
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dv) + row) = ov;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 
@@ -706,7 +872,15 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
     const int64_t bhkv = a.BH / (a.H / a.Hkv);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE, PAIRED>), dim3((unsigned)(nkt * bhkv)), dim3(64 * NW), 0, stream,
                        a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && MODE == (int)Mode::kSparse && a.part_slots > 0) {   // the other pieces of split key tiles
+        BwdArgs b = a;
+        b.extra_pass = 1;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE, PAIRED>), dim3((unsigned)a.part_slots), dim3(64 * NW), 0,
+                           stream, b);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 template <int D, int NW, int NS, int MODE>
@@ -734,13 +908,30 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
         case Mode::kCausal:
             e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kCausal>(a, stream);
             return e != hipSuccess ? e : launch_dq<D, 8, 3, (int)Mode::kCausal>(a, stream);
-        case Mode::kSparse:
+        case Mode::kSparse: {
+            // split plan, dK/dV (pieces of long key-tile lists write partials),
+            // the ordered reduction of split key tiles, dQ
+            const int nkt = (a.N + a.block - 1) / a.block;
+            const int64_t items = (int64_t)nkt * (a.BH / (a.H / a.Hkv));
             if (a.block == 128) {
-                e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kSparse>(a, stream);
+                hipLaunchKernelGGL(bwd_plan_kernel<128>, dim3(1), dim3(256), 0, stream, a, nkt, items);
+                e = hipGetLastError();
+                if (e == hipSuccess) e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kSparse>(a, stream);
+                if (e == hipSuccess) {
+                    hipLaunchKernelGGL((bwd_reduce_kernel<D, 128>), dim3((unsigned)items), dim3(256), 0, stream, a, nkt);
+                    e = hipGetLastError();
+                }
                 return e != hipSuccess ? e : launch_dq<D, 4, 2, (int)Mode::kSparse>(a, stream);
             }
-            e = launch_dkdv<D, D == 64 ? 2 : 4, (int)Mode::kSparse>(a, stream);
+            hipLaunchKernelGGL(bwd_plan_kernel<64>, dim3(1), dim3(256), 0, stream, a, nkt, items);
+            e = hipGetLastError();
+            if (e == hipSuccess) e = launch_dkdv<D, D == 64 ? 2 : 4, (int)Mode::kSparse>(a, stream);
+            if (e == hipSuccess) {
+                hipLaunchKernelGGL((bwd_reduce_kernel<D, 64>), dim3((unsigned)items), dim3(256), 0, stream, a, nkt);
+                e = hipGetLastError();
+            }
             return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse>(a, stream);
+        }
         case Mode::kRange: break;   // no backward for key-range launches
     }
     return hipErrorInvalidValue;
@@ -756,6 +947,52 @@ int64_t bwd_workspace_bytes(int64_t BH, int64_t N) {
 void bwd_workspace_carve(BwdArgs& a, void* ws) {
     a.npad = (int)vt_padded_keys(a.N);
     a.stats = static_cast<float*>(ws);
+}
+
+namespace {
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+int64_t bwd_sparse_workspace_base(int64_t BH, int64_t BHkv, int64_t N, int64_t block) {
+    const int64_t nkt = (N + block - 1) / block;
+    return align256(bwd_workspace_bytes(BH, N)) + align256(BHkv * nkt * (int64_t)sizeof(int2));
+}
+
+int64_t bwd_sparse_slot_bytes(int64_t block, int64_t d) { return 2 * block * d * 4; }
+
+int64_t bwd_sparse_slots(const int32_t* t_row_ptr, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t block,
+                         int64_t meta_heads) {
+    const int64_t nkt = (N + block - 1) / block, group = H / Hkv, subs = block / BT;
+    const int64_t nnz = t_row_ptr[meta_heads * nkt];
+    int64_t slots = 0;
+    for (int64_t kvbh = 0; kvbh < B * Hkv; ++kvbh) {
+        const int64_t bh0 = (kvbh / Hkv) * H + (kvbh % Hkv) * group;
+        for (int64_t kt = 0; kt < nkt; ++kt) {
+            int64_t tiles = 0;
+            for (int64_t gi = 0; gi < group; ++gi) {
+                const int64_t r = meta_of(bh0 + gi, (int)H, (int)Hkv, (int)meta_heads) * nkt + kt;
+                int64_t lo = std::min<int64_t>(std::max<int64_t>(t_row_ptr[r], 0), nnz);
+                int64_t hi = std::min<int64_t>(std::max<int64_t>(t_row_ptr[r + 1], lo), nnz);
+                tiles += (hi - lo) * subs;
+            }
+            const int np = pieces_of((int)std::min<int64_t>(tiles, INT32_MAX));
+            if (np > 1) slots += np;
+        }
+    }
+    return slots;
+}
+
+void bwd_sparse_workspace_carve(BwdArgs& a, void* ws, int64_t ws_bytes) {
+    bwd_workspace_carve(a, ws);
+    const int64_t group = a.H / a.Hkv, BHkv = a.BH / group;
+    unsigned char* p = static_cast<unsigned char*>(ws);
+    a.plan = reinterpret_cast<int2*>(p + align256(bwd_workspace_bytes(a.BH, a.N)));
+    const int64_t base = bwd_sparse_workspace_base(a.BH, BHkv, a.N, a.block);
+    const int64_t per_slot = bwd_sparse_slot_bytes(a.block, a.d) + (int64_t)sizeof(int2);
+    a.part_slots = std::min<int64_t>(std::max<int64_t>(0, ws_bytes - base - 256) / per_slot, INT32_MAX);
+    a.extra = reinterpret_cast<int2*>(p + base);
+    a.part = reinterpret_cast<float*>(p + base + align256(a.part_slots * (int64_t)sizeof(int2)));
+    a.extra_pass = 0;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream) {

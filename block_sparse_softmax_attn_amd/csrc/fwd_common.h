@@ -111,12 +111,36 @@ struct BwdArgs {
     // base-2 units, then D = dO . O, per 64-row block)
     float* stats;
     int npad;
+    // block-sparse dK/dV: a key block whose query-tile list is long is split
+    // into up to `pieces` pieces of workgroups; plan[kvbh * nkt + kt] = (first
+    // partial slot, pieces) and the pieces' fp32 partial dK, dV go to
+    // part[slot][2][BKV][d] for an ordered reduction.
+    // The main dK/dV launch runs piece 0 of every key tile; a second launch of
+    // part_slots workgroups runs extra[w] = (key tile, piece >= 1) of the split
+    // ones ((-1, -1) past the used slots; piece 0 entries are skipped).
+    int extra_pass;
+    int2* plan;
+    int2* extra;
+    float* part;
+    int64_t part_slots;   // partial slots the workspace holds (no split beyond them)
 };
 
-// Bytes of backward workspace for BH query heads of N rows.
+// Bytes of backward workspace for BH query heads of N rows (dense, causal).
 int64_t bwd_workspace_bytes(int64_t BH, int64_t N);
-// Point the BwdArgs at their workspace pieces (a.BH, a.N set).
+// The block-sparse backward's workspace: the row statistics and the split
+// plan (the minimum), then, per partial dK/dV slot of BKV = block keys, its
+// fp32 partials and its entry of the extra-piece list (plus 256 bytes of
+// alignment once).
+int64_t bwd_sparse_workspace_base(int64_t BH, int64_t BHkv, int64_t N, int64_t block);
+int64_t bwd_sparse_slot_bytes(int64_t block, int64_t d);
+// Partial slots the split plan uses for host transposed offsets t_row_ptr
+// ([meta_heads * ceil(N / block) + 1]).
+int64_t bwd_sparse_slots(const int32_t* t_row_ptr, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t block,
+                         int64_t meta_heads);
+// Point the BwdArgs at their workspace pieces (a.BH, a.N set; for the sparse
+// backward also a.H, a.Hkv, a.d, a.block, a.meta_heads, and ws_bytes given).
 void bwd_workspace_carve(BwdArgs& a, void* ws);
+void bwd_sparse_workspace_carve(BwdArgs& a, void* ws, int64_t ws_bytes);
 // Row statistics, then the dK/dV and dQ kernels, all on `stream`.
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream);
 

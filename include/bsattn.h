@@ -239,16 +239,34 @@ int attn_blockmask_transpose(const int32_t* row_ptr, const int32_t* col, int64_t
                              int64_t block, int32_t* t_row_ptr, int32_t* t_col, int64_t capacity);
 
 /*
+ * attn_bwd_blocksparse_workspace_bytes - device workspace attn_bwd_blocksparse
+ *   and attn_bwd_blocksparse_gqa use for this metadata: the row statistics,
+ *   the split plan, and fp32 partial dK, dV (2 * block * d * 4 bytes each) for
+ *   the pieces of long key-block lists.  A key block whose transposed list
+ *   holds more than 32 query tiles of 64 rows is processed by up to 8
+ *   workgroups, one per piece of the list; their partial sums are added in
+ *   piece order by a reduction pass (deterministic).
+ *   t_row_ptr : HOST copy of attn_blockmask_transpose's offsets for the
+ *               metadata ([meta_heads * ceil(N / block) + 1]), or NULL: then
+ *               the minimum workspace (no list is split).  A workspace between
+ *               the minimum and the returned size is accepted; the split is
+ *               then turned off for the whole call.
+ *   Returns -1 for sizes, dtype, block or meta_heads the backward does not accept.
+ *
  * attn_bwd_blocksparse - gradients of attn_fwd_blocksparse.
- *   Tensor, size and workspace arguments as for attn_bwd; block, row_ptr, col,
- *   flags, nnz, meta_heads as for attn_fwd_blocksparse (DEVICE copies of the
+ *   Tensor and size arguments as for attn_bwd; block, row_ptr, col, flags,
+ *   nnz, meta_heads as for attn_fwd_blocksparse (DEVICE copies of the
  *   canonical metadata); t_row_ptr, t_col: DEVICE copies of
  *   attn_blockmask_transpose's output for the same metadata (nnz entries).
- *   Offsets are clamped to nnz and out-of-range entries are skipped, as in the
- *   forward.  Source: as for attn_bwd, over the active key-block sets of
- *   "Exact Blocks, Rings, and Sparsity", section 5.
+ *   workspace : device, at least attn_bwd_blocksparse_workspace_bytes(..., NULL,
+ *   ...) bytes, 256-byte aligned.  Offsets are clamped to nnz and out-of-range
+ *   entries are skipped, as in the forward.  Source: as for attn_bwd, over the
+ *   active key-block sets of "Exact Blocks, Rings, and Sparsity", section 5.
  *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_ECAPACITY, ATTN_EHIP.
  */
+int64_t attn_bwd_blocksparse_workspace_bytes(int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t d, int dtype,
+                                             int64_t block, const int32_t* t_row_ptr, int64_t meta_heads);
+
 int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
                          int dtype, float scale, int causal, int64_t block,

@@ -197,6 +197,41 @@ def test_bwd_workspace_bytes(m):
     assert m.bwd_workspace_bytes(1, 2, 300, 128) == 2 * 7 * 512
 
 
+def test_bwd_blocksparse_workspace_bytes_counts_split_slots(m):
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    a256 = lambda x: (x + 255) // 256 * 256
+    B, H, Hkv, N, d, block = 1, 4, 2, 8192, 128, 128
+    nb = N // block
+    # key block 0 is listed by every query block (64 entries = 128 tiles of 64
+    # queries per query head), the others by one query block each
+    lists = [[0, qb] if qb else [0] for qb in range(nb)]
+    rp, col = workloads.lists_to_csr(lists)
+    mask = m.blockmask_build(rp, col, 1, N, block, False)
+    t_rp = np.ascontiguousarray(mask.transposed()[0], dtype=np.int32)
+    ptr = t_rp.ctypes.data_as(ctypes.c_void_p)
+    base = a256(B * H * (nb * 2 + 1) * 512) + a256(B * Hkv * nb * 8)
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, block, None, 1) == base
+    # group of 2 query heads: 256 tiles on key block 0 -> min(8, ceil(256 / 32)) = 8 pieces per key/value
+    # head; each slot holds fp32 partial dK, dV and one 8-byte entry of the extra-piece list
+    slot = 2 * block * d * 4 + 8
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, block, ptr, 1) == base + 256 + 2 * 8 * slot
+    assert m.bwd_blocksparse_workspace_bytes(B, H, N, d, mask, Hkv=Hkv) == base + 256 + 2 * 8 * slot
+    # one query head per key/value head: 128 tiles -> 4 pieces
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, H, N, d, 1, block, ptr, 1) == (
+        a256(B * H * (nb * 2 + 1) * 512) + a256(B * H * nb * 8) + 256 + 4 * 4 * slot)
+    # lists of at most 32 tiles are not split
+    short = [[qb] for qb in range(nb)]
+    rp2, col2 = workloads.lists_to_csr(short)
+    t2 = np.ascontiguousarray(m.blockmask_build(rp2, col2, 1, N, block, False).transposed()[0], dtype=np.int32)
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, block, t2.ctypes.data_as(ctypes.c_void_p),
+                                                    1) == base
+    # rejected: fp32, block size, meta_heads
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 0, block, None, 1) == -1
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, 32, None, 1) == -1
+    assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, block, None, 3) == -1
+
+
 @pytest.mark.parametrize("args,expect", [
     (dict(q=0), -1), (dict(dout=0), -1), (dict(dq=0), -1), (dict(dv=FAKE + 4), -1), (dict(lse=FAKE + 8), -1),
     (dict(B=0), -1), (dict(N=0), -1), (dict(d=96), -2), (dict(dtype=0), -2), (dict(dtype=5), -2),

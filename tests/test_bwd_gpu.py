@@ -216,6 +216,40 @@ def test_bwd_dense_b1_h32_n8192_d128(lib):
     _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, False, cfg.seed, heads=[(0, 5)])
 
 
+def _global_column_lists(nb):
+    """Every query block lists key block 0 (a globally attended block) and its own block."""
+    return [[0, qb] if qb else [0] for qb in range(nb)]
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_bwd_sparse_long_key_lists_split_or_not(lib, split):
+    # key block 0 of 64-key blocks is listed by all 70 query blocks (70 tiles > 32): with the full
+    # workspace its dK/dV are summed from 3 pieces, with the minimum workspace in one workgroup
+    B, H, N, d, block = 1, 2, 4480, 64, 64
+    print(f"case bwd sparse split={split}", flush=True)
+    lists = _global_column_lists(N // block)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    rp, col = workloads.lists_to_csr(lists)
+    mask = lib.blockmask_build(rp, col, 1, N, block, True)
+    fwd = lambda q, k, v: oracle.attn_fwd_blocksparse(q, k, v, scale, True, block, rp, col, 1)
+    q, k, v, do, o_in, lse_in = _setup(B, H, N, d, 4800, fwd, [(0, 1)],
+                                       lambda q, k, v: lib.attn_fwd_blocksparse(q, k, v, mask, scale=scale))
+    full = lib.bwd_blocksparse_workspace_bytes(B, H, N, d, mask)
+    least = int(lib._get_lib().attn_bwd_blocksparse_workspace_bytes(B, H, H, N, d, 1, block, None, 1))
+    assert full > least
+    ws = torch.empty(full if split else least, dtype=torch.uint8, device="cuda")
+    grads = lib.attn_bwd_blocksparse(*(t.cuda() for t in (q, k, v, o_in, lse_in, do)), mask, scale=scale,
+                                     workspace=ws)
+    again = lib.attn_bwd_blocksparse(*(t.cuda() for t in (q, k, v, o_in, lse_in, do)), mask, scale=scale,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(grads, again))   # deterministic, split or not
+    allowed = lambda b, h: (lambda rows: A.token_mask_block_sparse(N, True, block, rp, col, 0, rows))
+    ref = lambda b, h, q_, k_, v_, do_, o_, l_: oracle.attention_head_bwd(q_, k_, v_, do_, scale, allowed(b, h),
+                                                                        o=o_, lse=l_)
+    _check_heads(grads, q, k, v, do, o_in, lse_in, scale, [(0, 1)], allowed, ref, f"bwd sparse split={split}")
+
+
 def test_bwd_block_sparse_b1_h16_n16300_d128(lib):
     cfg = workloads.CONFIGS["c4"]
     print("case bwd c4", flush=True)
