@@ -164,10 +164,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     const int64_t BHkv = a.BH / group;
     int64_t kvbh;
     int kt;   // causal: the first key tiles see the most queries and start first
-    // block-sparse: the main launch runs piece 0 of every key tile, the extra
-    // launch the other pieces of split key tiles from the plan's list
+    // block-sparse: the first part_slots workgroups run the pieces >= 1 of
+    // split key tiles from the plan's list (so the long lists start first),
+    // the others piece 0 of every key tile
     int piece = 0;
-    if (MODE == (int)Mode::kSparse && a.extra_pass) {
+    const int64_t nextra = MODE == (int)Mode::kSparse ? a.part_slots : 0;
+    if (MODE == (int)Mode::kSparse && (int64_t)blockIdx.x < nextra) {
         const int32_t* ex = reinterpret_cast<const int32_t*>(a.extra);
         const int64_t item = ld_meta(ex, 2 * (int64_t)blockIdx.x);
         piece = ld_meta(ex, 2 * (int64_t)blockIdx.x + 1);
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         kvbh = ord / nkt;
         kt = (int)(ord % nkt);
     } else {
-        rank_major_order(blockIdx.x, (int64_t)nkt * BHkv, nkt, kvbh, kt);
+        rank_major_order(blockIdx.x - nextra, (int64_t)nkt * BHkv, nkt, kvbh, kt);
     }
     const int64_t bh0 = (kvbh / a.Hkv) * a.H + (kvbh % a.Hkv) * group;   // first query head of the group
     const int kb0 = kt * G::BKV;
@@ -870,17 +872,10 @@ template <int D, int NW, int MODE, bool PAIRED = (D == 128)>
 hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
     const int64_t nkt = (a.N + DkdvGeo<D, NW, PAIRED>::BKV - 1) / DkdvGeo<D, NW, PAIRED>::BKV;
     const int64_t bhkv = a.BH / (a.H / a.Hkv);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE, PAIRED>), dim3((unsigned)(nkt * bhkv)), dim3(64 * NW), 0, stream,
-                       a);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && MODE == (int)Mode::kSparse && a.part_slots > 0) {   // the other pieces of split key tiles
-        BwdArgs b = a;
-        b.extra_pass = 1;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE, PAIRED>), dim3((unsigned)a.part_slots), dim3(64 * NW), 0,
-                           stream, b);
-        e = hipGetLastError();
-    }
-    return e;
+    const int64_t extra = MODE == (int)Mode::kSparse ? a.part_slots : 0;   // workgroups for the extra pieces
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, NW, MODE, PAIRED>), dim3((unsigned)(extra + nkt * bhkv)), dim3(64 * NW), 0,
+                       stream, a);
+    return hipGetLastError();
 }
 
 template <int D, int NW, int NS, int MODE>
@@ -989,10 +984,13 @@ void bwd_sparse_workspace_carve(BwdArgs& a, void* ws, int64_t ws_bytes) {
     a.plan = reinterpret_cast<int2*>(p + align256(bwd_workspace_bytes(a.BH, a.N)));
     const int64_t base = bwd_sparse_workspace_base(a.BH, BHkv, a.N, a.block);
     const int64_t per_slot = bwd_sparse_slot_bytes(a.block, a.d) + (int64_t)sizeof(int2);
-    a.part_slots = std::min<int64_t>(std::max<int64_t>(0, ws_bytes - base - 256) / per_slot, INT32_MAX);
+    // no more slots than key tiles times pieces, and a launch grid (slots plus
+    // key tiles) that fits 32 bits
+    const int64_t items = (a.N + a.block - 1) / a.block * BHkv;
+    a.part_slots = std::max<int64_t>(0, ws_bytes - base - 256) / per_slot;
+    a.part_slots = std::min<int64_t>({a.part_slots, items * kMaxPieces, (int64_t)INT32_MAX - items});
     a.extra = reinterpret_cast<int2*>(p + base);
     a.part = reinterpret_cast<float*>(p + base + align256(a.part_slots * (int64_t)sizeof(int2)));
-    a.extra_pass = 0;
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream) {

@@ -115,10 +115,10 @@ struct BwdArgs {
     // into up to `pieces` pieces of workgroups; plan[kvbh * nkt + kt] = (first
     // partial slot, pieces) and the pieces' fp32 partial dK, dV go to
     // part[slot][2][BKV][d] for an ordered reduction.
-    // The main dK/dV launch runs piece 0 of every key tile; a second launch of
-    // part_slots workgroups runs extra[w] = (key tile, piece >= 1) of the split
-    // ones ((-1, -1) past the used slots; piece 0 entries are skipped).
-    int extra_pass;
+    // The dK/dV launch has part_slots + (key tiles) workgroups: the first run
+    // extra[w] = (key tile, piece >= 1) of the split key tiles ((-1, -1) past
+    // the used slots; piece-0 entries are skipped), the rest piece 0 of every
+    // key tile.
     int2* plan;
     int2* extra;
     float* part;
