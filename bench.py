@@ -47,13 +47,19 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz, dense
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_softmax_attn_amd", "csrc", "fwd_bf16.hip")
+# the forward kernel's source and the headers it includes: the recorded counters stay valid
+# only while none of them changes
+KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_softmax_attn_amd", "csrc", f)
+                  for f in ("fwd_bf16.hip", "fwd_common.h", "gfx950_util.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_{workload}_traffic.json")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def allowed_pairs_dense(cfg) -> int:

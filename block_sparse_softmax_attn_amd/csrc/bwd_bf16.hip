@@ -52,6 +52,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // workgroup while the rest of the GPU idles).
 constexpr int kPieceTiles = 32;
 constexpr int kMaxPieces = 8;
+constexpr int64_t kMaxSlots = 1 << 18;   // partial slots a call uses at most
 
 __host__ __device__ inline int pieces_of(int ntiles) {
     if (ntiles <= kPieceTiles) return 1;
@@ -80,18 +81,75 @@ __device__ inline int sparse_key_tiles(const BwdArgs& a, int64_t kvbh, int kt, i
     return n;
 }
 
+// The split plan, by one workgroup of 256 threads: for every (key/value head,
+// key tile) in order, its number of pieces and the first of its partial slots
+// (an exclusive scan over the split items; unsplit items get slot -1), then the
+// extra-piece list. It runs as one more workgroup of the row-statistics launch,
+// beside the statistics, so it costs no launch of its own.
+__device__ void split_plan(const BwdArgs& a, int nkt, int64_t items) {
+    __shared__ int warp_tot[4];
+    __shared__ int carry;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nqb_meta = (a.N + a.block - 1) / a.block, subs = a.block / BT;
+    if (tid == 0) carry = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < items; base += 256) {
+        const int64_t it = base + tid;
+        int np = 0;
+        if (it < items) np = pieces_of(sparse_key_tiles(a, it / nkt, (int)(it % nkt), nqb_meta, subs));
+        const int need = np > 1 ? np : 0;
+        // inclusive scan inside the wave, then across the 4 waves
+        int x = need;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) warp_tot[w] = x;
+        __syncthreads();
+        int before = carry;
+        for (int i = 0; i < w; ++i) before += warp_tot[i];
+        if (it < items) a.plan[it] = make_int2(need ? before + x - need : -1, max(np, 1));
+        __syncthreads();
+        if (tid == 255) carry = before + x;
+        __syncthreads();
+    }
+    const int used = carry;
+    __syncthreads();
+    if (used > a.part_slots) {   // the workspace holds fewer slots: no key tile is split
+        for (int64_t it = tid; it < items; it += 256) a.plan[it] = make_int2(-1, 1);
+        for (int64_t w2 = tid; w2 < a.part_slots; w2 += 256) a.extra[w2] = make_int2(-1, -1);
+        return;
+    }
+    // the extra-piece list, indexed by slot: slot base + p holds (item, p)
+    for (int64_t w2 = used + tid; w2 < a.part_slots; w2 += 256) a.extra[w2] = make_int2(-1, -1);
+    for (int64_t it = tid; it < items; it += 256) {
+        const int2 pl = a.plan[it];
+        for (int p = 0; p < pl.y && pl.x >= 0; ++p) a.extra[pl.x + p] = make_int2((int)it, p);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // row statistics: one workgroup per 64-row block (plus one padding block)
 // ---------------------------------------------------------------------------
 
 // stats[bh][blk][0..63]   = LSE_i * log2 e  (+inf: row without keys, or i >= N)
 // stats[bh][blk][64..127] = D_i = dO_i . O_i (0 for i >= N)
-template <int D>
-__global__ __launch_bounds__(256) void bwd_stats_kernel(const __bf16* __restrict__ o, const __bf16* __restrict__ dout,
-                                                        const float* __restrict__ lse, float* __restrict__ stats,
-                                                        int N, int nblk) {
+// PLAN: column nblk + 1 of the grid holds the split-plan workgroup (row 0) and
+// nothing else.
+template <int D, bool PLAN>
+__global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a, int nblk, int nkt, int64_t items) {
     const int blk = blockIdx.x;
     const int64_t bh = blockIdx.y;
+    if (PLAN && blk == nblk + 1) {
+        if (bh == 0) split_plan(a, nkt, items);
+        return;
+    }
+    const __bf16* __restrict__ o = static_cast<const __bf16*>(a.o);
+    const __bf16* __restrict__ dout = static_cast<const __bf16*>(a.dout);
+    const float* __restrict__ lse = a.lse;
+    float* __restrict__ stats = a.stats;
+    const int N = a.N;
     const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
     const int i = blk * BT + r;
     float acc = 0.f;
@@ -776,91 +834,58 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
 // block-sparse dK/dV split: plan and ordered reduction
 // ---------------------------------------------------------------------------
 
-// One workgroup: for every (key/value head, key tile) in order, its number of
-// pieces and the first of its partial slots (an exclusive scan over the split
-// items; unsplit items get slot -1).
-template <int BKV>
-__global__ __launch_bounds__(256) void bwd_plan_kernel(BwdArgs a, int nkt, int64_t items) {
-    __shared__ int warp_tot[4];
-    __shared__ int carry;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int nqb_meta = (a.N + a.block - 1) / a.block, subs = a.block / BT;
-    if (tid == 0) carry = 0;
-    __syncthreads();
-    for (int64_t base = 0; base < items; base += 256) {
-        const int64_t it = base + tid;
-        int np = 0;
-        if (it < items) np = pieces_of(sparse_key_tiles(a, it / nkt, (int)(it % nkt), nqb_meta, subs));
-        const int need = np > 1 ? np : 0;
-        // inclusive scan inside the wave, then across the 4 waves
-        int x = need;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(x, off);
-            if (lane >= off) x += y;
-        }
-        if (lane == 63) warp_tot[w] = x;
-        __syncthreads();
-        int before = carry;
-        for (int i = 0; i < w; ++i) before += warp_tot[i];
-        if (it < items) a.plan[it] = make_int2(need ? before + x - need : -1, max(np, 1));
-        __syncthreads();
-        if (tid == 255) carry = before + x;
-        __syncthreads();
-    }
-    const int used = carry;
-    __syncthreads();
-    if (used > a.part_slots) {   // the workspace holds fewer slots: no key tile is split
-        for (int64_t it = tid; it < items; it += 256) a.plan[it] = make_int2(-1, 1);
-        for (int64_t w2 = tid; w2 < a.part_slots; w2 += 256) a.extra[w2] = make_int2(-1, -1);
-        return;
-    }
-    // the extra-piece list, indexed by slot: slot base + p holds (item, p)
-    for (int64_t w2 = used + tid; w2 < a.part_slots; w2 += 256) a.extra[w2] = make_int2(-1, -1);
-    for (int64_t it = tid; it < items; it += 256) {
-        const int2 pl = a.plan[it];
-        for (int p = 0; p < pl.y && pl.x >= 0; ++p) a.extra[pl.x + p] = make_int2((int)it, p);
-    }
-}
+// The ordered reduction of split key tiles. A split key tile's partials sit in
+// consecutive slots from its first; each of its RCH workgroups owns one chunk of
+// the [dK | dV] block and adds the pieces' values in piece order (all loads
+// issued first), so the result does not depend on scheduling. Workgroups are
+// indexed by (slot, chunk); only a split tile's first slot (piece 0 in the
+// extra list) does work.
+template <int D, int BKV>
+struct ReduceGeo {
+    static constexpr int TILE = 2 * BKV * D;           // floats per slot: dK, then dV
+    static constexpr int F = 2;                        // float4 per thread and piece
+    static constexpr int RCH = TILE / (256 * 4 * F);   // workgroups per key tile
+    static_assert(RCH * 256 * 4 * F == TILE, "chunking must cover the slot");
+};
 
-// One workgroup per (key/value head, key tile): dK = scale * sum of the pieces'
-// partials, dV = sum, in piece order (deterministic), for split key tiles.
-// Each thread owns E float4 of dK and of dV and adds the pieces one after the
-// other, so each piece is E independent loads in flight per thread.
 template <int D, int BKV>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int nkt) {
-    constexpr int E = BKV * D / (256 * 4);
-    const int64_t item = blockIdx.x;
-    const int2 pl = plan_at(a, item);
-    if (pl.y <= 1) return;
+    using G = ReduceGeo<D, BKV>;
+    const int64_t w = blockIdx.x / G::RCH;
+    const int ch = blockIdx.x % G::RCH;
+    const int32_t* ex = reinterpret_cast<const int32_t*>(a.extra);
+    const int item0 = ld_meta(ex, 2 * w);
+    if (item0 < 0 || ld_meta(ex, 2 * w + 1) != 0) return;
+    const int64_t item = item0;
+    const int np = plan_at(a, item).y;   // its first slot is w
     const int64_t kvbh = item / nkt;
     const int kb0 = (int)(item % nkt) * BKV;
-    const float* base = a.part + (int64_t)pl.x * (2 * BKV * D);
-    float4 sk[E], sv[E];
+    const float* base = a.part + w * G::TILE;
+    float4 x[kMaxPieces][G::F];
 #pragma unroll
-    for (int i = 0; i < E; ++i) sk[i] = sv[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p = 0; p < pl.y; ++p) {
-        const float* pk = base + (int64_t)p * (2 * BKV * D);
+    for (int p = 0; p < kMaxPieces; ++p)
 #pragma unroll
-        for (int i = 0; i < E; ++i) {
-            const int e = (threadIdx.x + 256 * i) * 4;
-            const float4 xk = *reinterpret_cast<const float4*>(pk + e);
-            const float4 xv = *reinterpret_cast<const float4*>(pk + BKV * D + e);
-            sk[i].x += xk.x; sk[i].y += xk.y; sk[i].z += xk.z; sk[i].w += xk.w;
-            sv[i].x += xv.x; sv[i].y += xv.y; sv[i].z += xv.z; sv[i].w += xv.w;
+        for (int i = 0; i < G::F; ++i) {
+            const int e = ((ch * G::F + i) * 256 + threadIdx.x) * 4;
+            x[p][i] = p < np ? *reinterpret_cast<const float4*>(base + (int64_t)p * G::TILE + e)
+                             : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-    }
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-        const int e = (threadIdx.x + 256 * i) * 4;
-        const int key = e / D, c = e % D;
+    for (int i = 0; i < G::F; ++i) {
+        float4 sum = x[0][i];
+#pragma unroll
+        for (int p = 1; p < kMaxPieces; ++p) {
+            sum.x += x[p][i].x; sum.y += x[p][i].y; sum.z += x[p][i].z; sum.w += x[p][i].w;
+        }
+        const int e = ((ch * G::F + i) * 256 + threadIdx.x) * 4;
+        const bool is_k = e < BKV * D;
+        const int r = is_k ? e : e - BKV * D;
+        const int key = r / D, c = r % D;
         if (kb0 + key >= a.N) continue;
-        const int64_t row = (kvbh * a.N + kb0 + key) * (int64_t)D + c;
-        const bf16x4 ok = {(__bf16)(sk[i].x * a.scale), (__bf16)(sk[i].y * a.scale), (__bf16)(sk[i].z * a.scale),
-                           (__bf16)(sk[i].w * a.scale)};
-        const bf16x4 ov = {(__bf16)sv[i].x, (__bf16)sv[i].y, (__bf16)sv[i].z, (__bf16)sv[i].w};
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dk) + row) = ok;
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.dv) + row) = ov;
+        const float m = is_k ? a.scale : 1.f;
+        const bf16x4 out = {(__bf16)(sum.x * m), (__bf16)(sum.y * m), (__bf16)(sum.z * m), (__bf16)(sum.w * m)};
+        __bf16* dst = static_cast<__bf16*>(is_k ? a.dk : a.dv);
+        *reinterpret_cast<bf16x4*>(dst + (kvbh * a.N + kb0 + key) * (int64_t)D + c) = out;
     }
 }
 
@@ -885,11 +910,27 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D, int BKV>
+hipError_t launch_reduce(const BwdArgs& a, int nkt, hipStream_t stream) {
+    if (a.part_slots == 0) return hipSuccess;
+    hipLaunchKernelGGL((bwd_reduce_kernel<D, BKV>), dim3((unsigned)(a.part_slots * ReduceGeo<D, BKV>::RCH)), dim3(256),
+                       0, stream, a, nkt);
+    return hipGetLastError();
+}
+
 template <int D>
 hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
     const int nblk = a.npad / BT;
-    hipLaunchKernelGGL(bwd_stats_kernel<D>, dim3((unsigned)(nblk + 1), (unsigned)a.BH), dim3(256), 0, stream,
-                       static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dout), a.lse, a.stats, a.N, nblk);
+    // block-sparse: the split plan rides in the statistics launch (one more
+    // grid column whose row 0 computes it)
+    const int nkt_sparse = mode == Mode::kSparse ? (a.N + a.block - 1) / a.block : 0;
+    const int64_t items = (int64_t)nkt_sparse * (a.BH / (a.H / a.Hkv));
+    if (mode == Mode::kSparse)
+        hipLaunchKernelGGL((bwd_stats_kernel<D, true>), dim3((unsigned)(nblk + 2), (unsigned)a.BH), dim3(256), 0,
+                           stream, a, nblk, nkt_sparse, items);
+    else
+        hipLaunchKernelGGL((bwd_stats_kernel<D, false>), dim3((unsigned)(nblk + 1), (unsigned)a.BH), dim3(256), 0,
+                           stream, a, nblk, 0, (int64_t)0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // dK/dV: 128 keys per workgroup (one key block of a sparse pattern; 64 for
@@ -904,27 +945,15 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
             e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kCausal>(a, stream);
             return e != hipSuccess ? e : launch_dq<D, 8, 3, (int)Mode::kCausal>(a, stream);
         case Mode::kSparse: {
-            // split plan, dK/dV (pieces of long key-tile lists write partials),
-            // the ordered reduction of split key tiles, dQ
-            const int nkt = (a.N + a.block - 1) / a.block;
-            const int64_t items = (int64_t)nkt * (a.BH / (a.H / a.Hkv));
+            // dK/dV (pieces of long key-tile lists write partials), the ordered
+            // reduction of split key tiles, dQ
             if (a.block == 128) {
-                hipLaunchKernelGGL(bwd_plan_kernel<128>, dim3(1), dim3(256), 0, stream, a, nkt, items);
-                e = hipGetLastError();
-                if (e == hipSuccess) e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kSparse>(a, stream);
-                if (e == hipSuccess) {
-                    hipLaunchKernelGGL((bwd_reduce_kernel<D, 128>), dim3((unsigned)items), dim3(256), 0, stream, a, nkt);
-                    e = hipGetLastError();
-                }
+                e = launch_dkdv<D, D == 64 ? 4 : 8, (int)Mode::kSparse>(a, stream);
+                if (e == hipSuccess) e = launch_reduce<D, 128>(a, nkt_sparse, stream);
                 return e != hipSuccess ? e : launch_dq<D, 4, 2, (int)Mode::kSparse>(a, stream);
             }
-            hipLaunchKernelGGL(bwd_plan_kernel<64>, dim3(1), dim3(256), 0, stream, a, nkt, items);
-            e = hipGetLastError();
-            if (e == hipSuccess) e = launch_dkdv<D, D == 64 ? 2 : 4, (int)Mode::kSparse>(a, stream);
-            if (e == hipSuccess) {
-                hipLaunchKernelGGL((bwd_reduce_kernel<D, 64>), dim3((unsigned)items), dim3(256), 0, stream, a, nkt);
-                e = hipGetLastError();
-            }
+            e = launch_dkdv<D, D == 64 ? 2 : 4, (int)Mode::kSparse>(a, stream);
+            if (e == hipSuccess) e = launch_reduce<D, 64>(a, nkt_sparse, stream);
             return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse>(a, stream);
         }
         case Mode::kRange: break;   // no backward for key-range launches
@@ -974,7 +1003,7 @@ int64_t bwd_sparse_slots(const int32_t* t_row_ptr, int64_t B, int64_t H, int64_t
             if (np > 1) slots += np;
         }
     }
-    return slots;
+    return slots > kMaxSlots ? 0 : slots;   // beyond the cap the call splits nothing
 }
 
 void bwd_sparse_workspace_carve(BwdArgs& a, void* ws, int64_t ws_bytes) {
@@ -984,11 +1013,12 @@ void bwd_sparse_workspace_carve(BwdArgs& a, void* ws, int64_t ws_bytes) {
     a.plan = reinterpret_cast<int2*>(p + align256(bwd_workspace_bytes(a.BH, a.N)));
     const int64_t base = bwd_sparse_workspace_base(a.BH, BHkv, a.N, a.block);
     const int64_t per_slot = bwd_sparse_slot_bytes(a.block, a.d) + (int64_t)sizeof(int2);
-    // no more slots than key tiles times pieces, and a launch grid (slots plus
-    // key tiles) that fits 32 bits
+    // no more slots than key tiles times pieces, and at most kMaxSlots, so the
+    // dK/dV grid (slots plus key tiles) and the reduction grid (slots times its
+    // chunks) stay far inside 32-bit work-item counts
     const int64_t items = (a.N + a.block - 1) / a.block * BHkv;
     a.part_slots = std::max<int64_t>(0, ws_bytes - base - 256) / per_slot;
-    a.part_slots = std::min<int64_t>({a.part_slots, items * kMaxPieces, (int64_t)INT32_MAX - items});
+    a.part_slots = std::min<int64_t>({a.part_slots, items * kMaxPieces, kMaxSlots});
     a.extra = reinterpret_cast<int2*>(p + base);
     a.part = reinterpret_cast<float*>(p + base + align256(a.part_slots * (int64_t)sizeof(int2)));
 }

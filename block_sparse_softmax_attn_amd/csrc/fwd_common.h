@@ -133,8 +133,10 @@ int64_t bwd_workspace_bytes(int64_t BH, int64_t N);
 // alignment once).
 int64_t bwd_sparse_workspace_base(int64_t BH, int64_t BHkv, int64_t N, int64_t block);
 int64_t bwd_sparse_slot_bytes(int64_t block, int64_t d);
+
 // Partial slots the split plan uses for host transposed offsets t_row_ptr
-// ([meta_heads * ceil(N / block) + 1]).
+// ([meta_heads * ceil(N / block) + 1]); 0 when they would exceed the cap of
+// 2^18 slots a call uses (the call then splits nothing).
 int64_t bwd_sparse_slots(const int32_t* t_row_ptr, int64_t B, int64_t H, int64_t Hkv, int64_t N, int64_t block,
                          int64_t meta_heads);
 // Point the BwdArgs at their workspace pieces (a.BH, a.N set; for the sparse

@@ -250,7 +250,9 @@ int attn_blockmask_transpose(const int32_t* row_ptr, const int32_t* col, int64_t
  *               metadata ([meta_heads * ceil(N / block) + 1]), or NULL: then
  *               the minimum workspace (no list is split).  A workspace between
  *               the minimum and the returned size is accepted; the split is
- *               then turned off for the whole call.
+ *               then turned off for the whole call.  A call uses at most 2^18
+ *               partial slots; metadata that would need more gets the minimum
+ *               (no split).
  *   Returns -1 for sizes, dtype, block or meta_heads the backward does not accept.
  *
  * attn_bwd_blocksparse - gradients of attn_fwd_blocksparse.

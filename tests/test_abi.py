@@ -226,6 +226,15 @@ def test_bwd_blocksparse_workspace_bytes_counts_split_slots(m):
     t2 = np.ascontiguousarray(m.blockmask_build(rp2, col2, 1, N, block, False).transposed()[0], dtype=np.int32)
     assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, block, t2.ctypes.data_as(ctypes.c_void_p),
                                                     1) == base
+    # a call uses at most 2^18 slots: 64-key blocks that each see 33 query tiles split in 2 pieces;
+    # 2^17 of them fill the cap exactly, one more block of them needs more and gets no split at all
+    for nkt, slots in ((1 << 17, 1 << 18), ((1 << 17) + 1, 0)):
+        t_big = np.arange(0, 33 * nkt + 1, 33, dtype=np.int32)
+        n_big = 64 * nkt
+        least = lib.attn_bwd_blocksparse_workspace_bytes(1, 1, 1, n_big, 64, 1, 64, None, 1)
+        full = lib.attn_bwd_blocksparse_workspace_bytes(1, 1, 1, n_big, 64, 1, 64,
+                                                        t_big.ctypes.data_as(ctypes.c_void_p), 1)
+        assert full == (least + 256 + slots * (2 * 64 * 64 * 4 + 8) if slots else least)
     # rejected: fp32, block size, meta_heads
     assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 0, block, None, 1) == -1
     assert lib.attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, 32, None, 1) == -1
