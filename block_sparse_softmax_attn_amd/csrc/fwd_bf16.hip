@@ -87,6 +87,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::V_BYTES], sV1[G::V_BYTES], sV2[VB2], sV3[VB3];
     unsigned char* const kbuf[4] = {sK0, sK1, sK2, sK3};
     unsigned char* const vbuf[4] = {sV0, sV1, sV2, sV3};
+    const unsigned kl[4] = {lds_addr(sK0), lds_addr(sK1), lds_addr(sK2), lds_addr(sK3)};
+    const unsigned vl[4] = {lds_addr(sV0), lds_addr(sV1), lds_addr(sV2), lds_addr(sV3)};
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -220,20 +222,47 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             v_off[i] = d * a.npad + v_swz(d, p) * 8;
         }
     }
-    auto issue_tile = [&](int kb0, unsigned char* dK, unsigned char* dV) {
+    // Row-major K and V tiles: byte offsets inside the tile, fixed for the
+    // whole loop, from a tile base that moves in scalar registers.  A tile
+    // that reaches past the last key clamps its rows to that key instead.
+    unsigned k_boff[G::K_PER_W], v_boff[VTR ? G::V_PER_W : 1];
 #pragma unroll
-        for (int i = 0; i < G::K_PER_W; ++i) {
-            const int key = min(kb0 + k_row[i], NK - 1);
-            dma16(Kh + (int64_t)key * D + k_col[i], dK + (w * G::K_PER_W + i) * 1024);
-        }
+    for (int i = 0; i < G::K_PER_W; ++i) k_boff[i] = (unsigned)(2 * (k_row[i] * D + k_col[i]));
 #pragma unroll
-        for (int i = 0; i < G::V_PER_W; ++i) {
+    for (int i = 0; i < (VTR ? G::V_PER_W : 0); ++i) v_boff[i] = (unsigned)(2 * (v_row[i] * D + v_off[i]));
+    const unsigned wk = __builtin_amdgcn_readfirstlane(w * G::K_PER_W * 1024);   // this wave's part of a tile
+    const unsigned wv = __builtin_amdgcn_readfirstlane(w * G::V_PER_W * 1024);
+    auto issue_tile = [&](int kb0, int u) {
+        if (kb0 + BN <= NK) {
+            const __bf16* kt = Kh + (int64_t)kb0 * D;
+#pragma unroll
+            for (int i = 0; i < G::K_PER_W; ++i) dma16_at(kt, k_boff[i], kl[u] + wk + i * 1024);
             if constexpr (VTR) {
-                const int key = min(kb0 + v_row[i], NK - 1);
-                dma16(Vh + (int64_t)key * D + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
-            } else {
-                dma16(Vth + (int64_t)kb0 + v_off[i], dV + (w * G::V_PER_W + i) * 1024);
+                const __bf16* vt = Vh + (int64_t)kb0 * D;
+#pragma unroll
+                for (int i = 0; i < G::V_PER_W; ++i) dma16_at(vt, v_boff[i], vl[u] + wv + i * 1024);
             }
+        } else {
+            const int rb = min(kb0, NK - 1);   // rows clamped to NK - 1 stay at or after rb
+            const __bf16* kt = Kh + (int64_t)rb * D;
+#pragma unroll
+            for (int i = 0; i < G::K_PER_W; ++i) {
+                const int key = min(kb0 + k_row[i], NK - 1);
+                dma16_at(kt, (unsigned)(2 * ((key - rb) * D + k_col[i])), kl[u] + wk + i * 1024);
+            }
+            if constexpr (VTR) {
+                const __bf16* vt = Vh + (int64_t)rb * D;
+#pragma unroll
+                for (int i = 0; i < G::V_PER_W; ++i) {
+                    const int key = min(kb0 + v_row[i], NK - 1);
+                    dma16_at(vt, (unsigned)(2 * ((key - rb) * D + v_off[i])), vl[u] + wv + i * 1024);
+                }
+            }
+        }
+        if constexpr (!VTR) {
+#pragma unroll
+            for (int i = 0; i < G::V_PER_W; ++i)
+                dma16(Vth + (int64_t)kb0 + v_off[i], vbuf[u] + (w * G::V_PER_W + i) * 1024);
         }
     };
     f32x16 oacc[D / 32];
@@ -250,7 +279,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         // 0 below (at most the later tiles' loads outstanding) also covers Q.
 #pragma unroll
         for (int s = 0; s < NS - 1; ++s)
-            if (s < ntiles) issue_tile(describe(s).kb0, kbuf[s], vbuf[s]);
+            if (s < ntiles) issue_tile(describe(s).kb0, s);
 
         // One tile's math for this wave: scores, masks, online softmax, PV.
         auto compute = [&](const TileDesc& t, const unsigned char* bK, const unsigned char* bV) {
@@ -334,7 +363,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             else wait_vmcnt<0>();
             barrier();
             const int un = (u + NS - 1) % NS;
-            if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, kbuf[un], vbuf[un]);
+            if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, un);
             const TileDesc t = describe(it);
             // a wave whose rows all precede the tile skips its math
             if (!(t.causal && t.kb0 > wdiag)) compute(t, kbuf[u], vbuf[u]);

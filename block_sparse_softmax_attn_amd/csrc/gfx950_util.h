@@ -28,6 +28,20 @@ static __device__ __forceinline__ void dma16(const void* gsrc, void* lds) {
 #endif
 }
 
+// The same load from a uniform base address (an SGPR pair) plus this lane's
+// 32-bit byte offset, into the uniform LDS byte address lds: a tile whose
+// base moves in scalar registers needs no per-lane address arithmetic.
+static __device__ __forceinline__ void dma16_at(const void* sbase, unsigned voff, unsigned lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
+#endif
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+static __device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
 // s_waitcnt vmcnt(n) leaving the other counters alone (gfx9 encoding).
 template <int n>
 static __device__ __forceinline__ void wait_vmcnt() {
