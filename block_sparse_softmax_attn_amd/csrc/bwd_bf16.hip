@@ -336,22 +336,41 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         rm_row[i] = r;
         rm_col[i] = rt_swz<D>(r, p) * 8;
     }
+    // Loads from a tile base that moves in scalar registers plus fixed
+    // per-lane byte offsets; a tile that reaches past row N - 1 clamps its
+    // rows to it instead.
+    unsigned rm_boff[G::PER_T];
+#pragma unroll
+    for (int i = 0; i < G::PER_T; ++i) rm_boff[i] = (unsigned)(2 * (rm_row[i] * D + rm_col[i]));
+    const unsigned lq[2] = {lds_addr(sQ0), lds_addr(sQ1)}, lo[2] = {lds_addr(sO0), lds_addr(sO1)};
+    const unsigned ls[2] = {lds_addr(sS0), lds_addr(sS1)};
+    const unsigned wl = __builtin_amdgcn_readfirstlane(w * G::PER_T * 1024);   // this wave's part of a tile
     auto issue = [&](const QTile& t, int u) {
-        unsigned char* dQ = u ? sQ1 : sQ0;
-        unsigned char* dO = u ? sO1 : sO0;
         const int q0 = max(t.q0, 0);
         const __bf16* Qh = static_cast<const __bf16*>(a.q) + t.bhq * (int64_t)N * D;
         const __bf16* dOh = static_cast<const __bf16*>(a.dout) + t.bhq * (int64_t)N * D;
         const float* Sh = a.stats + t.bhq * (int64_t)(nblk + 1) * 128;
+        if (q0 + BT <= N) {
+            const __bf16* qt = Qh + (int64_t)q0 * D;
+            const __bf16* ot = dOh + (int64_t)q0 * D;
 #pragma unroll
-        for (int i = 0; i < G::PER_T; ++i) {
-            const int row = min(q0 + rm_row[i], N - 1);
-            const int off = (w * G::PER_T + i) * 1024;
-            dma16(Qh + (int64_t)row * D + rm_col[i], dQ + off);
-            dma16(dOh + (int64_t)row * D + rm_col[i], dO + off);
+            for (int i = 0; i < G::PER_T; ++i) {
+                dma16_at(qt, rm_boff[i], lq[u] + wl + i * 1024);
+                dma16_at(ot, rm_boff[i], lo[u] + wl + i * 1024);
+            }
+        } else {
+            const int rb = min(q0, N - 1);   // clamped rows stay at or after rb
+            const __bf16* qt = Qh + (int64_t)rb * D;
+            const __bf16* ot = dOh + (int64_t)rb * D;
+#pragma unroll
+            for (int i = 0; i < G::PER_T; ++i) {
+                const unsigned off = (unsigned)(2 * ((min(q0 + rm_row[i], N - 1) - rb) * D + rm_col[i]));
+                dma16_at(qt, off, lq[u] + wl + i * 1024);
+                dma16_at(ot, off, lo[u] + wl + i * 1024);
+            }
         }
         // row statistics of this block (lanes 0-31) and of the next (32-63)
-        if (w == 0) dma16(Sh + (q0 / BT) * 128 + lane * 4, u ? sS1 : sS0);
+        if (w == 0) dma16_at(Sh + (q0 / BT) * 128, (unsigned)(lane * 16), ls[u]);
     };
 
     // ---- operands, accumulators and one tile's math for each design ----
@@ -723,13 +742,32 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
         k_row[i] = r;
         k_col[i] = rt_swz<D>(r, p) * 8;
     }
-    auto issue = [&](int kb0, int u) {
+    // scalar tile base plus fixed per-lane offsets, as in the dK/dV kernel
+    unsigned k_boff[G::PER_T];
 #pragma unroll
-        for (int i = 0; i < G::PER_T; ++i) {
-            const int key = min(kb0 + k_row[i], N - 1);
-            const int off = (w * G::PER_T + i) * 1024;
-            dma16(Kh + (int64_t)key * D + k_col[i], kbuf[u] + off);
-            dma16(Vh + (int64_t)key * D + k_col[i], vbuf[u] + off);
+    for (int i = 0; i < G::PER_T; ++i) k_boff[i] = (unsigned)(2 * (k_row[i] * D + k_col[i]));
+    const unsigned kl[3] = {lds_addr(sK0), lds_addr(sK1), lds_addr(sK2)};
+    const unsigned vl[3] = {lds_addr(sV0), lds_addr(sV1), lds_addr(sV2)};
+    const unsigned wl = __builtin_amdgcn_readfirstlane(w * G::PER_T * 1024);
+    auto issue = [&](int kb0, int u) {
+        if (kb0 + BT <= N) {
+            const __bf16* kt = Kh + (int64_t)kb0 * D;
+            const __bf16* vt = Vh + (int64_t)kb0 * D;
+#pragma unroll
+            for (int i = 0; i < G::PER_T; ++i) {
+                dma16_at(kt, k_boff[i], kl[u] + wl + i * 1024);
+                dma16_at(vt, k_boff[i], vl[u] + wl + i * 1024);
+            }
+        } else {
+            const int rb = min(kb0, N - 1);   // clamped rows stay at or after rb
+            const __bf16* kt = Kh + (int64_t)rb * D;
+            const __bf16* vt = Vh + (int64_t)rb * D;
+#pragma unroll
+            for (int i = 0; i < G::PER_T; ++i) {
+                const unsigned off = (unsigned)(2 * ((min(kb0 + k_row[i], N - 1) - rb) * D + k_col[i]));
+                dma16_at(kt, off, kl[u] + wl + i * 1024);
+                dma16_at(vt, off, vl[u] + wl + i * 1024);
+            }
         }
     };
 
