@@ -438,7 +438,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             for (int qc = 0; qc < 2; ++qc) {
                 if (!live[qc]) continue;
                 const int qb0 = q0 + 32 * qc;
-                const bool cmask = causal && qb0 < kw0 + 31;
+                // causal: scores of keys after their query become -inf (P = 0)
+                // in a block of their own, so unmasked tiles pay nothing for it
+                if (causal && qb0 < kw0 + 31) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (kj > qb0 + 8 * (v >> 2) + 4 * hi + (v & 3)) pr[qc][v] = -__builtin_inff();
+                }
 #pragma unroll
                 for (int g4 = 0; g4 < 4; ++g4) {
                     const float4 l4 = *reinterpret_cast<const float4*>(st + 32 * qc + 8 * g4 + 4 * hi);
@@ -446,8 +452,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int v = 4 * g4 + e;
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pr[qc][v], sl2, -lv[e]));
-                        if (cmask && kj > qb0 + 8 * g4 + 4 * hi + e) p = 0.f;
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(pr[qc][v], sl2, -lv[e]));
                         pb[qc][v >> 3][v & 7] = (__bf16)p;
                     }
                 }
@@ -507,7 +512,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         for (int qc = 0; qc < BT / 32; ++qc) {
             const int qb0 = q0 + 32 * qc;
             if (causal && qb0 + 31 < kw0) continue;   // all 32 queries precede all keys of this wave
-            const bool cmask = causal && qb0 < kw0 + 31;
             // ---- S = Q K^T and dP = dO V^T, queries as rows: lane (l32, hi)
             // gets query qb0 + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
             bf16x8 fa[D / 16], fb[D / 16];
@@ -533,6 +537,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
                     ta[t][db] = tr_operand<D>(bO, trl, 2 * qc + t, db);
                     tb[t][db] = tr_operand<D>(bQ, trl, 2 * qc + t, db);
                 }
+            // causal: scores of keys after their query become -inf (P = 0), in
+            // a block of their own
+            if (causal && qb0 < kw0 + 31) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (kj > qb0 + 8 * (v >> 2) + 4 * hi + (v & 3)) s[v] = -__builtin_inff();
+            }
             // ---- P = exp2(s * scale log2 e - lse2) and dS = P (dP - D), bf16 ----
             bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -544,8 +555,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g4 + e;
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lv[e]));
-                    if (cmask && kj > qb0 + 8 * g4 + 4 * hi + e) p = 0.f;
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lv[e]));
                     const __bf16 pr = (__bf16)p;
                     pb[v >> 3][v & 7] = pr;
                     dsb[v >> 3][v & 7] = (__bf16)((float)pr * (dp[v] - dv[e]));
@@ -813,14 +823,19 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr, qf[k], s, 0, 0, 0);
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr, dof[k], dp, 0, 0, 0);
                 }
+                // masked scores become -inf (P = 0) in a block of their own, so
+                // unmasked tiles pay nothing for it
+                if (t.masked) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
+                        if (j >= t.nlim || (t.causal && j > qi)) s[v] = -__builtin_inff();
+                    }
+                }
                 bf16x8 dsb[2];
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lse2));
-                    if (t.masked) {
-                        const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
-                        if (j >= t.nlim || (t.causal && j > qi)) p = 0.f;
-                    }
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lse2));
                     dsb[v >> 3][v & 7] = (__bf16)(p * (dp[v] - dval));
                 }
                 // ---- dQ^T += K^T dS^T over this block's two 16-key steps ----
