@@ -204,7 +204,12 @@ struct DkdvGeo {
 template <int D, int NW, int MODE, bool PAIRED>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     using G = DkdvGeo<D, NW, PAIRED>;
-    __shared__ __attribute__((aligned(1024))) unsigned char sQ0[G::TB], sQ1[G::TB], sO0[G::TB], sO1[G::TB];
+    // Q tiles of the two stages, then dO tiles: sQO + u TB (Q), sQO + (2 + u) TB (dO)
+    __shared__ __attribute__((aligned(1024))) unsigned char sQO[4 * G::TB];
+    unsigned char* const sQ0 = sQO;
+    unsigned char* const sQ1 = sQO + G::TB;
+    unsigned char* const sO0 = sQO + 2 * G::TB;
+    unsigned char* const sO1 = sQO + 3 * G::TB;
     __shared__ __attribute__((aligned(1024))) float sS0[256], sS1[256];
     __shared__ __attribute__((aligned(16))) bf16x8 sP[PAIRED ? G::PAIRS : 1][2][2][64];   // [pair][block][step][lane]
 
@@ -409,9 +414,20 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // Barrier.  Phase 2: dV (P wave, P still in registers) or dS and dK (dS
     // wave).  Every wave reaches the barrier, also when the causal mask leaves
     // it nothing to do.
+    // Paired: the wave's phase-1 operand (Q for the P wave, dO for the dS wave)
+    // and phase-2 operand (dO^T, Q^T) are at a role-dependent distance from
+    // the stage's Q tile; folded into the lane offsets once, every read is a
+    // register plus an immediate.
+    int a_off[D / 16];
+    TrLane<D> t_off = trl;
+#pragma unroll
+    for (int k = 0; k < D / 16; ++k) a_off[k] = rtl.off[k] + (role == 0 ? 0 : 2 * G::TB);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) t_off.off[h][db] += role == 0 ? 2 * G::TB : 0;
     auto compute_paired = [&](int q0, int u) {
         const unsigned char* bQ = u ? sQ1 : sQ0;
-        const unsigned char* bO = u ? sO1 : sO0;
         const float* st = u ? sS1 : sS0;
         bool live[2];
 #pragma unroll
@@ -420,7 +436,6 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // q0 + 32qc + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
         f32x16 pr[2];
         bf16x8 pb[2][2];
-        const unsigned char* bA = role == 0 ? bQ : bO;
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
             pr[qc] = f32x16{};
@@ -428,7 +443,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             bf16x8 fa[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k)
-                fa[k] = *reinterpret_cast<const bf16x8*>(bA + rtl.off[k] + 32 * qc * (2 * D));
+                fa[k] = *reinterpret_cast<const bf16x8*>(bQ + a_off[k] + 32 * qc * (2 * D));
             __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) pr[qc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k], kvf[k], pr[qc], 0, 0, 0);
@@ -485,12 +500,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
                 }
             }
             // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave) over two 16-query steps
-            const unsigned char* bT = role == 0 ? bO : bQ;
             bf16x8 ta[2][D / 32];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int db = 0; db < D / 32; ++db) ta[t][db] = tr_operand<D>(bT, trl, 2 * qc + t, db);
+                for (int db = 0; db < D / 32; ++db) ta[t][db] = tr_operand<D>(bQ, t_off, 2 * qc + t, db);
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
