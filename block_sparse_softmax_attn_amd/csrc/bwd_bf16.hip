@@ -840,11 +840,12 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
                 // masked scores become -inf (P = 0) in a block of their own, so
                 // unmasked tiles pay nothing for it
                 if (t.masked) {
+                    // key j masked when j >= nlim or, causal, j > qi: one bound
+                    const int lim = t.causal ? min(t.nlim - 1, qi) : t.nlim - 1;
+                    const int r = lim - t.kb0 - 32 * c - 4 * hi;
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
-                        if (j >= t.nlim || (t.causal && j > qi)) s[v] = -__builtin_inff();
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        if (8 * (v >> 2) + (v & 3) > r) s[v] = -__builtin_inff();
                 }
                 bf16x8 dsb[2];
 #pragma unroll

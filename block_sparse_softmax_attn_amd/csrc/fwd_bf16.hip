@@ -296,14 +296,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                 }
             }
             if (t.masked) {
+                // key j is masked when j >= nlim or, causal, j > qdiag: one bound
+                // lim; element (c, v) holds j = kb0 + 4hi + (32c + 8(v>>2) + (v&3)),
+                // so each element is one compare of a constant with r
+                const int lim = t.causal ? min(t.nlim - 1, qdiag) : t.nlim - 1;
+                const int r = lim - t.kb0 - 4 * hi;
 #pragma unroll
                 for (int c = 0; c < BN / 32; ++c)
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int j = t.kb0 + 32 * c + 8 * (v >> 2) + 4 * hi + (v & 3);
-                        const bool bad = (j >= t.nlim) || (t.causal && j > qdiag);
-                        s[c][v] = bad ? -__builtin_inff() : s[c][v];
-                    }
+                    for (int v = 0; v < 16; ++v)
+                        s[c][v] = 32 * c + 8 * (v >> 2) + (v & 3) > r ? -__builtin_inff() : s[c][v];
             }
             // ---- online softmax ----
             float mx = -__builtin_inff();
