@@ -1,6 +1,6 @@
 """Throughput of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense-h32-n8192-d128]
 
 A step is one pass of the hot path over one batch of synthetic N(0,1) bf16
 input already resident in HBM: one attn_fwd (dense, causal) or
@@ -45,6 +45,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402  (seeded input recipes: shapes, seeds, block lists)
 
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz, dense
 # the forward kernel's source and the headers it includes: the recorded counters stay valid
@@ -148,7 +150,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="dense-h32-n8192-d128",
+                    choices=[k for k in workloads.CONFIGS if workloads.CONFIGS[k].dtype == "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -157,7 +160,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU: --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
               "(the attention forward is measured on one MI355X; sharding is described in the design notes)",
               file=sys.stderr)
         sys.exit(2)
@@ -167,7 +170,6 @@ def main():
 
     import torch
     import block_sparse_softmax_attn_amd as attn
-    import workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -303,7 +305,6 @@ def bench_bwd(args, cfg, dev):
     computed once, untimed)."""
     import torch
     import block_sparse_softmax_attn_amd as attn
-    import workloads
 
     gen = torch.Generator(device=dev)
     gen.manual_seed(cfg.seed)

@@ -144,7 +144,7 @@ def test_builder_matches_oracle_random(m, causal):
 
 
 def test_builder_matches_oracle_on_sparse_workload(m):
-    cfg = workloads.CONFIGS["c4"]
+    cfg = workloads.CONFIGS["sparse-causal-h16-n16300-d128"]
     rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
     _check_builder(m, rows, 1, cfg.N, cfg.block, True)
     _check_builder(m, rows, 1, cfg.N, cfg.block, False)

@@ -205,14 +205,14 @@ def test_bwd_workspace_too_small_is_rejected(lib):
 # ---- full-size workloads, compared on one or two heads ----
 
 def test_bwd_causal_b4_h16_n2048_d64(lib):
-    cfg = workloads.CONFIGS["c2"]
-    print("case bwd c2", flush=True)
+    cfg = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
+    print("case bwd causal-b4-h16-n2048-d64", flush=True)
     _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, True, cfg.seed, heads=[(0, 0), (3, 15)])
 
 
 def test_bwd_dense_b1_h32_n8192_d128(lib):
-    cfg = workloads.CONFIGS["c3"]
-    print("case bwd c3", flush=True)
+    cfg = workloads.CONFIGS["dense-h32-n8192-d128"]
+    print("case bwd dense-h32-n8192-d128", flush=True)
     _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, False, cfg.seed, heads=[(0, 5)])
 
 
@@ -251,7 +251,7 @@ def test_bwd_sparse_long_key_lists_split_or_not(lib, split):
 
 
 def test_bwd_block_sparse_b1_h16_n16300_d128(lib):
-    cfg = workloads.CONFIGS["c4"]
-    print("case bwd c4", flush=True)
+    cfg = workloads.CONFIGS["sparse-causal-h16-n16300-d128"]
+    print("case bwd sparse-causal-h16-n16300-d128", flush=True)
     lists = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
     _sparse_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.block, True, lists, 1, cfg.seed, heads=[(0, 9)])

@@ -381,7 +381,7 @@ def test_allowed_pair_closed_forms(N, b):
 
 
 def test_local_global_random_pattern_properties():
-    cfg = workloads.CONFIGS["c4"]
+    cfg = workloads.CONFIGS["sparse-causal-h16-n16300-d128"]
     rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
     nqb = -(-cfg.N // cfg.block)
     assert len(rows) == nqb == 128

@@ -51,15 +51,15 @@ def test_dense_small(lib, shape, causal, dtype):
     _dense_case(lib, B, H, N, d, dtype, causal, seed=1000 + N + d + causal)
 
 
-def test_c1_full(lib):
-    cfg = workloads.CONFIGS["c1"]
-    print("case c1", flush=True)
+def test_dense_f32_h1_n256_d64_full(lib):
+    cfg = workloads.CONFIGS["dense-f32-h1-n256-d64"]
+    print("case dense-f32-h1-n256-d64", flush=True)
     _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.seed, cfg.scale)
 
 
-def test_c2_full(lib):
-    cfg = workloads.CONFIGS["c2"]
-    print("case c2", flush=True)
+def test_causal_b4_h16_n2048_d64_full(lib):
+    cfg = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
+    print("case causal-b4-h16-n2048-d64", flush=True)
     _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.seed, cfg.scale)
 
 
@@ -83,14 +83,14 @@ def _sampled_dense(lib, cfg, rows_per_head=None):
     print(f"{cfg.name}: max|dO| {worst[0]:.3e} max|dLSE| {worst[1]:.3e}", flush=True)
 
 
-def test_c3_sampled(lib):
-    print("case c3", flush=True)
-    _sampled_dense(lib, workloads.CONFIGS["c3"], rows_per_head=256)
+def test_dense_h32_n8192_d128_sampled(lib):
+    print("case dense-h32-n8192-d128", flush=True)
+    _sampled_dense(lib, workloads.CONFIGS["dense-h32-n8192-d128"], rows_per_head=256)
 
 
-def test_c5_sampled(lib):
-    print("case c5", flush=True)
-    _sampled_dense(lib, workloads.CONFIGS["c5"])
+def test_causal_h8_n131072_d128_sampled(lib):
+    print("case causal-h8-n131072-d128", flush=True)
+    _sampled_dense(lib, workloads.CONFIGS["causal-h8-n131072-d128"])
 
 
 # ---------------------------------------------------------------------------
@@ -133,10 +133,10 @@ def test_sparse_random_lists(lib, N, d, meta, block, causal, dtype):
     _sparse_case(lib, B, H, N, d, dtype, causal, block, rows, mh, seed=N + d)
 
 
-def test_c4_sampled(lib):
-    cfg = workloads.CONFIGS["c4"]
+def test_sparse_causal_h16_n16300_d128_sampled(lib):
+    cfg = workloads.CONFIGS["sparse-causal-h16-n16300-d128"]
     rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
-    print("case c4", flush=True)
+    print("case sparse-causal-h16-n16300-d128", flush=True)
 
     def sample(h):
         r = set(workloads.sample_rows(cfg.N, 384, cfg.seed * 1000 + h).tolist())

@@ -72,16 +72,16 @@ class Config:
 
 
 CONFIGS: Dict[str, Config] = {
-    "c1": Config("c1", 1, 1, 256, 64, "f32", False, False, 0, 1, 0,
+    "dense-f32-h1-n256-d64": Config("dense-f32-h1-n256-d64", 1, 1, 256, 64, "f32", False, False, 0, 1, 0,
                  "dense non-causal, B=1 H=1 N=256 d=64, fp32"),
-    "c2": Config("c2", 4, 16, 2048, 64, "bf16", True, False, 0, 2, 0,
+    "causal-b4-h16-n2048-d64": Config("causal-b4-h16-n2048-d64", 4, 16, 2048, 64, "bf16", True, False, 0, 2, 0,
                  "causal, B=4 H=16 N=2048 d=64, bf16"),
-    "c3": Config("c3", 1, 32, 8192, 128, "bf16", False, False, 0, 3, 0,
+    "dense-h32-n8192-d128": Config("dense-h32-n8192-d128", 1, 32, 8192, 128, "bf16", False, False, 0, 3, 0,
                  "dense non-causal, B=1 H=32 N=8192 d=128, bf16"),
-    "c4": Config("c4", 1, 16, 16300, 128, "bf16", True, True, 128, 4, 0,
+    "sparse-causal-h16-n16300-d128": Config("sparse-causal-h16-n16300-d128", 1, 16, 16300, 128, "bf16", True, True, 128, 4, 0,
                  "block-sparse causal, B=1 H=16 N=16300 d=128, b=128, bf16, "
                  "local band 4 + 2 global + 2 random earlier blocks, duplicates, empty rows"),
-    "c5": Config("c5", 1, 8, 131072, 128, "bf16", True, False, 0, 5, 1024,
+    "causal-h8-n131072-d128": Config("causal-h8-n131072-d128", 1, 8, 131072, 128, "bf16", True, False, 0, 5, 1024,
                  "causal long context, B=1 H=8 N=131072 d=128, bf16, 1024 sampled rows per head"),
 }
 
