@@ -162,6 +162,19 @@ def test_gqa_sparse_backward(lib, causal, meta):
     _bwd_check(lib, B, H, Hkv, N, d, causal, 7400, sparse=(block, rp, col, mh))
 
 
+def test_gqa_sparse_backward_long_key_lists_are_split(lib):
+    # key block 0 of 64-key blocks is listed by all 36 query blocks of both query heads of each
+    # key/value head: 72 query tiles > 32, so its dK/dV are summed from 3 pieces
+    B, H, Hkv, N, d, block = 1, 4, 2, 2304, 64, 64
+    print("case gqa sparse bwd split", flush=True)
+    nb = N // block
+    rp, col = workloads.lists_to_csr([[0, qb] if qb else [0] for qb in range(nb)])
+    mask = lib.blockmask_build(rp, col, 1, N, block, True)
+    least = int(lib._get_lib().attn_bwd_blocksparse_workspace_bytes(B, H, Hkv, N, d, 1, block, None, 1))
+    assert lib.bwd_blocksparse_workspace_bytes(B, H, N, d, mask, Hkv=Hkv) > least
+    _bwd_check(lib, B, H, Hkv, N, d, True, 7500, sparse=(block, rp, col, 1))
+
+
 def test_hkv_equal_h_matches_plain_bitwise(lib):
     B, H, N, d = 1, 4, 300, 128
     q, k, v = (t.cuda() for t in _inputs(B, H, H, N, d, "bf16", 7500))
