@@ -115,10 +115,11 @@ struct BwdArgs {
     // into up to `pieces` pieces of workgroups; plan[kvbh * nkt + kt] = (first
     // partial slot, pieces) and the pieces' fp32 partial dK, dV go to
     // part[slot][2][BKV][d] for an ordered reduction.
+    // extra[slot] = (key tile, piece) for every used slot ((-1, -1) past them).
     // The dK/dV launch has part_slots + (key tiles) workgroups: the first run
-    // extra[w] = (key tile, piece >= 1) of the split key tiles ((-1, -1) past
-    // the used slots; piece-0 entries are skipped), the rest piece 0 of every
-    // key tile.
+    // the pieces >= 1 named by extra (piece-0 entries are skipped), the rest
+    // piece 0 of every key tile; the reduction's workgroups sit on the piece-0
+    // entries, the first slot of each split key tile.
     int2* plan;
     int2* extra;
     float* part;
