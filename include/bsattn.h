@@ -202,8 +202,10 @@ int attn_fwd_blocksparse_prepared(const void* q, const void* k, void* o, float* 
  * kernel, the dQ kernel, all on `stream`; results are deterministic (no
  * atomics).
  *
- * attn_bwd_workspace_bytes - device workspace attn_bwd and attn_bwd_blocksparse
- *   need (the row statistics): B*H*(ceil(N/128)*2 + 1)*512 bytes.
+ * attn_bwd_workspace_bytes - device workspace attn_bwd needs (the row
+ *   statistics): B*H*(ceil(N/128)*2 + 1)*512 bytes.  attn_bwd_gqa and the
+ *   block-sparse backward size theirs with attn_bwd_gqa_workspace_bytes and
+ *   attn_bwd_blocksparse_workspace_bytes.
  *   Returns -1 for sizes or a dtype the kernels do not accept.
  *
  * attn_bwd - gradients of attn_fwd.
