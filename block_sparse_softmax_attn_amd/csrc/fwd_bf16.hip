@@ -42,7 +42,8 @@
 namespace bsattn {
 namespace {
 
-constexpr int BN = 64;                 // keys per tile step
+constexpr int kBN = 64;                // keys per tile step (32 for 64-key sparse blocks at d = 128)
+constexpr int kVtKeys = 64;            // keys per workgroup of the V^T pass
 constexpr float kSlack = 8.0f;         // lazy-rescale headroom, base-2 units
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -53,8 +54,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 //          straight into LDS and read with plain 16-byte LDS loads.
 enum VSrc : int { kVsTr = 0, kVsT = 1 };
 
-template <int D, int NW, int NS, int VSRC>
+template <int D, int NW, int NS, int VSRC, int BN_ = kBN>
 struct Geo {
+    static constexpr int BN = BN_;                   // keys per tile step
     static constexpr int NT = 64 * NW;               // threads per workgroup
     static constexpr int BM = 32 * NW;               // query rows per workgroup
     static constexpr int K_BYTES = BN * D * 2;       // K tile: BN rows of D bf16
@@ -75,9 +77,9 @@ struct TileDesc {
     int masked;    // any element mask needed (uniform over the workgroup)
 };
 
-template <int D, int NW, int NS, int MODE, int VSRC>
+template <int D, int NW, int NS, int MODE, int VSRC, int BN = kBN>
 __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
-    using G = Geo<D, NW, NS, VSRC>;
+    using G = Geo<D, NW, NS, VSRC, BN>;
     constexpr bool VTR = VSRC == kVsTr;
     // One array per stage: distinct objects let the compiler see that a tile in
     // flight never aliases the tile being read.
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             v_off[i] = rt_swz<D>(r, p) * 8;
         } else {
             const int d = byte / (2 * BN), p = (byte % (2 * BN)) / 16;
-            v_off[i] = d * a.npad + v_swz(d, p) * 8;
+            v_off[i] = d * a.npad + v_swz<BN>(d, p) * 8;
         }
     }
     // Row-major K and V tiles: byte offsets inside the tile, fixed for the
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                     if constexpr (VTR) {
                         vf = tr_operand<D>(bV, trl, g, db);   // keys in the order pf[g] holds them
                     } else {
-                        vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz(d, 2 * g + hi) * 16);
+                        vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz<BN>(d, 2 * g + hi) * 16);
                     }
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g], oacc[db], 0, 0, 0);
                 }
@@ -424,11 +426,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void v_transpose_kernel(const __bf16* __restrict__ v, __bf16* __restrict__ vt,
                                                            int N, int npad) {
-    __shared__ __bf16 tile[BN][D + 2];
-    const int kb0 = blockIdx.x * BN;
+    __shared__ __bf16 tile[kVtKeys][D + 2];
+    const int kb0 = blockIdx.x * kVtKeys;
     const int64_t bh = blockIdx.y;
     const __bf16* src = v + bh * (int64_t)N * D;
-    for (int c = threadIdx.x; c < BN * D / 8; c += 256) {
+    for (int c = threadIdx.x; c < kVtKeys * D / 8; c += 256) {
         const int r = c / (D / 8), ch = c % (D / 8);
         const int key = kb0 + r;
         u32x4 x = {0u, 0u, 0u, 0u};
@@ -439,8 +441,8 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const __bf16* __restri
     }
     __syncthreads();
     __bf16* dst = vt + bh * (int64_t)npad * D;
-    for (int c = threadIdx.x; c < D * (BN / 8); c += 256) {
-        const int d = c / (BN / 8), ch = c % (BN / 8);
+    for (int c = threadIdx.x; c < D * (kVtKeys / 8); c += 256) {
+        const int d = c / (kVtKeys / 8), ch = c % (kVtKeys / 8);
         bf16x8 out;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -452,20 +454,21 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(const __bf16* __restri
     }
 }
 
-template <int D, int NW, int NS, int MODE, int VSRC>
+template <int D, int NW, int NS, int MODE, int VSRC, int BN = kBN>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    using G = Geo<D, NW, NS, VSRC>;
+    using G = Geo<D, NW, NS, VSRC, BN>;
     const int64_t nqt = (a.N + G::BM - 1) / G::BM;
     const int64_t grid = nqt * a.BH * (MODE == (int)Mode::kRange ? a.nsplit : 1);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VSRC>), dim3((unsigned)grid), dim3(G::NT), 0, stream, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VSRC, BN>), dim3((unsigned)grid), dim3(G::NT), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
 // V^T from the caller's workspace when a.vt is set, else V read in place.
-template <int D, int NW, int NS, int MODE>
+template <int D, int NW, int NS, int MODE, int BN = kBN>
 hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
-    if (a.vt != nullptr) return launch<D, NW, NS, MODE, kVsT>(a, stream);
-    return launch<D, NW, NS, MODE, kVsTr>(a, stream);
+    if (a.vt != nullptr) return launch<D, NW, NS, MODE, kVsT, BN>(a, stream);
+    return launch<D, NW, NS, MODE, kVsTr, BN>(a, stream);
 }
 
 template <int D>
@@ -492,7 +495,10 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
         case Mode::kRange: return launch_v<D, 8, 3, (int)Mode::kRange>(a, stream);
         case Mode::kSparse:
             if (a.block == 128) return launch_v<D, 4, 2, (int)Mode::kSparse>(a, stream);
-            return launch_v<D, 2, 2, (int)Mode::kSparse>(a, stream);
+            // 64-key blocks at d = 128: 32-key tile steps, so a workgroup's two
+            // stages take 32 KiB of LDS and four workgroups (two waves per SIMD)
+            // fit a CU; 64-key steps left one wave per SIMD (LDS-bound)
+            return launch_v<D, 2, 2, (int)Mode::kSparse, D == 128 ? 32 : kBN>(a, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -502,7 +508,7 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
 int64_t vt_padded_keys(int64_t N) { return (N + 127) / 128 * 128; }
 
 hipError_t launch_v_transpose(const FwdArgs& a, hipStream_t stream) {
-    const dim3 grid((unsigned)(a.npad / BN), (unsigned)a.BH);
+    const dim3 grid((unsigned)(a.npad / kVtKeys), (unsigned)a.BH);
     if (a.d == 64)
         hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, stream, static_cast<const __bf16*>(a.v),
                            static_cast<__bf16*>(a.vt), a.N, a.npad);

@@ -63,8 +63,10 @@ template <int D>
 static __device__ __forceinline__ int k_swz(int r, int c) {
     return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
-// Transposed tiles (V^T, Q^T, ...) hold 64 tokens per row: 128-byte rows, 8 chunks.
-static __device__ __forceinline__ int v_swz(int d, int c) { return c ^ ((d >> 1) & 7); }
+// Transposed V^T tiles hold KEYS tokens per row: 2 KEYS-byte rows of KEYS / 8
+// chunks (8 for 64 keys, 4 for 32); the mask stays inside the row.
+template <int KEYS = 64>
+static __device__ __forceinline__ int v_swz(int d, int c) { return c ^ ((d >> 1) & (KEYS / 8 - 1)); }
 
 // Row r, logical chunk c of a row-major tile that is read both with plain
 // 16-byte loads (16 consecutive rows at one chunk) and with transposing loads
