@@ -667,11 +667,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
 // dQ: query-stationary
 // ---------------------------------------------------------------------------
 
-template <int D, int NW, int NS>
+template <int D, int NW, int NS, int KT = BT>
 struct DqGeo {
     static constexpr int NT = 64 * NW;
     static constexpr int BM = 32 * NW;               // queries per workgroup
-    static constexpr int TB = BT * D * 2;            // bytes of a K or V tile
+    static constexpr int TB = KT * D * 2;            // bytes of a K or V tile (KT keys)
     static constexpr int PER_T = TB / 1024 / NW;
     static constexpr int PER_W = 2 * PER_T;
     static_assert(TB % (1024 * NW) == 0, "tile must split over waves");
@@ -686,9 +686,9 @@ struct KeyTile {
     int masked;   // any element mask needed
 };
 
-template <int D, int NW, int NS, int MODE>
+template <int D, int NW, int NS, int MODE, int KT = BT>
 __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
-    using G = DqGeo<D, NW, NS>;
+    using G = DqGeo<D, NW, NS, KT>;
     constexpr int T2 = NS > 2 ? G::TB : 16;
     __shared__ __attribute__((aligned(1024))) unsigned char sK0[G::TB], sK1[G::TB], sK2[T2];
     __shared__ __attribute__((aligned(1024))) unsigned char sV0[G::TB], sV1[G::TB], sV2[T2];
@@ -727,11 +727,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     // ---- schedule of 64-key tiles (the forward's) ----
     int ntiles = 0, e0 = 0, subs = 1, nqb_meta = 0;
     if (MODE == (int)Mode::kDense) {
-        ntiles = (N + BT - 1) / BT;
+        ntiles = (N + KT - 1) / KT;
     } else if (MODE == (int)Mode::kCausal) {
-        ntiles = (min(N, q0 + G::BM) + BT - 1) / BT;
+        ntiles = (min(N, q0 + G::BM) + KT - 1) / KT;
     } else {
-        subs = a.block / BT;
+        subs = a.block / KT;
         nqb_meta = (N + a.block - 1) / a.block;
         const int64_t r = meta_of(bh, a.H, a.Hkv, a.meta_heads) * nqb_meta + qt;   // BM == block for sparse launches
         int lo = ld_meta(a.row_ptr, r), hi_ = ld_meta(a.row_ptr, r + 1);
@@ -746,15 +746,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
             const int e = e0 + it / subs;
             const int kb = ld_meta(a.col, e);
             const bool valid = kb >= 0 && kb < nqb_meta;
-            t.kb0 = valid ? kb * a.block + (it % subs) * BT : 0;
+            t.kb0 = valid ? kb * a.block + (it % subs) * KT : 0;
             t.nlim = valid ? N : 0;
-            t.causal = ((ld_meta_byte(a.flags, e) & 1) != 0) || (a.causal && t.kb0 + BT - 1 > q0);
+            t.causal = ((ld_meta_byte(a.flags, e) & 1) != 0) || (a.causal && t.kb0 + KT - 1 > q0);
         } else {
-            t.kb0 = it * BT;
+            t.kb0 = it * KT;
             t.nlim = N;
-            t.causal = (MODE == (int)Mode::kCausal) && (t.kb0 + BT - 1 > q0);
+            t.causal = (MODE == (int)Mode::kCausal) && (t.kb0 + KT - 1 > q0);
         }
-        t.masked = t.causal || (t.kb0 + BT > t.nlim);
+        t.masked = t.causal || (t.kb0 + KT > t.nlim);
         return t;
     };
 
@@ -774,7 +774,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
     const unsigned vl[3] = {lds_addr(sV0), lds_addr(sV1), lds_addr(sV2)};
     const unsigned wl = __builtin_amdgcn_readfirstlane(w * G::PER_T * 1024);
     auto issue = [&](int kb0, int u) {
-        if (kb0 + BT <= N) {
+        if (kb0 + KT <= N) {
             const __bf16* kt = Kh + (int64_t)kb0 * D;
             const __bf16* vt = Vh + (int64_t)kb0 * D;
 #pragma unroll
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dq_kernel(BwdArgs a) {
             const unsigned char* bK = kbuf[u];
             const unsigned char* bV = vbuf[u];
 #pragma unroll
-            for (int c = 0; c < BT / 32; ++c) {
+            for (int c = 0; c < KT / 32; ++c) {
                 // ---- S^T and dP^T: lane (l32, hi) gets key
                 // kb0 + 32c + 8(v>>2) + 4hi + (v&3) of query qi in element v ----
                 f32x16 s = f32x16{}, dp = f32x16{};
@@ -971,10 +971,11 @@ hipError_t launch_dkdv(const BwdArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int D, int NW, int NS, int MODE>
+template <int D, int NW, int NS, int MODE, int KT = BT>
 hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
     const int64_t nqt = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NS, MODE>), dim3((unsigned)(nqt * a.BH)), dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, NW, NS, MODE, KT>), dim3((unsigned)(nqt * a.BH)), dim3(64 * NW), 0, stream,
+                       a);
     return hipGetLastError();
 }
 
@@ -1022,7 +1023,9 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
             }
             e = launch_dkdv<D, D == 64 ? 2 : 4, (int)Mode::kSparse>(a, stream);
             if (e == hipSuccess) e = launch_reduce<D, 64>(a, nkt_sparse, stream);
-            return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse>(a, stream);
+            // dQ of 64-key blocks at d = 128 in 32-key steps: 32 KiB of LDS per
+            // workgroup, so two waves per SIMD fit (64-key steps: one)
+            return e != hipSuccess ? e : launch_dq<D, 2, 2, (int)Mode::kSparse, D == 128 ? 32 : BT>(a, stream);
         }
         case Mode::kRange: break;   // no backward for key-range launches
     }
