@@ -242,14 +242,17 @@ def test_prepared_v_path_is_bitwise_equal(lib):
         got = lib.attn_fwd_prepared(q, k, ws, causal=causal)
         torch.cuda.synchronize()
         assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
-    nqb = -(-N // 128)
-    rng = workloads.SplitMix64(85)
-    rp, col = workloads.lists_to_csr(workloads.random_lists(nqb, nqb, rng, max_len=nqb, empty_prob_per_mille=200))
-    mask = lib.blockmask_build(rp, col, 1, N, 128, True)
-    ref = lib.attn_fwd_blocksparse(q, k, v, mask)
-    got = lib.attn_fwd_blocksparse_prepared(q, k, lib.prepare_v(v), mask)
-    torch.cuda.synchronize()
-    assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1])
+    # 128-key blocks (64-key tile steps) and 64-key blocks (32-key steps at d = 128)
+    for block in (128, 64):
+        nqb = -(-N // block)
+        rng = workloads.SplitMix64(85 + block)
+        rp, col = workloads.lists_to_csr(workloads.random_lists(nqb, nqb, rng, max_len=nqb,
+                                                                empty_prob_per_mille=200))
+        mask = lib.blockmask_build(rp, col, 1, N, block, True)
+        ref = lib.attn_fwd_blocksparse(q, k, v, mask)
+        got = lib.attn_fwd_blocksparse_prepared(q, k, lib.prepare_v(v), mask)
+        torch.cuda.synchronize()
+        assert torch.equal(ref[0], got[0]) and torch.equal(ref[1], got[1]), f"block {block}"
 
 
 def test_prepared_v_buffer_too_small_is_rejected(lib):
