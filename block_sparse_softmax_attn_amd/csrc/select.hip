@@ -39,26 +39,40 @@ __device__ __forceinline__ float to_f32(T x) {
     return (float)x;
 }
 
-// out[h][blk][c] = mean over the rows of block blk of x[h][row][c].
+// out[h][blk][c] = mean over the rows of block blk of x[h][row][c].  Each
+// thread owns one 16-byte chunk of a row (E values) and adds it over every
+// RG-th row of the block; the RG partial sums per column are then added in
+// row-group order (deterministic).
 template <int D, typename T>
 __global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, float* __restrict__ out, int N,
                                                    int block, int nb) {
-    constexpr int RG = 256 / D;   // row groups
+    constexpr int E = 16 / (int)sizeof(T);   // values per 16-byte chunk
+    constexpr int CPR = D / E;               // chunks per row
+    constexpr int RG = 256 / CPR;            // row groups
+    static_assert(CPR * E == D && RG * CPR == 256, "chunking must cover the row");
     __shared__ float part[RG][D];
     const int blk = blockIdx.x;
     const int64_t h = blockIdx.y;
-    const int c = threadIdx.x % D, rg = threadIdx.x / D;
+    const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
     const int r0 = blk * block, r1 = min(N, r0 + block);
-    const T* src = x + h * (int64_t)N * D;
-    float acc = 0.f;
-    for (int r = r0 + rg; r < r1; r += RG) acc += to_f32(src[(int64_t)r * D + c]);
-    part[rg][c] = acc;
-    __syncthreads();
-    if (rg == 0) {
-        float s = 0.f;
+    const T* src = x + h * (int64_t)N * D + ch * E;
+    float acc[E];
 #pragma unroll
-        for (int g = 0; g < RG; ++g) s += part[g][c];
-        out[(h * nb + blk) * (int64_t)D + c] = s / (float)(r1 - r0);
+    for (int e = 0; e < E; ++e) acc[e] = 0.f;
+    for (int r = r0 + rg; r < r1; r += RG) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)r * D);
+        const T* vals = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] += to_f32(vals[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[rg][ch * E + e] = acc[e];
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += 256) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) sum += part[g][c];
+        out[(h * nb + blk) * (int64_t)D + c] = sum / (float)(r1 - r0);
     }
 }
 
