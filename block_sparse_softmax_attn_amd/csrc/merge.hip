@@ -33,20 +33,26 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int c = (threadIdx.x % TPR) * 4;
     if (row >= rows) return;
+    // one pass with a running max (the partial states are folded in split
+    // order, each rescaled to the new max), unrolled so that several splits'
+    // loads are in flight at once; empty states (LSE = -inf) are skipped
     float m = -__builtin_inff();
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, lse_part[(int64_t)s * rows + row]);
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     float tot = 0.f;
-    if (m > -__builtin_inff()) {
-        for (int s = 0; s < nsplit; ++s) {
-            const float ls = lse_part[(int64_t)s * rows + row];
-            const float wgt = ls > -__builtin_inff() ? expf(ls - m) : 0.f;
-            const float4 x = *reinterpret_cast<const float4*>(o_part + ((int64_t)s * rows + row) * D + c);
-            acc.x += wgt * x.x;
-            acc.y += wgt * x.y;
-            acc.z += wgt * x.z;
-            acc.w += wgt * x.w;
-            tot += wgt;
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) {
+        const float ls = lse_part[(int64_t)s * rows + row];
+        const float4 x = *reinterpret_cast<const float4*>(o_part + ((int64_t)s * rows + row) * D + c);
+        if (ls > -__builtin_inff()) {
+            const float mn = fmaxf(m, ls);
+            const float keep = expf(m - mn);   // 0 while nothing is folded in yet
+            const float wgt = expf(ls - mn);
+            acc.x = acc.x * keep + wgt * x.x;
+            acc.y = acc.y * keep + wgt * x.y;
+            acc.z = acc.z * keep + wgt * x.z;
+            acc.w = acc.w * keep + wgt * x.w;
+            tot = tot * keep + wgt;
+            m = mn;
         }
     }
     const float inv = tot > 0.f ? 1.0f / tot : 0.f;
