@@ -217,6 +217,37 @@ def test_outputs_not_written_past_n(lib):
     assert torch.all(big_o[B * H * N * d:] == 7.0) and torch.all(big_l[B * H * N:] == 7.0)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_growing_logits_rescale_every_tile(lib, d, causal):
+    # key j = (j + 1) * k0: for queries with q . k0 > 0 the logits grow along the keys, so the
+    # running max rises by far more than the lazy-rescale slack on every tile and the rescale
+    # runs each time; queries with q . k0 < 0 keep their first tile's max
+    B, H, N = 1, 2, 777
+    print(f"case growing logits d={d} causal={causal}", flush=True)
+    q, k, v = inputs(B, H, N, d, "bf16", 91 + d)
+    growth = torch.arange(1, N + 1, dtype=torch.float32).view(1, 1, N, 1)
+    k = (k[:, :, :1, :].float() * growth).to(torch.bfloat16).contiguous()
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = lib.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, causal)
+    # Attention here sits on a few keys of |V| up to ~4, where the fixed 1e-2 bound of the N(0,1)
+    # workloads is below bf16 resolution.  Bound per element from the arithmetic: P rounded to
+    # bf16 (relative 2^-8 per weight) gives at most 2^-8 sum_j P_ij |V_jc|; O stored in bf16
+    # adds half an ulp of |O|; 1e-4 covers the fp32 scores, exponentials and sums.
+    q64, k64, v64 = to64(q), to64(k), to64(v)
+    logits = scale * np.einsum("bhid,bhjd->bhij", q64, k64)
+    if causal:
+        logits = np.where(np.tril(np.ones((N, N), dtype=bool)), logits, -np.inf)
+    prob = np.exp(logits - lse_ref[..., None])
+    half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 2.0 ** -126))) - 8)
+    bound = 2.0 ** -8 * np.einsum("bhij,bhjc->bhic", prob, np.abs(v64)) + half_ulp + 1e-4
+    err = np.abs(to64(o) - o_ref)
+    assert np.all(err <= bound), f"max excess {np.max(err - bound):.3e}, max|dO| {err.max():.3e}"
+    assert np.max(np.abs(to64(lse) - lse_ref)) <= 1e-3
+
+
 def test_single_key_gives_its_value_on_gpu(lib):
     q, k, v = (t.cuda() for t in inputs(2, 3, 1, 128, "bf16", 82))
     o, lse = lib.attn_fwd(q, k, v, causal=False)
