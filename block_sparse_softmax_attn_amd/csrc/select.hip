@@ -100,8 +100,13 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     __shared__ float sc[kRowsPerWg][kMaxBlocks];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nwg_h = (a.nb + kRowsPerWg - 1) / kRowsPerWg;
-    const int64_t bh = blockIdx.x / nwg_h;
-    const int qb0 = (int)(blockIdx.x % nwg_h) * kRowsPerWg;
+    // each XCD takes a contiguous range of heads, so one head's pooled keys
+    // stay in one L2; inside it the workgroups with the most (causal)
+    // candidates start first
+    int64_t bh;
+    int rank;
+    rank_major_order(blockIdx.x, (int64_t)nwg_h * a.BH, nwg_h, bh, rank);
+    const int qb0 = (nwg_h - 1 - rank) * kRowsPerWg;
     const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
     const int group = a.H / a.Hkv;
 
