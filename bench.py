@@ -30,7 +30,8 @@ products; its cpu_baseline is the float64 gradient oracle), --pass select
 (one step = the device mean-pooled selector, --topk blocks of 128 per query
 block, then the block-sparse forward on its output, on the workload's shapes
 with causal masking; reports the selector's cost against the dense tiles it
-lets the forward skip).
+lets the forward skip), --pass splitkv (one step = attn_fwd_splitkv over --splits
+key ranges in one launch, then the merge of the fp32 partial states).
 """
 from __future__ import annotations
 
@@ -155,8 +156,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
-    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "select"])
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd", "select", "splitkv"])
     ap.add_argument("--topk", type=int, default=16)
+    ap.add_argument("--splits", type=int, default=8)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -179,6 +181,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.which == "bwd":
         bench_bwd(args, cfg, dev)
+        return
+    if args.which == "splitkv":
+        bench_splitkv(args, cfg, dev)
         return
     if args.which == "select":
         bench_select(args, cfg, dev)
@@ -433,6 +438,40 @@ def bench_select(args, cfg, dev):
                      "skipped_tile_time_ms_estimate": round(dense_ms * skipped / dense_tiles, 4),
                      "selector_cost_over_skipped_work": round(sel_ms / (dense_ms * skipped / dense_tiles), 5),
                      "step_speedup_over_dense": round(dense_ms / step_ms, 3)},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_splitkv(args, cfg, dev):
+    """One step = attn_fwd_splitkv: the forward over --splits key ranges in one
+    launch (fp32 partial states in the workspace), then the merge launch."""
+    import torch
+    import block_sparse_softmax_attn_amd as attn
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    q, k, v = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
+               .to(torch.bfloat16).contiguous() for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
+    lib = attn._get_lib()
+    ws = torch.empty(lib.attn_fwd_splitkv_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, 1, args.splits),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    step = lambda: attn.attn_fwd_splitkv(q, k, v, scale=cfg.scale, causal=cfg.causal, num_splits=args.splits,
+                                         out=o, lse=lse, workspace=ws)
+    wall_ms, _ = _time_calls(step, args.steps, args.warmup, stream)
+    pairs = allowed_pairs_dense(cfg)
+    rows = cfg.B * cfg.H * cfg.N
+    merge_bytes = args.splits * rows * (cfg.d * 4 + 4) + rows * (cfg.d * 2 + 4)
+    rec = {
+        "metric": "attention fwd TFLOP/s (allowed pairs), key ranges in one launch + merge, 1\u00d7MI355X",
+        "value": round(4 * cfg.d * pairs / (wall_ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.description + f", {args.splits} key ranges", "B": cfg.B, "H": cfg.H,
+                   "N": cfg.N, "d": cfg.d, "causal": cfg.causal, "splits": args.splits,
+                   "merge_bytes_per_step": merge_bytes, "parallelism": "single GPU"},
     }
     print(json.dumps(rec), flush=True)
 
