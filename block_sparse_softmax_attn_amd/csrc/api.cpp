@@ -516,6 +516,9 @@ extern "C" int attn_select_meanpool(const void* q, const void* k, int64_t B, int
     if (!aligned16(q) || !aligned16(k) || !aligned16(workspace)) return ATTN_EINVAL;
     if (B * H * N > (int64_t(1) << 40) / d) return ATTN_EINVAL;
     const int64_t nb = (N + block - 1) / block;
+    // one 256-thread workgroup per (head of Q or K, block) in a flat grid: keep
+    // the grid's work-items under 2^32
+    if (nb * B * (H + Hkv) >= (int64_t(1) << 24)) return ATTN_EUNSUPPORTED;
     float* qm = static_cast<float*>(workspace);
     float* km = qm + B * H * nb * d;
     const hipError_t e = bsattn::launch_select(q, k, dtype == ATTN_BF16, B, static_cast<int>(H),

@@ -13,13 +13,17 @@
 //
 // Two kernels, both far off the attention's critical cost (section 5: the
 // selector must cost less than the tiles it skips):
-//   pool:   block means of Q and K in fp32, one read of each (HBM-bound);
+//   pool:   block means of Q and K in fp32, one read of each, in one launch
+//           (HBM-bound);
 //   select: per head, 8 query blocks per workgroup; each thread scores the
 //           key blocks it owns against the 8 pooled queries (k_bar is read
-//           once per 8 query blocks), then one wave per query block takes the
-//           top-k by repeated wave-wide argmax and writes the canonical CSR
-//           row (ascending, unique) with its flags, straight into the
-//           metadata the block-sparse kernels read.
+//           once per 8 query blocks), then one wave per query block finds the
+//           k-th largest score by a radix select over order-preserving 32-bit
+//           keys (one bit per pass, counted with wave ballots, stopping once
+//           the keys that share the fixed bits are exactly the ones still
+//           needed), and writes the canonical CSR row (ascending, unique) with
+//           its flags, straight into the metadata the block-sparse kernels
+//           read.  Equal scores go to the lower block index.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,32 +38,63 @@ constexpr int kRowsPerWg = 8;          // query blocks per select workgroup
 constexpr int kMaxBlocks = 2048;       // key blocks per head the select kernel holds
 constexpr int kMaxTopk = 64;
 
+// Order-preserving map of a score to an unsigned key: a larger score gives a
+// larger key, -0 is folded into +0 (so equal scores give equal keys) and NaN
+// ranks with -inf.  Every score maps to at least 0x007fffff, so 0 is free to
+// mark a slot that holds no candidate.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    s = s != s ? -__builtin_inff() : s + 0.0f;
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 template <typename T>
 __device__ __forceinline__ float to_f32(T x) {
     return (float)x;
 }
 
-// out[h][blk][c] = mean over the rows of block blk of x[h][row][c].  Each
-// thread owns one 16-byte chunk of a row (E values) and adds it over every
-// RG-th row of the block; the RG partial sums per column are then added in
-// row-group order (deterministic).
+// out[h][blk][c] = mean over the rows of block blk of x[h][row][c], for Q's
+// heads then K's in one flat grid (workgroup = (head, block)).  Each thread
+// owns one 16-byte chunk of a row (E values) and adds it over every RG-th row
+// of the block, four rows' loads in flight at a time; the RG partial sums per
+// column are then added in row-group order (deterministic).
 template <int D, typename T>
-__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ x, float* __restrict__ out, int N,
-                                                   int block, int nb) {
+__global__ __launch_bounds__(256) void pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                   float* __restrict__ qm, float* __restrict__ km, int64_t BHq,
+                                                   int N, int block, int nb) {
     constexpr int E = 16 / (int)sizeof(T);   // values per 16-byte chunk
     constexpr int CPR = D / E;               // chunks per row
     constexpr int RG = 256 / CPR;            // row groups
     static_assert(CPR * E == D && RG * CPR == 256, "chunking must cover the row");
     __shared__ float part[RG][D];
-    const int blk = blockIdx.x;
-    const int64_t h = blockIdx.y;
+    const int blk = (int)(blockIdx.x % (unsigned)nb);
+    int64_t h = blockIdx.x / (unsigned)nb;
+    const T* x = q;
+    float* out = qm;
+    if (h >= BHq) {
+        h -= BHq;
+        x = k;
+        out = km;
+    }
     const int ch = threadIdx.x % CPR, rg = threadIdx.x / CPR;
     const int r0 = blk * block, r1 = min(N, r0 + block);
     const T* src = x + h * (int64_t)N * D + ch * E;
     float acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.f;
-    for (int r = r0 + rg; r < r1; r += RG) {
+    int r = r0 + rg;
+    for (; r + 3 * RG < r1; r += 4 * RG) {
+        uint4 raw[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) raw[u] = *reinterpret_cast<const uint4*>(src + (int64_t)(r + u * RG) * D);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const T* vals = reinterpret_cast<const T*>(&raw[u]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[e] += to_f32(vals[e]);
+        }
+    }
+    for (; r < r1; r += RG) {
         const uint4 raw = *reinterpret_cast<const uint4*>(src + (int64_t)r * D);
         const T* vals = reinterpret_cast<const T*>(&raw);
 #pragma unroll
@@ -94,10 +129,12 @@ __device__ __forceinline__ int64_t row_start(int qb, int topk, int nb, int causa
     return (int64_t)topk * (topk + 1) / 2 + (int64_t)(qb - topk) * topk;
 }
 
-template <int D>
+// MB: the key blocks per head this instance holds (nb <= MB); the score
+// buffer is sized by it, so the smaller instance fits more workgroups per CU.
+template <int D, int MB>
 __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     __shared__ float qs[kRowsPerWg][D];
-    __shared__ float sc[kRowsPerWg][kMaxBlocks];
+    __shared__ float sc[kRowsPerWg][MB];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int nwg_h = (a.nb + kRowsPerWg - 1) / kRowsPerWg;
     // each XCD takes a contiguous range of heads, so one head's pooled keys
@@ -147,56 +184,64 @@ __global__ __launch_bounds__(256) void select_kernel(SelArgs a) {
     __syncthreads();
 
     // top-k per query block: one wave per row, candidates kb = lane + 64 j
-    constexpr int J = kMaxBlocks / 64;
+    constexpr int J = MB / 64;
     const int64_t per_head = row_start(a.nb, a.topk, a.nb, a.causal);
+    const uint64_t below = (1ull << lane) - 1ull;   // lanes under this one
     for (int rr = w; rr < kRowsPerWg; rr += 4) {
         const int qb = qb0 + rr;
         if (qb >= a.nb) break;
         const int ncand = a.causal ? qb + 1 : a.nb;
         const int kk = min(a.topk, ncand);
-        float sv[J];
+        const int jn = (ncand + 63) >> 6;   // 64-candidate slices that hold candidates
+        uint32_t key[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int c = lane + 64 * j;
-            sv[j] = c < ncand ? sc[rr][c] : -__builtin_inff();
+            key[j] = (j < jn && c < ncand) ? score_key(sc[rr][c]) : 0u;
         }
-        uint32_t chosen = 0u;   // bit j: candidate lane + 64 j is selected
-        for (int round = 0; round < kk; ++round) {
-            float bv = -__builtin_inff();
-            int bi = 0x7fffffff;
+        // Radix select of the kk-th largest key T, from the top bit down:
+        // 'prefix' holds T's bits fixed so far (the bits in 'mask'), 'match'
+        // counts the candidates whose masked key equals it, and 'need' how
+        // many of those belong to the top kk (every candidate with a larger
+        // masked key does).  Once match == need they all do and the rest of
+        // T's bits do not matter.
+        uint32_t prefix = 0u, mask = 0u;
+        int need = kk, match = ncand;
+        for (int bit = 31; bit >= 0 && match != need; --bit) {
+            const uint32_t m2 = mask | (1u << bit), p2 = prefix | (1u << bit);
+            int cnt = 0;   // candidates that match and have this bit set
 #pragma unroll
-            for (int j = 0; j < J; ++j) {
-                const int c = lane + 64 * j;
-                if (c < ncand && !((chosen >> j) & 1u) && sv[j] > bv) {   // strict: the lower index wins ties
-                    bv = sv[j];
-                    bi = c;
-                }
+            for (int j = 0; j < J; ++j)
+                if (j < jn) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64((key[j] & m2) == p2));
+            if (cnt >= need) {
+                prefix = p2;
+                match = cnt;
+            } else {
+                need -= cnt;
+                match -= cnt;
             }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (ov > bv || (ov == bv && oi < bi)) {
-                    bv = ov;
-                    bi = oi;
-                }
-            }
-            if ((bi & 63) == lane) chosen |= 1u << (bi >> 6);
+            mask = m2;
         }
         // write the row in ascending order: ballot per 64-candidate slice
         const int64_t start = bh * per_head + row_start(qb, a.topk, a.nb, a.causal);
         const int r = (int)(bh * a.nb + qb);
         if (lane == 0) a.row_ptr[r] = (int32_t)start;
         if (lane == 0 && r == a.BH * a.nb - 1) a.row_ptr[r + 1] = (int32_t)(start + kk);
-        int written = 0;
+        int written = 0, eq_left = need;   // keys equal to the prefix still to take, lowest index first
         const bool partial = (a.N % a.block) != 0;
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const bool f = (chosen >> j) & 1u;
+            if (j >= jn) continue;
+            const uint32_t km = key[j] & mask;
+            const bool valid = lane + 64 * j < ncand;
+            const uint64_t em = __builtin_amdgcn_ballot_w64(valid && km == prefix);
+            const bool f =
+                valid && (km > prefix || (km == prefix && __builtin_popcountll(em & below) < eq_left));
+            eq_left -= min(eq_left, __builtin_popcountll(em));
             const uint64_t m = __builtin_amdgcn_ballot_w64(f);
             if (f) {
                 const int c = lane + 64 * j;
-                const int pos = written + __builtin_popcountll(m & ((1ull << lane) - 1ull));
+                const int pos = written + __builtin_popcountll(m & below);
                 a.col[start + pos] = c;
                 uint8_t fl = 0;
                 if (a.causal && c == qb && a.block > 1) fl |= ATTN_FLAG_DIAGONAL;
@@ -225,23 +270,22 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int64_t B, int
                          float scale, int causal, int block, int topk, int share, int32_t* row_ptr, int32_t* col,
                          uint8_t* flags, float* qm, float* km, hipStream_t stream) {
     const int nb = (N + block - 1) / block;
-    const dim3 gq((unsigned)nb, (unsigned)(B * H)), gk((unsigned)nb, (unsigned)(B * Hkv));
+    const int64_t BHq = B * H;
+    const dim3 gp((unsigned)(nb * (BHq + B * Hkv)));
     if (d == 64) {
-        if (bf16) {
-            hipLaunchKernelGGL((pool_kernel<64, __bf16>), gq, dim3(256), 0, stream, (const __bf16*)q, qm, N, block, nb);
-            hipLaunchKernelGGL((pool_kernel<64, __bf16>), gk, dim3(256), 0, stream, (const __bf16*)k, km, N, block, nb);
-        } else {
-            hipLaunchKernelGGL((pool_kernel<64, float>), gq, dim3(256), 0, stream, (const float*)q, qm, N, block, nb);
-            hipLaunchKernelGGL((pool_kernel<64, float>), gk, dim3(256), 0, stream, (const float*)k, km, N, block, nb);
-        }
+        if (bf16)
+            hipLaunchKernelGGL((pool_kernel<64, __bf16>), gp, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
+                               qm, km, BHq, N, block, nb);
+        else
+            hipLaunchKernelGGL((pool_kernel<64, float>), gp, dim3(256), 0, stream, (const float*)q, (const float*)k, qm,
+                               km, BHq, N, block, nb);
     } else {
-        if (bf16) {
-            hipLaunchKernelGGL((pool_kernel<128, __bf16>), gq, dim3(256), 0, stream, (const __bf16*)q, qm, N, block, nb);
-            hipLaunchKernelGGL((pool_kernel<128, __bf16>), gk, dim3(256), 0, stream, (const __bf16*)k, km, N, block, nb);
-        } else {
-            hipLaunchKernelGGL((pool_kernel<128, float>), gq, dim3(256), 0, stream, (const float*)q, qm, N, block, nb);
-            hipLaunchKernelGGL((pool_kernel<128, float>), gk, dim3(256), 0, stream, (const float*)k, km, N, block, nb);
-        }
+        if (bf16)
+            hipLaunchKernelGGL((pool_kernel<128, __bf16>), gp, dim3(256), 0, stream, (const __bf16*)q,
+                               (const __bf16*)k, qm, km, BHq, N, block, nb);
+        else
+            hipLaunchKernelGGL((pool_kernel<128, float>), gp, dim3(256), 0, stream, (const float*)q, (const float*)k,
+                               qm, km, BHq, N, block, nb);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -262,10 +306,14 @@ hipError_t launch_select(const void* q, const void* k, bool bf16, int64_t B, int
     s.share = share;
     s.scale = scale;
     const int64_t grid = (int64_t)((nb + kRowsPerWg - 1) / kRowsPerWg) * B * H;
-    if (d == 64)
-        hipLaunchKernelGGL(select_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, s);
-    else
-        hipLaunchKernelGGL(select_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, s);
+    const dim3 gs((unsigned)grid);
+    if (nb <= kMaxBlocks / 2) {
+        if (d == 64) hipLaunchKernelGGL((select_kernel<64, kMaxBlocks / 2>), gs, dim3(256), 0, stream, s);
+        else hipLaunchKernelGGL((select_kernel<128, kMaxBlocks / 2>), gs, dim3(256), 0, stream, s);
+    } else {
+        if (d == 64) hipLaunchKernelGGL((select_kernel<64, kMaxBlocks>), gs, dim3(256), 0, stream, s);
+        else hipLaunchKernelGGL((select_kernel<128, kMaxBlocks>), gs, dim3(256), 0, stream, s);
+    }
     return hipGetLastError();
 }
 

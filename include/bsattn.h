@@ -396,8 +396,10 @@ int attn_bwd_blocksparse_gqa(const void* q, const void* k, const void* v, const 
  *           block-sparse entry points).  nnz = attn_select_meanpool_nnz(...).
  *   workspace : device, attn_select_meanpool_workspace_bytes(...) bytes (the
  *               fp32 block means), 16-byte aligned.
- *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype, d, block, too many blocks),
- *   ATTN_ECAPACITY (capacity or workspace too small), ATTN_EHIP.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype, d, block, too many blocks,
+ *   or nb * B * (H + Hkv) >= 2^24: the pooling launch takes one workgroup per
+ *   head of Q or K and block), ATTN_ECAPACITY (capacity or workspace too
+ *   small), ATTN_EHIP.
  */
 int64_t attn_select_meanpool_nnz(int64_t B, int64_t H, int64_t N, int64_t block, int causal, int64_t topk);
 

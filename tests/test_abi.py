@@ -423,3 +423,16 @@ def test_select_rejects_bad_arguments(m):
     assert call(d=96) == -2 and call(dt=7) == -2 and call(blk=32) == -2 and call(topk=65) == -2
     assert call(topk=0) == -1
     assert call(cap=10) == -3 and call(ws=100) == -3
+
+
+def test_select_rejects_an_oversized_pooling_grid(m):
+    # one pooling workgroup per (head of Q or K, block): 16 blocks * 6 heads * B >= 2^24
+    from block_sparse_softmax_attn_amd._lib import get
+    lib = get()
+    B = -(-(1 << 24) // 96)
+    st = lib.attn_select_meanpool(FAKE, FAKE, B, 4, 2, 1000, 64, 1, ctypes.c_float(0.1), 1, 64, 4, 0, FAKE, FAKE,
+                                  FAKE, 1 << 40, FAKE, 1 << 40, None)
+    assert st == -2
+    st = lib.attn_select_meanpool(FAKE, FAKE, B - 1, 4, 2, 1000, 64, 1, ctypes.c_float(0.1), 1, 64, 4, 0, FAKE, FAKE,
+                                  FAKE, 10, FAKE, 1 << 40, None)
+    assert st == -3     # just under the limit: only the capacity is short

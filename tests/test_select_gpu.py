@@ -145,3 +145,29 @@ def test_selection_then_sparse_attention_end_to_end(lib):
     o_ref, lse_ref = oracle.attn_fwd_blocksparse(q, k, v, scale, True, block, rp, col, B * H)
     compare(to64(o).reshape(-1, d), to64(lse).reshape(-1), o_ref.reshape(-1, d), lse_ref.reshape(-1), "bf16",
             "selector + sparse forward")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nb,topk,share", [(40, 15, False), (40, 15, True), (1100, 64, False)],
+                         ids=["nb40-k15", "nb40-k15-shared", "nb1100-k64"])
+def test_exact_ties_go_to_the_lower_index(lib, nb, topk, share, causal):
+    # Every key block is a bitwise copy of one of four patterns whose mean
+    # logits sit far apart, so scores tie exactly inside a pattern's class and
+    # the top-k boundary falls inside a class: the selection is then fixed by
+    # the tie rule alone (lower block index first) and must equal the oracle's.
+    block, d = 64, 64
+    H, Hkv = (2, 1) if share else (1, 1)
+    N = nb * block
+    print(f"case select ties nb={nb} topk={topk} share={share} causal={causal}", flush=True)
+    g = torch.Generator().manual_seed(8300 + nb)
+    alpha = torch.tensor([2.0, 1.0, 0.0, -1.0])
+    pat = 0.5 * torch.randn((4, block, d), generator=g) + alpha[:, None, None]
+    cls = (torch.arange(nb) * 7) % 4          # classes interleaved over the 64-block slices
+    k = pat[cls].reshape(1, 1, N, d).repeat(1, Hkv, 1, 1).to(torch.bfloat16).contiguous()
+    q = (torch.randn((1, H, N, d), generator=g) + 1.0).to(torch.bfloat16).contiguous()
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    rp, col = oracle.meanpool_select(to64(q), to64(k), scale, block, causal, topk, share)
+    mask = lib.select_meanpool(q.cuda(), k.cuda(), block, topk, causal=causal, scale=scale, share_groups=share)
+    torch.cuda.synchronize()
+    assert np.array_equal(mask._dev[0].cpu().numpy(), rp)
+    assert np.array_equal(mask._dev[1].cpu().numpy(), col)
