@@ -1,0 +1,76 @@
+"""The measurement script's contract, on the CPU: one GPU only, no silent
+run without a GPU, the CPU baseline is the oracle's own record, and stored HBM
+byte counts are used only for the kernel source they were taken on."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import bench
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                          timeout=300, cwd=ROOT)
+
+
+@pytest.mark.parametrize("n", ["2", "8", "0"])
+def test_more_or_fewer_than_one_gpu_is_refused(n):
+    r = _run("--gpus", n)
+    assert r.returncode == 2 and r.stdout == ""
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the refusal on a machine without a GPU")
+def test_no_gpu_is_an_error_not_a_fallback():
+    r = _run("--steps", "1", "--warmup", "0", "--no-cpu-baseline")
+    assert r.returncode == 1 and r.stdout == ""
+    assert "needs a ROCm GPU" in r.stderr
+
+
+def test_unknown_workload_is_refused():
+    r = _run("--workload", "no-such-workload")
+    assert r.returncode == 2 and "invalid choice" in r.stderr
+
+
+def test_allowed_pairs_closed_forms():
+    c3 = workloads.CONFIGS["dense-h32-n8192-d128"]
+    assert bench.allowed_pairs_dense(c3) == 32 * 8192 * 8192
+    c2 = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
+    assert bench.allowed_pairs_dense(c2) == 4 * 16 * 2048 * 2049 // 2
+
+
+def test_cpu_baseline_is_the_oracle_on_whole_heads():
+    cfg = workloads.CONFIGS["dense-f32-h1-n256-d64"]
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    rec = bench.cpu_baseline(cfg, q, k, v, budget_s=0.0)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
+    assert rec["value"] > 0 and rec["cores"] >= 1
+    assert rec["sample"].startswith(f"1 of {cfg.B * cfg.H} (batch, head) pairs of {cfg.name}")
+
+
+def test_stored_traffic_is_used_only_for_the_same_kernel_source(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "fwd_{workload}_traffic.json"))
+    assert bench.read_traffic("w") is None                   # nothing stored
+    rec = {"kernel_source_sha256": bench.kernel_source_hash(), "traffic_bytes_per_launch": 12345}
+    (tmp_path / "fwd_w_traffic.json").write_text(json.dumps(rec))
+    assert bench.read_traffic("w") == 12345
+    rec["kernel_source_sha256"] = "0" * 64                    # taken on another version of the kernel
+    (tmp_path / "fwd_w_traffic.json").write_text(json.dumps(rec))
+    assert bench.read_traffic("w") is None
+
+
+def test_committed_traffic_records_name_their_workloads():
+    prof = os.path.join(ROOT, "profiles")
+    for name in os.listdir(prof):
+        if name.endswith("_traffic.json"):
+            rec = json.load(open(os.path.join(prof, name)))
+            w = name[len("fwd_bf16_"):-len("_traffic.json")]
+            assert w in workloads.CONFIGS, name
+            assert rec["traffic_bytes_per_launch"] > 0 and len(rec["kernel_source_sha256"]) == 64
