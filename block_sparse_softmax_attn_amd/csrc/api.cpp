@@ -160,6 +160,7 @@ extern "C" int attn_prepare_v(const void* v, int64_t B, int64_t H, int64_t N, in
     const int64_t need = attn_prepared_v_bytes(B, H, N, d, dtype);
     if (need < 0) return (d != 64 && d != 128) ? ATTN_EUNSUPPORTED : ATTN_EINVAL;
     if (!aligned16(v)) return ATTN_EINVAL;
+    if (B * H > 65535) return ATTN_EUNSUPPORTED;   // the transpose launch puts the heads on the grid's rows
     const int st = check_vt(vt, vt_bytes_given, B, H, N, d);
     if (st != ATTN_OK) return st;
     bsattn::FwdArgs a{};

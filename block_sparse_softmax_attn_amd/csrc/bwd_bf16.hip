@@ -136,13 +136,13 @@ __device__ void split_plan(const BwdArgs& a, int nkt, int64_t items) {
 // stats[bh][blk][0..63]   = LSE_i * log2 e  (+inf: row without keys, or i >= N)
 // stats[bh][blk][64..127] = D_i = dO_i . O_i (0 for i >= N)
 // PLAN: column nblk + 1 of the grid holds the split-plan workgroup (row 0) and
-// nothing else.
+// nothing else.  Grid rows stride over the heads (the grid's second dimension
+// is capped below B*H on large batches).
 template <int D, bool PLAN>
 __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a, int nblk, int nkt, int64_t items) {
     const int blk = blockIdx.x;
-    const int64_t bh = blockIdx.y;
     if (PLAN && blk == nblk + 1) {
-        if (bh == 0) split_plan(a, nkt, items);
+        if (blockIdx.y == 0) split_plan(a, nkt, items);
         return;
     }
     const __bf16* __restrict__ o = static_cast<const __bf16*>(a.o);
@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a, int nblk, int
     const int N = a.N;
     const int r = threadIdx.x >> 2, part = threadIdx.x & 3;
     const int i = blk * BT + r;
+    for (int64_t bh = blockIdx.y; bh < a.BH; bh += gridDim.y) {
     float acc = 0.f;
     if (i < N) {
         const __bf16* orow = o + (bh * N + i) * (int64_t)D;
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(256) void bwd_stats_kernel(BwdArgs a, int nblk, int
         }
         st[r] = l2;
         st[64 + r] = acc;
+    }
     }
 }
 
@@ -994,11 +996,12 @@ hipError_t launch_d(const BwdArgs& a, Mode mode, hipStream_t stream) {
     // grid column whose row 0 computes it)
     const int nkt_sparse = mode == Mode::kSparse ? (a.N + a.block - 1) / a.block : 0;
     const int64_t items = (int64_t)nkt_sparse * (a.BH / (a.H / a.Hkv));
+    const unsigned rows = (unsigned)(a.BH < 65535 ? a.BH : 65535);   // grid rows stride over the heads
     if (mode == Mode::kSparse)
-        hipLaunchKernelGGL((bwd_stats_kernel<D, true>), dim3((unsigned)(nblk + 2), (unsigned)a.BH), dim3(256), 0,
+        hipLaunchKernelGGL((bwd_stats_kernel<D, true>), dim3((unsigned)(nblk + 2), rows), dim3(256), 0,
                            stream, a, nblk, nkt_sparse, items);
     else
-        hipLaunchKernelGGL((bwd_stats_kernel<D, false>), dim3((unsigned)(nblk + 1), (unsigned)a.BH), dim3(256), 0,
+        hipLaunchKernelGGL((bwd_stats_kernel<D, false>), dim3((unsigned)(nblk + 1), rows), dim3(256), 0,
                            stream, a, nblk, 0, (int64_t)0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

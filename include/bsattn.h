@@ -159,8 +159,9 @@ int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, f
  *   each 16-key group, keys >= N zero).
  *   v : device [B,H,N,d] bf16.  vt : device, vt_bytes >=
  *   attn_prepared_v_bytes(...), 16-byte aligned, must not overlap v.
- *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype other than ATTN_BF16, d),
- *   ATTN_ECAPACITY, ATTN_EHIP.
+ *   Errors: ATTN_EINVAL, ATTN_EUNSUPPORTED (dtype other than ATTN_BF16, d,
+ *   or B*H > 65535: the transpose takes one grid row per head), ATTN_ECAPACITY,
+ *   ATTN_EHIP.
  *
  * attn_fwd_prepared / attn_fwd_blocksparse_prepared - attn_fwd /
  *   attn_fwd_blocksparse without the V argument: V^T is read from `vt`, which

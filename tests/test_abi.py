@@ -94,6 +94,9 @@ def test_prepared_entry_points_reject_bad_arguments(m):
     assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 1, FAKE, 100, None) == -3
     assert lib.attn_prepare_v(FAKE, 1, 2, 100, 64, 1, FAKE + 4, 1 << 20, None) == -1
     assert lib.attn_prepare_v(FAKE, 0, 2, 100, 64, 1, FAKE, 1 << 20, None) == -1
+    # one transpose grid row per head: B*H above 65535 is refused before the buffer check
+    assert lib.attn_prepare_v(FAKE, 2, 32768, 100, 64, 1, FAKE, 100, None) == -2
+    assert lib.attn_prepare_v(FAKE, 3, 21845, 100, 64, 1, FAKE, 100, None) == -3
     # prepared forwards: bf16 only, V^T buffer required
     assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 0, f, 0, FAKE, 1 << 20, None) == -2
     assert lib.attn_fwd_prepared(FAKE, FAKE, FAKE, FAKE, 1, 2, 100, 64, 1, f, 0, None, 1 << 20, None) == -1

@@ -101,3 +101,31 @@ def test_causal_backward_past_4_gib(lib, big):
         for name, got, ref, bd in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, bounds):
             compare_grad(to64(_head(got, h))[0, 0], ref, bd, f"large causal backward head {h} {name}")
     del o, lse, dq, dk, dv
+
+
+def test_backward_with_more_heads_than_grid_rows(lib):
+    # 70 000 heads: the statistics launch caps its grid rows at 65535 and
+    # strides over the heads, so the last heads take the second pass
+    Bs, Hs, Ns, Ds = 2, 35000, 64, 64
+    print(f"case backward B{Bs} H{Hs} N{Ns} d{Ds}", flush=True)
+    scale = float(np.float32(1.0 / math.sqrt(Ds)))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9102)
+    q, k, v, do = (torch.randn((Bs, Hs, Ns, Ds), generator=g, device="cuda", dtype=torch.bfloat16) for _ in range(4))
+    o, lse = lib.attn_fwd(q, k, v, scale=scale, causal=False)
+    heads = [(0, 0), (1, 30534), (1, Hs - 1)]   # flat heads 0, 65534, 69999
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        o_ex, lse_ex = oracle.attn_fwd(q[sl].cpu(), k[sl].cpu(), v[sl].cpu(), scale, False)
+        o[sl] = torch.from_numpy(o_ex).to(torch.bfloat16).cuda()
+        lse[sl] = torch.from_numpy(lse_ex).to(torch.float32).cuda()
+    dq, dk, dv = lib.attn_bwd(q, k, v, o, lse, do, scale=scale, causal=False)
+    torch.cuda.synchronize()
+    allowed = lambda rows: A.token_mask_dense(Ns, False, rows)
+    for b, h in heads:
+        q64, k64, v64, do64, o64 = (to64(t[b, h]) for t in (q, k, v, do, o))
+        l64 = to64(lse[b, h])
+        refs = oracle.attention_head_bwd(q64, k64, v64, do64, scale, allowed, o=o64, lse=l64)
+        bounds = bwd_bounds_head(q64, k64, v64, do64, scale, allowed, o64, l64)
+        for name, got, ref, bd in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, bounds):
+            compare_grad(to64(got[b, h]), ref, bd, f"backward 70000 heads ({b},{h}) {name}")
