@@ -40,10 +40,10 @@ def test_unknown_workload_is_refused():
 
 
 def test_allowed_pairs_closed_forms():
-    c3 = workloads.CONFIGS["dense-h32-n8192-d128"]
-    assert bench.allowed_pairs_dense(c3) == 32 * 8192 * 8192
-    c2 = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
-    assert bench.allowed_pairs_dense(c2) == 4 * 16 * 2048 * 2049 // 2
+    dense = workloads.CONFIGS["dense-h32-n8192-d128"]
+    assert bench.allowed_pairs_dense(dense) == 32 * 8192 * 8192
+    causal = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
+    assert bench.allowed_pairs_dense(causal) == 4 * 16 * 2048 * 2049 // 2
 
 
 def test_cpu_baseline_is_the_oracle_on_whole_heads():
