@@ -26,9 +26,18 @@
 //     NSTAGE tiles in flight, 16-byte chunks XOR-swizzled per row so the
 //     fragment reads are bank-conflict free.
 //   * Logits are handled in base-2 units (scale * log2 e folded into one FMA
-//     before v_exp_f32).  The running max is only raised when a row's new max
-//     exceeds it by more than 8 (a factor 256): exact, since A and l share the
-//     stale max, and it removes almost every rescale of the accumulator.
+//     before v_exp_f32).  The reference value m of a row (the running max of
+//     the pages' update) is not recomputed tile by tile: the exponentials of a
+//     tile are taken against the current m and checked afterwards.  If every
+//     lane's sum over the tile is finite and at most 2^64, no exponential can
+//     have overflowed and the tile is folded in as is -- exact in real
+//     arithmetic for any m, since A and l share it.  Otherwise, and while a row
+//     has no m yet (its first tile), the tile's row max raises m, the state is
+//     rescaled by exp2(m_old - m), and the tile's exponentials are recomputed.
+//     The common path thus has no per-tile max reduction (a serial chain of
+//     dependent vector operations) and almost never rescales the accumulator.
+//   * The K fragments of the score product are read from LDS four MFMAs ahead
+//     of their use, so the matrix core does not wait for each read.
 //   * Causal: key tiles wholly in the future are never visited, a wave skips
 //     the tiles that lie past all of its rows, and only tiles that cross the
 //     diagonal get the element mask.  Block-sparse: the tile loop runs over the
@@ -44,7 +53,8 @@ namespace {
 
 constexpr int kBN = 64;                // keys per tile step (32 for 64-key sparse blocks at d = 128)
 constexpr int kVtKeys = 64;            // keys per workgroup of the V^T pass
-constexpr float kSlack = 8.0f;         // lazy-rescale headroom, base-2 units
+constexpr float kSumMax = 0x1p64f;     // largest per-lane tile sum folded in without a rescale
+constexpr int kKAhead = 4;             // K fragment reads in flight ahead of their MFMAs
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Where the V operand of a tile comes from:
@@ -270,7 +280,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int i = 0; i < D / 32; ++i) oacc[i] = f32x16{};
-    float m_run = -__builtin_inff();   // running max, base-2 units (possibly stale by < kSlack)
+    float m_run = -__builtin_inff();   // reference value m of the row, base-2 units (see the file comment)
     float ell = 0.f;                   // this lane's share of the denominator
     const float sl2 = a.scale_log2;
 
@@ -288,15 +298,28 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             // ---- S^T: lane (l32, hi) gets, in s[c][v], the score of query l32
             // and key kb0 + 32c + 8(v>>2) + 4hi + (v&3) ----
             f32x16 s[BN / 32];
+            constexpr int NF = (BN / 32) * (D / 16);   // fragment f: 32-key block f / (D/16), chunk f % (D/16)
+            auto kfrag = [&](int f) {
+                return *reinterpret_cast<const bf16x8*>(bK + koff[f % (D / 16)] + 32 * (f / (D / 16)) * (2 * D));
+            };
+            bf16x8 kfr[NF];
 #pragma unroll
-            for (int c = 0; c < BN / 32; ++c) {
-                s[c] = f32x16{};
+            for (int f = 0; f < kKAhead; ++f) kfr[f] = kfrag(f);
 #pragma unroll
-                for (int k = 0; k < D / 16; ++k) {
-                    const bf16x8 kf = *reinterpret_cast<const bf16x8*>(bK + koff[k] + 32 * c * (2 * D));
-                    s[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[k], s[c], 0, 0, 0);
-                }
+            for (int c = 0; c < BN / 32; ++c) s[c] = f32x16{};
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+                if (f + kKAhead < NF) kfr[f + kKAhead] = kfrag(f + kKAhead);
+                s[f / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[f], qf[f % (D / 16)], s[f / (D / 16)], 0, 0, 0);
             }
+            // keep the reads kKAhead MFMAs ahead (DS reads: 0x100, MFMA: 0x008)
+            __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+#pragma unroll
+            for (int f = 0; f < NF - kKAhead; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
             if (t.masked) {
                 // key j is masked when j >= nlim or, causal, j > qdiag: one bound
                 // lim; element (c, v) holds j = kb0 + 4hi + (32c + 8(v>>2) + (v&3)),
@@ -310,37 +333,50 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                         s[c][v] = 32 * c + 8 * (v >> 2) + (v & 3) > r ? -__builtin_inff() : s[c][v];
             }
             // ---- online softmax ----
-            float mx = -__builtin_inff();
-#pragma unroll
-            for (int c = 0; c < BN / 32; ++c)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[c][v]);
-            mx = xor32_max(mx);
-            const float mt = mx * sl2;
-            const bool upd = mt > m_run + kSlack;
-            if (__builtin_amdgcn_ballot_w64(upd) != 0) {
-                const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
-                m_run = upd ? mt : m_run;
-                ell *= alpha;
-#pragma unroll
-                for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
-            }
-            const float mu = (m_run == -__builtin_inff()) ? 0.f : m_run;
             // P rounds to bf16 for the PV product; the denominator sums the fp32
             // values so LSE keeps fp32 accuracy even for rows with few keys.
             bf16x8 pf[BN / 16];
             float ts[8];
+            auto exps = [&](float mu) {
 #pragma unroll
-            for (int g = 0; g < BN / 16; ++g) {
-                const int c = g >> 1, t8 = (g & 1) * 8;
+                for (int g = 0; g < BN / 16; ++g) {
+                    const int c = g >> 1, t8 = (g & 1) * 8;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][t8 + i], sl2, -mu));
-                    ts[i] = g == 0 ? p : ts[i] + p;
-                    pf[g][i] = (__bf16)p;
+                    for (int i = 0; i < 8; ++i) {
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[c][t8 + i], sl2, -mu));
+                        ts[i] = g == 0 ? p : ts[i] + p;
+                        pf[g][i] = (__bf16)p;
+                    }
                 }
+                return ((ts[0] + ts[1]) + (ts[2] + ts[3])) + ((ts[4] + ts[5]) + (ts[6] + ts[7]));
+            };
+            // Common path: the exponentials against the row's current m,
+            // checked afterwards (see the file comment).
+            float tsum = 0.f;
+            bool redo = __builtin_amdgcn_ballot_w64(m_run == -__builtin_inff()) != 0;
+            if (!redo) {
+                tsum = exps(m_run);
+                redo = __builtin_amdgcn_ballot_w64(!(tsum <= kSumMax)) != 0;
             }
-            ell += ((ts[0] + ts[1]) + (ts[2] + ts[3])) + ((ts[4] + ts[5]) + (ts[6] + ts[7]));
+            if (redo) {   // raise m to the tile's row max, rescale, recompute
+                float mx = -__builtin_inff();
+#pragma unroll
+                for (int c = 0; c < BN / 32; ++c)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[c][v]);
+                mx = xor32_max(mx);
+                const float mt = mx * sl2;
+                const bool upd = mt > m_run;
+                if (__builtin_amdgcn_ballot_w64(upd) != 0) {
+                    const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - mt) : 1.0f;
+                    m_run = upd ? mt : m_run;
+                    ell *= alpha;
+#pragma unroll
+                    for (int i = 0; i < D / 32; ++i) oacc[i] *= alpha;
+                }
+                tsum = exps((m_run == -__builtin_inff()) ? 0.f : m_run);
+            }
+            ell += tsum;
             // ---- O^T += V^T P^T ----
 #pragma unroll
             for (int g = 0; g < BN / 16; ++g)

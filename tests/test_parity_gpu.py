@@ -220,9 +220,10 @@ def test_outputs_not_written_past_n(lib):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_growing_logits_rescale_every_tile(lib, d, causal):
-    # key j = (j + 1) * k0: for queries with q . k0 > 0 the logits grow along the keys, so the
-    # running max rises by far more than the lazy-rescale slack on every tile and the rescale
-    # runs each time; queries with q . k0 < 0 keep their first tile's max
+    # key j = (j + 1) * k0: for queries with q . k0 > 0 the logits grow along the keys, so on
+    # most tiles some exponential against the row's current reference value passes 2^64, the
+    # tile's sum check fails, and the kernel raises the reference to the tile's max, rescales
+    # and recomputes the tile; queries with q . k0 < 0 keep their first tile's reference
     B, H, N = 1, 2, 777
     print(f"case growing logits d={d} causal={causal}", flush=True)
     q, k, v = inputs(B, H, N, d, "bf16", 91 + d)
