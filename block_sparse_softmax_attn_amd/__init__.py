@@ -30,15 +30,15 @@ from typing import Optional
 
 import numpy as np
 
-from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN_FLAG_PARTIAL, ATTN_OK,
-                   AttnError, LIB_PATH, check, get as _get_lib, status_string)
+from ._lib import (ATTN_BF16, ATTN_ECAPACITY, ATTN_F32, ATTN_FLAG_DIAGONAL, ATTN_FLAG_PARTIAL,
+                   ATTN_NOALLOC_SCRATCH_BYTES, ATTN_OK, AttnError, LIB_PATH, check, get as _get_lib, status_string)
 
 __all__ = ["attn_fwd", "attn_fwd_blocksparse", "blockmask_build", "prepared_v_bytes", "prepare_v", "attn_fwd_prepared",
-           "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_blocksparse", "bwd_workspace_bytes",
+           "attn_fwd_blocksparse_prepared", "attn_bwd", "attn_bwd_noalloc", "attn_bwd_blocksparse", "bwd_workspace_bytes",
            "bwd_blocksparse_workspace_bytes",
            "attn_fwd_splitkv", "attn_fwd_block", "attn_merge", "select_meanpool", "DeviceBlockMask",
            "BlockMask", "AttnError", "LIB_PATH",
-           "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL"]
+           "status_string", "ATTN_FLAG_DIAGONAL", "ATTN_FLAG_PARTIAL", "ATTN_NOALLOC_SCRATCH_BYTES"]
 
 
 def _dtype_code(t) -> int:
@@ -299,7 +299,8 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int, Hkv: Optional[int] = Non
 
 def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace, need=None, alloc=None):
     """Checked gradient outputs and workspace: a given workspace needs ``need``
-    bytes; one is allocated (``alloc`` bytes, default ``need``) when none is given."""
+    bytes; one is allocated (``alloc`` bytes, default ``need``) when none is
+    given, except for ``need == 0``, where no workspace is returned."""
     import torch
     _check_qkv(q, k, v)
     if q.dtype != torch.bfloat16:
@@ -320,6 +321,8 @@ def _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace, need=None, alloc=
         need = int(_get_lib().attn_bwd_gqa_workspace_bytes(B, H, k.shape[1], N, d, ATTN_BF16))
     if need < 0:
         raise ValueError("sizes not supported by the backward")
+    if workspace is None and need == 0 and not alloc:
+        return grads, None, 0   # the call takes no workspace
     if workspace is None:
         workspace = torch.empty(max(need, alloc or 0), dtype=torch.uint8, device=q.device)
     if workspace.device != q.device or not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < need:
@@ -345,6 +348,25 @@ def attn_bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool 
                                 dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, ATTN_BF16,
                                 ctypes.c_float(scale), int(bool(causal)), ws.data_ptr(), ws_bytes, _stream(q.device))
     check("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = False,
+                     dq=None, dk=None, dv=None):
+    """attn_bwd without a workspace: the library keeps the row statistics in
+    its own fixed per-GPU array (for callers that cannot allocate; pass dq, dk,
+    dv to allocate nothing here either).  Calls that overlap on one GPU race."""
+    import torch
+    B, H, N, d = q.shape
+    if k.shape[1] != H:
+        raise ValueError("attn_bwd_noalloc takes as many key/value heads as query heads")
+    (dq, dk, dv), _, _ = _bwd_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace=None, need=0)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        st = _get_lib().attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                         dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                                         ATTN_BF16, ctypes.c_float(scale), int(bool(causal)), _stream(q.device))
+    check("attn_bwd_noalloc", st)
     return dq, dk, dv
 
 

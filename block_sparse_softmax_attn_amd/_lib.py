@@ -20,6 +20,7 @@ ATTN_F32 = 0
 ATTN_BF16 = 1
 ATTN_FLAG_DIAGONAL = 1
 ATTN_FLAG_PARTIAL = 2
+ATTN_NOALLOC_SCRATCH_BYTES = 32 << 20   # the library's fixed scratch for attn_bwd_noalloc, per GPU
 
 EXPORTED = ("attn_status_string", "attn_prepared_v_bytes", "attn_fwd", "attn_blockmask_build",
             "attn_fwd_blocksparse", "attn_prepare_v", "attn_fwd_prepared", "attn_fwd_blocksparse_prepared",
@@ -27,7 +28,8 @@ EXPORTED = ("attn_status_string", "attn_prepared_v_bytes", "attn_fwd", "attn_blo
             "attn_bwd_blocksparse_workspace_bytes",
             "attn_fwd_splitkv_workspace_bytes", "attn_fwd_splitkv", "attn_fwd_block", "attn_merge", "attn_fwd_gqa", "attn_fwd_blocksparse_gqa",
             "attn_bwd_gqa_workspace_bytes", "attn_bwd_gqa", "attn_bwd_blocksparse_gqa",
-            "attn_select_meanpool_nnz", "attn_select_meanpool_workspace_bytes", "attn_select_meanpool")
+            "attn_select_meanpool_nnz", "attn_select_meanpool_workspace_bytes", "attn_select_meanpool",
+            "attn_bwd_noalloc")
 
 
 class AttnError(RuntimeError):
@@ -64,6 +66,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.attn_bwd.restype = i32
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp, i64, vp]
+    lib.attn_bwd_noalloc.restype = i32
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, f32, i32, vp]
     lib.attn_blockmask_transpose.restype = i32
     lib.attn_blockmask_transpose.argtypes = [vp, vp, i64, i64, i64, vp, vp, i64]
     lib.attn_bwd_blocksparse_workspace_bytes.restype = i64

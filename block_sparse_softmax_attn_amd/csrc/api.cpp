@@ -2,6 +2,7 @@
 // Every check happens before any launch; nothing here allocates device memory.
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "bsattn.h"
 #include "fwd_common.h"
@@ -317,6 +318,58 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
                         hipStream_t stream) {
     return bwd_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, dtype, scale, causal, workspace,
                      workspace_bytes_given, stream);
+}
+
+// ---- the backward without a caller workspace ----
+//
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc): attn_bwd_noalloc keeps the row
+// statistics in a fixed array of the library's code object instead of a
+// caller workspace.  Every GPU the library runs on holds its own copy of the
+// array until the process ends; its device address is looked up once per
+// device and kept.  In host code the array's name is only a host-side stand-in
+// for the symbol, never a device address: host code uses scratch_base().
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices] = {};
+hipError_t g_scratch_err[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on error).
+void* scratch_base() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N,
+                                int64_t d, int dtype, float scale, int causal, hipStream_t stream) {
+    // every argument check of attn_bwd, with the scratch standing in for the
+    // workspace; sizes whose statistics exceed it are refused before any HIP call
+    const int64_t need = bwd_ws(B, H, H, N, d, dtype);
+    if (need > ATTN_NOALLOC_SCRATCH_BYTES) {
+        const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, dtype, scale, causal,
+                                 reinterpret_cast<void*>(uintptr_t(256)), need);
+        return st != ATTN_OK ? st : ATTN_ECAPACITY;
+    }
+    const int st = check_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, dtype, scale, causal,
+                             reinterpret_cast<void*>(uintptr_t(256)), ATTN_NOALLOC_SCRATCH_BYTES);
+    if (st != ATTN_OK) return st;
+    void* ws = scratch_base();
+    if (ws == nullptr) return ATTN_EHIP;
+    return bwd_dense(q, k, v, o, lse, dout, dq, dk, dv, B, H, H, N, d, dtype, scale, causal, ws,
+                     ATTN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 extern "C" int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -228,6 +228,33 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int causal, void* workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attn_bwd_noalloc - attn_bwd for callers that cannot allocate device memory
+ *   (code under HIP graph capture, tight serving or training loops, harnesses
+ *   that forbid hipMalloc): the same gradients, bitwise, with no workspace
+ *   argument.  The row statistics go to a fixed array of
+ *   ATTN_NOALLOC_SCRATCH_BYTES bytes inside the library, one copy per GPU the
+ *   library runs on, held until the process ends; the call itself allocates
+ *   nothing (no hipMalloc, no allocating library routine).
+ *   Arguments, layouts and results as for attn_bwd (dense or causal,
+ *   ATTN_BF16); the caller still owns q, k, v, o, lse, dout, dq, dk, dv.
+ *   Limit: attn_bwd_workspace_bytes(B, H, N, d, dtype) must not exceed
+ *   ATTN_NOALLOC_SCRATCH_BYTES (B*H*(2*ceil(N/128)+1)*512 bytes, e.g. B*H*N
+ *   up to about 4.1M rows at N = 8192); larger sizes return ATTN_ECAPACITY
+ *   before any launch.
+ *   Calls on one GPU share its array and each overwrites it: calls that can
+ *   overlap on one GPU (different streams, host threads) race and must be
+ *   ordered by the caller.  Nothing in the array needs clearing between calls
+ *   (the first kernel of a call writes every statistic the later ones read).
+ *   Errors: as for attn_bwd; ATTN_EHIP also when the array's device address
+ *   cannot be obtained.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES (32LL << 20)
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t N, int64_t d,
+                     int dtype, float scale, int causal, hipStream_t stream);
+
+/*
  * attn_blockmask_transpose - HOST-side transpose of block-sparse metadata: for
  *   each key block, the query blocks whose lists name it, in increasing order
  *   (the dK/dV pass of the backward owns a key block and visits exactly these).
