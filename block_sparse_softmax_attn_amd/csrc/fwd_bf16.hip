@@ -214,6 +214,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // bytes [1024 g + 16 i, +16) of the tile, i.e. row r, physical chunk p,
     // with logical chunk swz(r, p) of that row.
     int k_row[G::K_PER_W], k_col[G::K_PER_W], v_off[G::V_PER_W > 0 ? G::V_PER_W : 1];
+    int64_t vt_off[VTR ? 1 : G::V_PER_W];   // V^T source offsets: dimension row d * npad can pass 2^31
     int v_row[VTR ? G::V_PER_W : 1];
 #pragma unroll
     for (int i = 0; i < G::K_PER_W; ++i) {
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             v_off[i] = rt_swz<D>(r, p) * 8;
         } else {
             const int d = byte / (2 * BN), p = (byte % (2 * BN)) / 16;
-            v_off[i] = d * a.npad + v_swz<BN>(d, p) * 8;
+            vt_off[i] = (int64_t)d * a.npad + v_swz<BN>(d, p) * 8;
         }
     }
     // Row-major K and V tiles: byte offsets inside the tile, fixed for the
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         if constexpr (!VTR) {
 #pragma unroll
             for (int i = 0; i < G::V_PER_W; ++i)
-                dma16(Vth + (int64_t)kb0 + v_off[i], vbuf[u] + (w * G::V_PER_W + i) * 1024);
+                dma16(Vth + kb0 + vt_off[i], vbuf[u] + (w * G::V_PER_W + i) * 1024);
         }
     };
     f32x16 oacc[D / 32];

@@ -24,9 +24,11 @@
 namespace bsattn {
 namespace {
 
+// o and lse may be exactly part 0 of o_part and lse_part (an in-place merge),
+// so the part pointers are not declared __restrict__.
 template <int D, bool OUT_BF16>
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_part,
-                                                    const float* __restrict__ lse_part, int nsplit, int64_t rows,
+__global__ __launch_bounds__(256) void merge_kernel(const float* o_part,
+                                                    const float* lse_part, int nsplit, int64_t rows,
                                                     void* o, float* lse) {
     constexpr int TPR = D / 4;                    // lanes per row
     constexpr int RPB = 256 / TPR;                // rows per workgroup

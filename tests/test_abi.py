@@ -114,6 +114,8 @@ def test_prepared_v_bytes(m):
     assert lib.attn_prepared_v_bytes(1, 32, 8192, 128, 1) == 32 * 128 * 8192 * 2
     assert lib.attn_prepared_v_bytes(1, 16, 16300, 128, 1) == 16 * 128 * 16384 * 2
     assert lib.attn_prepared_v_bytes(2, 3, 1, 64, 1) == 6 * 64 * 128 * 2
+    # one long head: dimension rows of V^T start past 2^31 elements (the kernel's offsets are 64-bit)
+    assert lib.attn_prepared_v_bytes(1, 1, 20 * 2 ** 20, 128, 1) == 128 * 20 * 2 ** 20 * 2
     assert lib.attn_prepared_v_bytes(1, 1, 256, 64, 0) == -1     # bf16 only
     assert lib.attn_prepared_v_bytes(1, 1, 256, 96, 1) == -1
     assert lib.attn_prepared_v_bytes(0, 1, 256, 64, 1) == -1

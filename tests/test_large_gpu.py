@@ -129,3 +129,39 @@ def test_backward_with_more_heads_than_grid_rows(lib):
         bounds = bwd_bounds_head(q64, k64, v64, do64, scale, allowed, o64, l64)
         for name, got, ref, bd in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs, bounds):
             compare_grad(to64(got[b, h]), ref, bd, f"backward 70000 heads ({b},{h}) {name}")
+
+
+def test_prepared_v_long_head_past_int32_dimension_offsets(lib):
+    """One head of N = 20 971 520 keys, d = 128: in the V^T buffer, dimension
+    row c starts at c * npad elements, past 2^31 for c >= 103, so the tile
+    loads of the prepared-V forward need 64-bit offsets.  The pattern keeps
+    only each query block's own (diagonal) block, so every query block reads
+    all 128 V^T rows of its block and its result is the dense causal
+    attention of that 128-row slice (checked against the oracle on three
+    blocks)."""
+    n_big, d, block = 20 * (1 << 20), 128, 128
+    assert 103 * n_big > (1 << 31)
+    per = n_big * d * 2
+    free, _ = torch.cuda.mem_get_info()
+    if free < 6 * per + (8 << 30):
+        pytest.skip(f"needs {(6 * per + (8 << 30)) / 1e9:.0f} GB of free GPU memory")
+    print(f"case prepared V long head N{n_big} d{d}", flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9200)
+    q, k, v = (torch.randn((1, 1, n_big, d), generator=g, device="cuda", dtype=torch.bfloat16) for _ in range(3))
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    nb = n_big // block
+    rp = np.arange(nb + 1, dtype=np.int32)
+    col = np.arange(nb, dtype=np.int32)
+    mask = lib.blockmask_build(rp, col, 1, n_big, block, True)
+    vt = torch.empty(lib.prepared_v_bytes(1, 1, n_big, d), dtype=torch.uint8, device="cuda")
+    lib.prepare_v(v, vt)
+    o, lse = lib.attn_fwd_blocksparse_prepared(q, k, vt, mask, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for b in (0, nb // 2, nb - 1):
+        sl = slice(b * block, (b + 1) * block)
+        o_ref, lse_ref = oracle.attn_fwd(q[:, :, sl].cpu(), k[:, :, sl].cpu(), v[:, :, sl].cpu(), scale, True)
+        compare(to64(o[:, :, sl].cpu()).reshape(-1, d), to64(lse[:, :, sl].cpu()).reshape(-1),
+                o_ref.reshape(-1, d), lse_ref.reshape(-1), "bf16", f"prepared V long head, block {b}")
+    del q, k, v, vt, o, lse
+    torch.cuda.empty_cache()
