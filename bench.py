@@ -1,24 +1,35 @@
 """Throughput of the fused attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense-h32-n8192-d128]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dense-h32-n8192-d128] [--all]
 
-A step is one pass of the hot path over one batch of synthetic N(0,1) bf16
-input already resident in HBM: one attn_fwd (dense, causal) or
+A step is one pass of the hot path over one batch of synthetic N(0,1) input
+already resident in HBM: one attn_fwd (dense, causal) or
 attn_fwd_blocksparse call, i.e. host validation and the single launch of the
 fused kernel, which reads Q, K and V in place.  The default workload is the
 dense non-causal d=128 case (B=1 H=32 N=8192), the one the throughput target
-is stated on.  Prints ONE JSON line:
+is stated on.  Prints ONE JSON line (--all: one line per workload, the
+fp32 one included):
 
   value    allowed-pair TFLOP/s over the K timed steps (4*d flops per allowed
            query-key pair: the QK^T and PV contractions), wall clock between
            two device synchronisations;
-  roofline the fused kernel against the bf16 MFMA peak: achieved = flops per
-           launch / mean launch duration (HIP events on the launch stream);
-           traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE and
-           WRITE_SIZE counters (calibrated on a plain copy), read from
-           profiles/ and reported only while the kernel source is unchanged;
+  timing   the fused kernel's duration per launch (HIP events on the launch
+           stream): mean, median and min over the timed steps;
+  roofline the fused kernel against the MFMA peak of its dtype: achieved =
+           flops per launch / mean launch duration; traffic = HBM bytes per
+           launch from rocprofv3 FETCH_SIZE and WRITE_SIZE counters
+           (calibrated on a plain copy), read from profiles/ and reported only
+           while the kernel source is unchanged;
+  config   the workload; for causal and block-sparse runs also the executed
+           work in b x b tiles (b = 128) and its rate;
+  check    after the timed steps, max|dO| and max|dLSE| of the timed output
+           against the float64 oracle on seeded query rows of every head,
+           with the tolerances (bf16 1e-2 / 1e-3, fp32 1e-5); the script
+           exits with status 3 after printing if they are exceeded;
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same
-           workload (whole heads, about 10 s), on this host's cores.
+           workload (about 10 s: whole heads, or the sampled rows of the
+           long-context workload, with rows/s and a labelled extrapolation
+           to every row), on this host's cores.
 
 Other flags: --no-cpu-baseline, --no-gemm-ceiling (skip the library bf16 GEMM
 that measures the sustained matrix-core rate next to the published peak),
@@ -50,6 +61,9 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402  (seeded input recipes: shapes, seeds, block lists)
 
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz, dense
+PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 matrix peak, dense
+TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-5, 1e-5)}   # max|dO|, max|dLSE| against the oracle
+CHECK_ROWS = 64              # seeded query rows per head the bench output is checked on
 # the forward kernel's source and the headers it includes: the recorded counters stay valid
 # only while none of them changes
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_softmax_attn_amd", "csrc", f)
@@ -81,34 +95,94 @@ def read_traffic(workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def host_cores() -> dict:
+    """The host cores this process may run on, and the BLAS threads numpy uses."""
+    from threadpoolctl import threadpool_info
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"cores": len(os.sched_getaffinity(0)),
+            "blas_threads": int(max([p.get("num_threads", 1) for p in blas] or [1])),
+            "blas": ",".join(sorted({str(p.get("internal_api", "?")) for p in blas})) or "none"}
+
+
 def cpu_baseline(cfg, q, k, v, budget_s: float = 10.0):
-    """The oracle as it stands, on whole heads of the same inputs, until the
-    time budget is spent (at least one head)."""
+    """The oracle as it stands on a bounded sample of the same inputs: whole
+    heads until the time budget is spent (at least one head), or, for the
+    workloads checked on sampled rows, the sampled rows of each head."""
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
 
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    done_heads, flops, t_total = 0, 0, 0.0
+    hc = host_cores()
+    done_heads, flops, rows_done, t_total = 0, 0, 0, 0.0
     H = cfg.H
     for h in range(H):
         qh, kh, vh = (t[:, h:h + 1].to("cpu") for t in (q, k, v))
+        rows = workloads.config_rows(cfg, h)
         t0 = time.perf_counter()
-        oracle.attn_fwd(qh, kh, vh, cfg.scale, cfg.causal)
+        oracle.attn_fwd(qh, kh, vh, cfg.scale, cfg.causal, rows=rows)
         t_total += time.perf_counter() - t0
         done_heads += 1
-        per_head = cfg.N * (cfg.N + 1) // 2 if cfg.causal else cfg.N * cfg.N
-        flops += 4 * cfg.d * per_head * cfg.B
+        r = np.arange(cfg.N) if rows is None else np.asarray(rows)
+        rows_done += len(r) * cfg.B
+        pairs = int(np.sum(r + 1)) if cfg.causal else len(r) * cfg.N
+        flops += 4 * cfg.d * pairs * cfg.B
         if t_total >= budget_s:
             break
-    return {
+    rec = {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(threads),
+        "cores": hc["cores"],
+        "blas_threads": hc["blas_threads"],
         "kind": "oracle",
-        "sample": f"{done_heads} of {cfg.B * H} (batch, head) pairs of {cfg.name}, every query row, "
-                  f"float64 numpy three-stage oracle, {t_total:.1f} s",
+        "rows_per_s": round(rows_done / t_total, 1),
     }
+    if cfg.sample_rows:
+        total_rows = cfg.B * cfg.H * cfg.N
+        rec["sample"] = (f"{cfg.sample_rows} sampled query rows of each of {done_heads} of {cfg.B * H} (batch, head) "
+                         f"pairs of {cfg.name} (every key of each row), float64 numpy three-stage oracle, "
+                         f"{t_total:.1f} s")
+        rec["extrapolated_all_rows_s"] = round(total_rows / (rows_done / t_total), 1)
+        rec["extrapolation"] = ("every row of every head at this row rate; rows later in a causal sequence "
+                                "have more keys, so this understates the full cost")
+    else:
+        rec["sample"] = (f"{done_heads} of {cfg.B * H} (batch, head) pairs of {cfg.name}, every query row, "
+                         f"float64 numpy three-stage oracle, {t_total:.1f} s")
+    return rec
+
+
+def oracle_check(cfg, q, k, v, o, lse, rows_per_head: int = CHECK_ROWS, mask_lists=None):
+    """max|dO| and max|dLSE| of a forward's output against the float64 oracle
+    on seeded query rows of every head (empty rows must be exactly O = 0 and
+    LSE = -inf; any NaN fails)."""
+    import numpy as np
+    import oracle
+
+    tol_o, tol_l = TOL[cfg.dtype]
+    worst_o = worst_l = 0.0
+    ok = True
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            rows = workloads.sample_rows(cfg.N, min(rows_per_head, cfg.N), 77 * 1000 + b * cfg.H + h)
+            qh, kh, vh = (t[b:b + 1, h:h + 1].to("cpu") for t in (q, k, v))
+            if mask_lists is None:
+                ro, rl = oracle.attn_fwd(qh, kh, vh, cfg.scale, cfg.causal, rows=rows)
+            else:
+                rp, col = mask_lists
+                ro, rl = oracle.attn_fwd_blocksparse(qh, kh, vh, cfg.scale, cfg.causal, cfg.block, rp, col, 1,
+                                                     rows=rows)
+            ro, rl = ro[0], rl[0]
+            go = o[b, h, rows].double().cpu().numpy()
+            gl = lse[b, h, rows].double().cpu().numpy()
+            live = np.isfinite(rl)
+            if np.isnan(go).any() or np.isnan(gl).any():
+                ok = False
+            if not np.array_equal(np.isfinite(gl), live) or not np.all(go[~live] == 0):
+                ok = False
+            if live.any():
+                worst_o = max(worst_o, float(np.abs(go[live] - ro[live]).max()))
+                worst_l = max(worst_l, float(np.abs(gl[live] - rl[live]).max()))
+    ok = ok and worst_o <= tol_o and worst_l <= tol_l
+    return {"rows_per_head": min(rows_per_head, cfg.N), "max_abs_dO": worst_o, "max_abs_dLSE": worst_l,
+            "tol_O": tol_o, "tol_LSE": tol_l, "ok": bool(ok), "reference": "float64 oracle, seeded rows"}
 
 
 def gemm_ceiling(n: int = 8192, reps: int = 20):
@@ -146,13 +220,133 @@ def copy_calibration(nbytes: int = 1 << 30):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "dispatches": 3}))
 
 
+def executed_tiles_128(cfg, mask=None) -> int:
+    """Executed work of a causal or block-sparse run in b x b tiles (b = 128;
+    the sparse pattern's own block): diagonal tiles count whole."""
+    if mask is not None:
+        return int(mask.executed_tile_pairs[0]) * cfg.B * cfg.H
+    nb = -(-cfg.N // 128)
+    return cfg.B * cfg.H * nb * (nb + 1) // 2
+
+
+def bench_fwd(args, cfg, dev, gemm=None):
+    """One workload's record: timed steps of the one-call forward, then the
+    oracle check of the timed output, then the CPU baseline."""
+    import torch
+    import block_sparse_softmax_attn_amd as attn
+
+    tdtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    q, k, v = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
+               .to(tdtype).contiguous() for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
+
+    # One step = one call of the one-call entry point: a single launch of the
+    # fused kernel, timed with HIP events on the launch stream.
+    mask_lists = None
+    if cfg.sparse:
+        rp, col = workloads.config_block_lists(cfg)
+        mask_lists = (rp, col)
+        t0 = time.perf_counter()
+        mask = attn.blockmask_build(rp, col, 1, cfg.N, cfg.block, cfg.causal)
+        build_ms = (time.perf_counter() - t0) * 1e3
+        pairs = int(mask.allowed_pairs[0]) * cfg.B * cfg.H
+        executed = executed_tiles_128(cfg, mask) * cfg.block * cfg.block
+        mask.to_device(dev)
+        fused = lambda: attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal,
+                                                  out=o, lse=lse)
+    else:
+        build_ms = None
+        pairs = allowed_pairs_dense(cfg)
+        executed = executed_tiles_128(cfg) * 128 * 128 if cfg.causal else None
+        fused = lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
+    flops = 4 * cfg.d * pairs
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fused()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    mean_launch_ms = sum(launch) / len(launch)
+    median_launch_ms = launch[len(launch) // 2] if len(launch) % 2 else 0.5 * (launch[len(launch) // 2 - 1] +
+                                                                              launch[len(launch) // 2])
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+
+    value = flops * args.steps / wall / 1e12
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "attention fwd TFLOP/s (allowed pairs) + % of bf16 MFMA peak, 1\u00d7MI355X",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": cfg.description,
+            "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "causal": cfg.causal,
+            "block_sparse": cfg.sparse, "scale": cfg.scale, "seed": cfg.seed,
+            "allowed_pairs": pairs, "flops_per_step": flops,
+            "flop_count": "4*d per allowed (query, key) pair",
+            "parallelism": "single GPU",
+        },
+        "timing": {"launch_ms_mean": round(mean_launch_ms, 5), "launch_ms_median": round(median_launch_ms, 5),
+                   "launch_ms_min": round(launch[0], 5), "launches": len(launch)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": read_traffic(cfg.name) if cfg.dtype == "bf16" else None,
+            "kernel": "fwd_bf16_kernel" if cfg.dtype == "bf16" else "fwd_f32_kernel",
+            "mean_launch_ms": round(mean_launch_ms, 5),
+        },
+    }
+    if cfg.dtype != "bf16":
+        rec["roofline"]["note"] = ("fp32 workload of 16.8 MFLOP: one small launch, latency-bound; "
+                                   "its time is reported for context, against the fp32 matrix peak")
+    if executed is not None:
+        rec["config"]["executed_tile_pairs_128"] = executed // (cfg.block * cfg.block if cfg.sparse else 128 * 128)
+        rec["config"]["executed_tile_flops_per_step"] = 4 * cfg.d * executed
+        rec["config"]["executed_tile_tflops"] = round(4 * cfg.d * executed * args.steps / wall / 1e12, 3)
+    if build_ms is not None:
+        rec["config"]["blockmask_build_ms_host"] = round(build_ms, 3)
+    if gemm is not None:
+        rec["roofline"]["measured_bf16_gemm_ceiling"] = gemm
+    rec["check"] = oracle_check(cfg, q, k, v, o, lse, mask_lists=mask_lists)
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v)
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="dense-h32-n8192-d128",
-                    choices=[k for k in workloads.CONFIGS if workloads.CONFIGS[k].dtype == "bf16"])
+    ap.add_argument("--workload", default="dense-h32-n8192-d128", choices=list(workloads.CONFIGS))
+    ap.add_argument("--all", action="store_true", help="one line per workload (every config)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm-ceiling", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
@@ -171,7 +365,7 @@ def main():
         return
 
     import torch
-    import block_sparse_softmax_attn_amd as attn
+    import block_sparse_softmax_attn_amd as attn  # noqa: F401  (fails loudly without the built library)
 
     if not torch.cuda.is_available():
         print("bench.py needs a ROCm GPU", file=sys.stderr)
@@ -179,6 +373,9 @@ def main():
     cfg = workloads.CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.which != "fwd" and cfg.dtype != "bf16":
+        print(f"--pass {args.which} takes a bf16 workload", file=sys.stderr)
+        sys.exit(2)
     if args.which == "bwd":
         bench_bwd(args, cfg, dev)
         return
@@ -188,100 +385,21 @@ def main():
     if args.which == "select":
         bench_select(args, cfg, dev)
         return
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(cfg.seed)
-    q, k, v = (torch.randn((cfg.B, cfg.H, cfg.N, cfg.d), generator=gen, device=dev, dtype=torch.float32)
-               .to(torch.bfloat16).contiguous() for _ in range(3))
-    o = torch.empty_like(q)
-    lse = torch.empty((cfg.B, cfg.H, cfg.N), device=dev, dtype=torch.float32)
-
-    # One step = one call of the one-call entry point: a single launch of the
-    # fused kernel, timed with HIP events on the launch stream.
-    if cfg.sparse:
-        rp, col = workloads.config_block_lists(cfg)
-        t0 = time.perf_counter()
-        mask = attn.blockmask_build(rp, col, 1, cfg.N, cfg.block, cfg.causal)
-        build_ms = (time.perf_counter() - t0) * 1e3
-        pairs = int(mask.allowed_pairs[0]) * cfg.B * cfg.H
-        executed = int(mask.executed_tile_pairs[0]) * cfg.B * cfg.H * cfg.block * cfg.block
-        mask.to_device(dev)
-        fused = lambda: attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal,
-                                                  out=o, lse=lse)
-    else:
-        build_ms = None
-        pairs = allowed_pairs_dense(cfg)
-        executed = None
-        fused = lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
-    flops = 4 * cfg.d * pairs
-
-    for _ in range(args.warmup):
-        fused()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        fused()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    mean_launch_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-
-    value = flops * args.steps / wall / 1e12
-    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
-    rec = {
-        "metric": "attention fwd TFLOP/s (allowed pairs) + % of bf16 MFMA peak, 1\u00d7MI355X",
-        "value": round(value, 3),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(wall * 1e3 / args.steps, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "config": {
-            "workload": cfg.description,
-            "B": cfg.B, "H": cfg.H, "N": cfg.N, "d": cfg.d, "causal": cfg.causal,
-            "block_sparse": cfg.sparse, "scale": cfg.scale, "seed": cfg.seed,
-            "allowed_pairs": pairs, "flops_per_step": flops,
-            "flop_count": "4*d per allowed (query, key) pair",
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 3),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": read_traffic(args.workload),
-            "kernel": "fwd_bf16_kernel",
-            "mean_launch_ms": round(mean_launch_ms, 5),
-        },
-    }
-    if executed is not None:
-        rec["config"]["executed_tile_flops_per_step"] = 4 * cfg.d * executed
-        rec["config"]["executed_tile_tflops"] = round(4 * cfg.d * executed * args.steps / wall / 1e12, 3)
-        rec["config"]["blockmask_build_ms_host"] = round(build_ms, 3)
-    if not args.no_gemm_ceiling:
-        rec["roofline"]["measured_bf16_gemm_ceiling"] = gemm_ceiling()
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, q, k, v)
-    print(json.dumps(rec), flush=True)
+    gemm = None if args.no_gemm_ceiling else gemm_ceiling()
+    failed = False
+    for c in (workloads.CONFIGS.values() if args.all else [cfg]):
+        rec = bench_fwd(args, c, dev, gemm)
+        failed = failed or not rec["check"]["ok"]
+        print(json.dumps(rec), flush=True)
+    if failed:
+        print("bench.py: the timed output exceeds the oracle tolerance (see \"check\")", file=sys.stderr)
+        sys.exit(3)
 
 
 def cpu_baseline_bwd(cfg, q, k, v, do, mask_lists, budget_s: float = 10.0):
     """The gradient oracle as it stands, on whole heads, until the budget is spent."""
     import oracle
-    from threadpoolctl import threadpool_info
-
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    hc = host_cores()
     done, flops, t_total = 0, 0, 0.0
     for h in range(cfg.H):
         qh, kh, vh, dh = (t[:, h:h + 1].to("cpu") for t in (q, k, v, do))
@@ -299,7 +417,8 @@ def cpu_baseline_bwd(cfg, q, k, v, do, mask_lists, budget_s: float = 10.0):
         if t_total >= budget_s:
             break
     return {
-        "value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+        "value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": hc["cores"],
+        "blas_threads": hc["blas_threads"], "kind": "oracle",
         "sample": f"{done} of {cfg.B * cfg.H} (batch, head) pairs of {cfg.name}, float64 numpy gradient oracle "
                   f"(forward recomputed), {t_total:.1f} s",
     }

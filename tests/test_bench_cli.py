@@ -74,3 +74,52 @@ def test_committed_traffic_records_name_their_workloads():
             w = name[len("fwd_bf16_"):-len("_traffic.json")]
             assert w in workloads.CONFIGS, name
             assert rec["traffic_bytes_per_launch"] > 0 and len(rec["kernel_source_sha256"]) == 64
+
+
+def test_cpu_baseline_reports_host_cores_and_blas_threads_separately():
+    cfg = workloads.CONFIGS["dense-f32-h1-n256-d64"]
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    rec = bench.cpu_baseline(cfg, q, k, v, budget_s=0.0)
+    assert rec["cores"] == len(os.sched_getaffinity(0))
+    assert rec["blas_threads"] >= 1
+    assert rec["rows_per_s"] > 0
+
+
+def test_cpu_baseline_on_sampled_rows_reports_rows_per_second_and_a_labelled_extrapolation():
+    import dataclasses
+    cfg = dataclasses.replace(workloads.CONFIGS["causal-h8-n131072-d128"], H=2, N=4096, sample_rows=256)
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    rec = bench.cpu_baseline(cfg, q, k, v, budget_s=0.0)
+    assert rec["sample"].startswith("256 sampled query rows of each of 1 of 2 (batch, head) pairs")
+    assert rec["extrapolated_all_rows_s"] > 0 and "extrapolation" in rec
+    # the rate counts the allowed pairs of the sampled rows only (causal: row r sees r + 1 keys)
+    assert rec["value"] > 0
+
+
+def test_oracle_check_passes_the_oracle_and_catches_a_planted_error():
+    import numpy as np
+    import oracle
+    cfg = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
+    import dataclasses
+    cfg = dataclasses.replace(cfg, B=1, H=2, N=300)
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    o_ref, lse_ref = oracle.attn_fwd(q, k, v, cfg.scale, cfg.causal)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_ref).float()
+    rec = bench.oracle_check(cfg, q, k, v, o, lse, rows_per_head=32)
+    assert rec["ok"] and rec["max_abs_dO"] <= 1e-2 and rec["max_abs_dLSE"] <= 1e-3
+    rows = workloads.sample_rows(cfg.N, 32, 77 * 1000 + 1)        # the rows checked on head 1
+    bad = o.clone()
+    bad[0, 1, rows[5], 3] += 0.05
+    rec = bench.oracle_check(cfg, q, k, v, bad, lse, rows_per_head=32)
+    assert not rec["ok"] and rec["max_abs_dO"] > 0.04
+    bad_l = lse.clone()
+    bad_l[0, 0, workloads.sample_rows(cfg.N, 32, 77 * 1000)[0]] = float("nan")
+    assert not bench.oracle_check(cfg, q, k, v, o, bad_l, rows_per_head=32)["ok"]
+
+
+def test_executed_tiles_of_causal_runs():
+    c2 = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
+    assert bench.executed_tiles_128(c2) == 8704        # 64 heads x 16 * 17 / 2
+    c5 = workloads.CONFIGS["causal-h8-n131072-d128"]
+    assert bench.executed_tiles_128(c5) == 4198400
