@@ -64,15 +64,14 @@ def token_mask_block_sparse(N: int, causal: bool, block: int, raw_row_ptr: np.nd
     block of row r (set semantics over the raw, uncanonicalised list)."""
     nqb = -(-N // block)
     sets = _row_block_sets(raw_row_ptr, raw_col, meta_head, nqb, nqb)
-    rows = np.asarray(rows)
+    rows = np.asarray(rows, dtype=np.int64)
     allowed = token_mask_dense(N, causal, rows)
-    key_block = np.arange(N) // block
-    for idx, i in enumerate(rows):
-        listed = np.zeros(nqb, dtype=bool)
-        s = sets[int(i) // block]
+    listed = np.zeros((nqb, nqb), dtype=bool)      # listed[query block, key block]
+    for qb, s in enumerate(sets):
         if s:
-            listed[list(s)] = True
-        allowed[idx] &= listed[key_block]
+            listed[qb, list(s)] = True
+    key_block = np.arange(N) // block
+    allowed &= listed[rows // block][:, key_block]
     return allowed
 
 

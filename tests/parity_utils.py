@@ -49,6 +49,26 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, dtype, label=""):
     return do, dl
 
 
+def per_head(fn, q, k, v, workers=8):
+    """Full-row oracle results of every (b, h), one head per task on a thread
+    pool (numpy's exponentials and BLAS release the GIL).  fn(q, k, v, b, h)
+    gets [1, 1, N, d] slices and returns the oracle's (O, LSE) for them."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, H, N, d = q.shape
+    jobs = [(b, h) for b in range(B) for h in range(H)]
+
+    def run(bh):
+        b, h = bh
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        return fn(q[sl], k[sl], v[sl], b, h)
+
+    with ThreadPoolExecutor(workers) as ex:
+        res = list(ex.map(run, jobs))
+    o = np.concatenate([r[0].reshape(1, N, d) for r in res]).reshape(B, H, N, d)
+    lse = np.concatenate([r[1].reshape(1, N) for r in res]).reshape(B, H, N)
+    return o, lse
+
+
 def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 

@@ -462,3 +462,17 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"planted mistake {name} passed every pin"
+
+
+def test_per_head_thread_pool_matches_whole_tensor_call():
+    # the GPU tests' threaded per-head evaluation returns the whole-tensor
+    # oracle result bit for bit, in [B, H, N, d] order
+    from parity_utils import per_head
+    B, H, N, d, block = 2, 3, 200, 64, 64
+    q, k, v = workloads.make_qkv(B, H, N, d, "bf16", 5)
+    nqb = -(-N // block)
+    rp, col = workloads.lists_to_csr([[qb, 0] if qb % 2 else [] for qb in range(nqb)])
+    whole = oracle.attn_fwd_blocksparse(q, k, v, 0.125, True, block, rp, col, 1)
+    split = per_head(lambda q1, k1, v1, b, h: oracle.attn_fwd_blocksparse(q1, k1, v1, 0.125, True, block,
+                                                                          rp, col, 1), q, k, v, workers=4)
+    assert np.array_equal(whole[0], split[0]) and np.array_equal(whole[1], split[1])

@@ -2,8 +2,9 @@
 oracle on the same seeded inputs, element by element.
 
 Small shapes are compared in full (several tiles, ragged tails, edge cases);
-the five named workloads run at full size in the bench's launch configuration
-and are compared on seeded samples of query rows.
+the five named workloads run at full size in the bench's launch configuration.
+All but the 131072-token causal one are compared on every row of every head;
+that one on 1024 seeded rows per head (the oracle's cost grows as N^2).
 """
 import math
 
@@ -13,7 +14,7 @@ import torch
 
 import oracle
 import workloads
-from parity_utils import compare, inputs, to64
+from parity_utils import compare, inputs, per_head, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +84,17 @@ def _sampled_dense(lib, cfg, rows_per_head=None):
     print(f"{cfg.name}: max|dO| {worst[0]:.3e} max|dLSE| {worst[1]:.3e}", flush=True)
 
 
-def test_dense_h32_n8192_d128_sampled(lib):
-    print("case dense-h32-n8192-d128", flush=True)
-    _sampled_dense(lib, workloads.CONFIGS["dense-h32-n8192-d128"], rows_per_head=256)
+def test_dense_h32_n8192_d128_full(lib):
+    # every row of every head
+    cfg = workloads.CONFIGS["dense-h32-n8192-d128"]
+    print("case dense-h32-n8192-d128 (all rows)", flush=True)
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    o, lse = lib.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=cfg.scale, causal=cfg.causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = per_head(lambda q1, k1, v1, b, h: oracle.attn_fwd(q1, k1, v1, cfg.scale, cfg.causal),
+                              q, k, v)
+    do, dl = compare(to64(o), to64(lse), o_ref, lse_ref, cfg.dtype, cfg.name)
+    print(f"{cfg.name}: max|dO| {do:.3e} max|dLSE| {dl:.3e} over {cfg.B * cfg.H * cfg.N} rows", flush=True)
 
 
 def test_causal_h8_n131072_d128_sampled(lib):
@@ -133,21 +142,23 @@ def test_sparse_random_lists(lib, N, d, meta, block, causal, dtype):
     _sparse_case(lib, B, H, N, d, dtype, causal, block, rows, mh, seed=N + d)
 
 
-def test_sparse_causal_h16_n16300_d128_sampled(lib):
+def test_sparse_causal_h16_n16300_d128_full(lib):
+    # every row of every head: empty query blocks, the partial last block and
+    # every local/global/random block of the pattern
     cfg = workloads.CONFIGS["sparse-causal-h16-n16300-d128"]
     rows = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
-    print("case sparse-causal-h16-n16300-d128", flush=True)
-
-    def sample(h):
-        r = set(workloads.sample_rows(cfg.N, 384, cfg.seed * 1000 + h).tolist())
-        # rows of every empty query block and of the partial last block
-        for qb, lst in enumerate(rows):
-            if not lst:
-                r.update((qb * cfg.block, qb * cfg.block + 77))
-        r.update(range(cfg.N - 44, cfg.N, 5))
-        return np.array(sorted(r))
-
-    _sparse_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.block, rows, 1, cfg.seed, sample)
+    rp, col = workloads.lists_to_csr(rows)
+    print("case sparse-causal-h16-n16300-d128 (all rows)", flush=True)
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    mask = lib.blockmask_build(rp, col, 1, cfg.N, cfg.block, cfg.causal)
+    o, lse = lib.attn_fwd_blocksparse(q.cuda(), k.cuda(), v.cuda(), mask, scale=cfg.scale, causal=cfg.causal)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = per_head(
+        lambda q1, k1, v1, b, h: oracle.attn_fwd_blocksparse(q1, k1, v1, cfg.scale, cfg.causal, cfg.block,
+                                                             rp, col, 1), q, k, v)
+    assert any(not r for r in rows) and cfg.N % cfg.block
+    do, dl = compare(to64(o), to64(lse), o_ref, lse_ref, cfg.dtype, cfg.name)
+    print(f"{cfg.name}: max|dO| {do:.3e} max|dLSE| {dl:.3e} over {cfg.B * cfg.H * cfg.N} rows", flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
