@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
+# BSATTN_LIBRARY names another build of the same library (the host-sanitized
+# checking build); by default the in-tree one is loaded.
+LIB_PATH = os.environ.get("BSATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "libbsattn.so")
 
 ATTN_OK = 0
 ATTN_EINVAL = -1

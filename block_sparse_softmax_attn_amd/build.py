@@ -39,9 +39,20 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, "-c", src, "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer, for the CPU-only
+# checking build of the argument validation and the block-mask builder.  Each
+# flag is scoped to the host pass (device code is compiled as usual).
+SANITIZE = [f for flag in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+                           "-fno-omit-frame-pointer")
+            for f in ("-Xarch_host", flag)]
+# the sources holding the host logic that the sanitized build instruments
+SANITIZED_SOURCES = ("api.cpp", "blockmask.cpp")
+SANITIZED_LIB = os.path.join(BUILD, "asan", "libbsattn.so")
+
+
+def _compile(src: str, obj_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [_hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -68,6 +79,42 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_sanitized(verbose: bool = True) -> str:
+    """A checking build at ``_build/asan/libbsattn.so``: api.cpp and blockmask.cpp
+    compiled with host ASan/UBSan, linked with the kernel objects of the normal
+    build (which must exist).  It is loaded only by a CPU test, in a process
+    that preloads the sanitizer runtime; the product library is never it."""
+    out = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(out, exist_ok=True)
+    objs = []
+    for src in sources():
+        name = os.path.basename(src)
+        if name in SANITIZED_SOURCES:
+            objs.append(_compile(src, out, SANITIZE))
+        else:
+            obj = os.path.join(BUILD, name + ".o")
+            if not os.path.exists(obj):
+                raise RuntimeError(f"{obj} is missing: run the normal build first")
+            objs.append(obj)
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", SANITIZED_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"built {SANITIZED_LIB}")
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (it carries the UBSan handlers)."""
+    r = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("the compiler's shared ASan runtime was not found")
+    return path
 
 
 if __name__ == "__main__":

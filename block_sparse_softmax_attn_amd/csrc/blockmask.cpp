@@ -39,7 +39,7 @@ extern "C" int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* r
     if (meta_heads < 1 || N < 1 || block < 1 || N > INT32_MAX || meta_heads > INT32_MAX)
         return ATTN_EINVAL;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
-    if (capacity < 0) return ATTN_EINVAL;
+    if (capacity < 0 || (capacity > 0 && (!col || !flags))) return ATTN_EINVAL;
     const int64_t nqb = (N + block - 1) / block;
     const int64_t nrows = meta_heads * nqb;
     if (nrows > INT32_MAX) return ATTN_EINVAL;
@@ -86,8 +86,8 @@ extern "C" int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* r
                     allowed += nrow_q * valid_in_block(kb, N, block);
                 }
                 if (out < capacity) {
-                    if (col) col[out] = kb;
-                    if (flags) flags[out] = f;
+                    col[out] = kb;
+                    flags[out] = f;
                 } else {
                     overflow = true;
                 }
@@ -101,7 +101,6 @@ extern "C" int attn_blockmask_build(const int32_t* raw_row_ptr, const int32_t* r
         executed_tile_pairs[h] = tiles;
     }
     *nnz = out;
-    if (out > 0 && (!col || !flags)) return ATTN_EINVAL;
     return overflow ? ATTN_ECAPACITY : ATTN_OK;
 }
 

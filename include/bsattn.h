@@ -101,6 +101,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *     CSR: each row strictly increasing and unique; future blocks dropped when
  *     causal; flags per entry use ATTN_FLAG_*.
  *   capacity          : entries available in col/flags; raw nnz always suffices.
+ *                       With capacity 0, col and flags may be NULL (a sizing
+ *                       call: ATTN_ECAPACITY and nnz, or ATTN_OK if nothing is
+ *                       listed); with capacity > 0 both are required.
  *   nnz               : entries written (or needed, with ATTN_ECAPACITY).
  *   allowed_pairs     : [meta_heads] logical (i, j) pairs with i, j < N allowed
  *                       by each pattern, per (b, h).

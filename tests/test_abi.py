@@ -184,6 +184,52 @@ def test_builder_capacity_error(m):
     assert st == ATTN_ECAPACITY and nnz[0] == 4 and list(out_rp) == [0, 2, 4] and al[0] == 256 and ex[0] == 4
 
 
+def test_builder_and_transpose_capacity_sweep(m):
+    # every capacity from 0 to nnz + 1 with output arrays of exactly that size:
+    # short capacities report ECAPACITY with the full nnz and offsets and write
+    # nothing past the arrays (the sanitized build checks the bounds); enough
+    # capacity gives the canonical result
+    from block_sparse_softmax_attn_amd._lib import ATTN_ECAPACITY, ATTN_OK, get
+    lib = get()
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p) if a.size else None
+    rng = workloads.SplitMix64(303)
+    for trial in range(12):
+        block = [1, 8, 64][trial % 3]
+        N = 1 + rng.below(400)
+        nqb = -(-N // block)
+        if nqb > 120:
+            continue
+        mh = 1 + rng.below(2)
+        causal = trial % 2
+        rows = workloads.random_lists(mh * nqb, nqb, rng, max_len=min(2 * nqb, 12), empty_prob_per_mille=200)
+        rp, col = workloads.lists_to_csr(rows)
+        full = m.blockmask_build(rp, col, mh, N, block, bool(causal))
+        for cap in range(full.nnz + 2):
+            out_rp = np.zeros(mh * nqb + 1, np.int32)
+            out_col = np.full(cap, -7, np.int32)
+            out_fl = np.full(cap, 0xEE, np.uint8)
+            nnz, al, ex = np.zeros(1, np.int64), np.zeros(mh, np.int64), np.zeros(mh, np.int64)
+            st = lib.attn_blockmask_build(p(rp), p(col), mh, N, block, causal, p(out_rp), p(out_col), p(out_fl),
+                                          cap, p(nnz), p(al), p(ex))
+            assert nnz[0] == full.nnz and np.array_equal(out_rp, full.row_ptr)
+            if cap < full.nnz:
+                assert st == ATTN_ECAPACITY
+                assert np.array_equal(out_col, full.col[:cap]) and np.array_equal(out_fl, full.flags[:cap])
+            else:
+                assert st == ATTN_OK
+                assert np.array_equal(out_col[:full.nnz], full.col) and np.all(out_col[full.nnz:] == -7)
+            t_rp = np.zeros(mh * nqb + 1, np.int32)
+            t_col = np.full(cap, -7, np.int32)
+            fr, fc = full.row_ptr.astype(np.int32), full.col.astype(np.int32)
+            st = lib.attn_blockmask_transpose(p(fr), p(fc), mh, N, block, p(t_rp), p(t_col), cap)
+            assert st == (ATTN_ECAPACITY if cap < full.nnz else ATTN_OK)
+            assert t_rp[-1] == full.nnz
+            if st == ATTN_OK:
+                assert np.all(t_col[full.nnz:] == -7)
+            else:
+                assert np.all(t_col == -7)
+
+
 # ---------------------------------------------------------------------------
 # backward entry points (argument checks only; no launch without a GPU)
 # ---------------------------------------------------------------------------
