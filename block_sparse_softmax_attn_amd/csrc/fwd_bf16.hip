@@ -36,8 +36,9 @@
 //     rescaled by exp2(m_old - m), and the tile's exponentials are recomputed.
 //     The common path thus has no per-tile max reduction (a serial chain of
 //     dependent vector operations) and almost never rescales the accumulator.
-//   * The K fragments of the score product are read from LDS four MFMAs ahead
-//     of their use, so the matrix core does not wait for each read.
+//   * The K fragments of the score product and the V fragments of the PV
+//     product are read from LDS four MFMAs ahead of their use, so the matrix
+//     core does not wait for each read.
 //   * Causal: key tiles wholly in the future are never visited, a wave skips
 //     the tiles that lie past all of its rows, and only tiles that cross the
 //     diagonal get the element mask.  Block-sparse: the tile loop runs over the
@@ -55,6 +56,7 @@ constexpr int kBN = 64;                // keys per tile step (32 for 64-key spar
 constexpr int kVtKeys = 64;            // keys per workgroup of the V^T pass
 constexpr float kSumMax = 0x1p64f;     // largest per-lane tile sum folded in without a rescale
 constexpr int kKAhead = 4;             // K fragment reads in flight ahead of their MFMAs
+constexpr int kVAhead = 4;             // V fragment reads in flight ahead of their MFMAs
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // Where the V operand of a tile comes from:
@@ -294,11 +296,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         for (int s = 0; s < NS - 1; ++s)
             if (s < ntiles) issue_tile(describe(s).kb0, s);
 
-        // One tile's math for this wave: scores, masks, online softmax, PV.
-        auto compute = [&](const TileDesc& t, const unsigned char* bK, const unsigned char* bV) {
+        // One tile's math for this wave, in three steps: scores (and masks),
+        // online softmax, PV.
+        f32x16 s[BN / 32];
+        bf16x8 pf[BN / 16];
+        auto scores = [&](const TileDesc& t, const unsigned char* bK) {
             // ---- S^T: lane (l32, hi) gets, in s[c][v], the score of query l32
             // and key kb0 + 32c + 8(v>>2) + 4hi + (v&3) ----
-            f32x16 s[BN / 32];
             constexpr int NF = (BN / 32) * (D / 16);   // fragment f: 32-key block f / (D/16), chunk f % (D/16)
             auto kfrag = [&](int f) {
                 return *reinterpret_cast<const bf16x8*>(bK + koff[f % (D / 16)] + 32 * (f / (D / 16)) * (2 * D));
@@ -333,10 +337,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                     for (int v = 0; v < 16; ++v)
                         s[c][v] = 32 * c + 8 * (v >> 2) + (v & 3) > r ? -__builtin_inff() : s[c][v];
             }
+        };
+        auto softmax = [&]() {
             // ---- online softmax ----
             // P rounds to bf16 for the PV product; the denominator sums the fp32
             // values so LSE keeps fp32 accuracy even for rows with few keys.
-            bf16x8 pf[BN / 16];
             float ts[8];
             auto exps = [&](float mu) {
 #pragma unroll
@@ -378,22 +383,39 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                 tsum = exps((m_run == -__builtin_inff()) ? 0.f : m_run);
             }
             ell += tsum;
-            // ---- O^T += V^T P^T ----
-#pragma unroll
-            for (int g = 0; g < BN / 16; ++g)
-#pragma unroll
-                for (int db = 0; db < D / 32; ++db) {
-                    const int d = 32 * db + l32;
-                    bf16x8 vf;
-                    if constexpr (VTR) {
-                        vf = tr_operand<D>(bV, trl, g, db);   // keys in the order pf[g] holds them
-                    } else {
-                        vf = *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz<BN>(d, 2 * g + hi) * 16);
-                    }
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[g], oacc[db], 0, 0, 0);
-                }
         };
-
+        auto pv = [&](const unsigned char* bV) {
+            // ---- O^T += V^T P^T ----
+            // fragment f: 16-key group g = f / (D/32), dimension block db = f % (D/32);
+            // read kVAhead MFMAs ahead of its use, like the K fragments
+            constexpr int NV = (BN / 16) * (D / 32);
+            constexpr int RD = VTR ? 2 : 1;            // LDS reads per fragment
+            auto vfrag = [&](int f) {
+                const int g = f / (D / 32), db = f % (D / 32);
+                if constexpr (VTR) {
+                    return tr_operand<D>(bV, trl, g, db);   // keys in the order pf[g] holds them
+                } else {
+                    const int d = 32 * db + l32;
+                    return *reinterpret_cast<const bf16x8*>(bV + d * (2 * BN) + v_swz<BN>(d, 2 * g + hi) * 16);
+                }
+            };
+            bf16x8 vfr[NV];
+#pragma unroll
+            for (int f = 0; f < kVAhead; ++f) vfr[f] = vfrag(f);
+#pragma unroll
+            for (int f = 0; f < NV; ++f) {
+                if (f + kVAhead < NV) vfr[f + kVAhead] = vfrag(f + kVAhead);
+                oacc[f % (D / 32)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfr[f], pf[f / (D / 32)],
+                                                                           oacc[f % (D / 32)], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, RD * kVAhead, 0);
+#pragma unroll
+            for (int f = 0; f < NV - kVAhead; ++f) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
+        };
         // Tile it, in stage buffer u = it % NS: wait for its loads, barrier
         // (every wave's loads have landed and every wave is done with tile
         // it-1), refill the buffer of tile it-1 with tile it+NS-1, compute.
@@ -407,7 +429,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             if (it + NS - 1 < ntiles) issue_tile(describe(it + NS - 1).kb0, un);
             const TileDesc t = describe(it);
             // a wave whose rows all precede the tile skips its math
-            if (!(t.causal && t.kb0 > wdiag)) compute(t, kbuf[u], vbuf[u]);
+            if (!(t.causal && t.kb0 > wdiag)) {
+                scores(t, kbuf[u]);
+                softmax();
+                pv(vbuf[u]);
+            }
         };
 
         for (int base = 0; base < ntiles; base += NS) {

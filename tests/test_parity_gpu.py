@@ -162,6 +162,31 @@ def test_sparse_causal_h16_n16300_d128_full(lib):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_sparse_many_blocks_every_row(lib, d, causal):
+    # 2 x 8 heads x 41 query blocks of 128 = 656 > 512 workgroup slots: each
+    # workgroup runs a sequence of query blocks (persistent form), the next
+    # block's first tile and query rows loaded during the current block's last
+    # tile.  One pattern per head, empty blocks, a ragged last block.
+    B, H, N, block = 2, 8, 5200, 128
+    nqb = -(-N // block)
+    rng = workloads.SplitMix64(4000 + d + causal)
+    rows = workloads.random_lists(H * nqb, nqb, rng, max_len=6, empty_prob_per_mille=120)
+    print(f"case sparse persistent d={d} causal={causal}", flush=True)
+    q, k, v = inputs(B, H, N, d, "bf16", 4100 + d)
+    rp, col = workloads.lists_to_csr(rows)
+    mask = lib.blockmask_build(rp, col, H, N, block, causal)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = lib.attn_fwd_blocksparse(q.cuda(), k.cuda(), v.cuda(), mask, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    assert B * H * nqb > 512 and any(not r for r in rows)
+    o_ref, lse_ref = per_head(
+        lambda q1, k1, v1, b, h: oracle.attn_fwd_blocksparse(q1, k1, v1, scale, causal, block, rp[h * nqb:(h + 1) * nqb + 1] - rp[h * nqb],
+                                                             col[rp[h * nqb]:rp[(h + 1) * nqb]], 1), q, k, v)
+    compare(to64(o), to64(lse), o_ref, lse_ref, "bf16", f"sparse persistent d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("block,d", [(128, 128), (64, 64), (64, 128)])
 def test_all_active_mask_equals_dense(lib, causal, block, d):
     # Where the block-sparse kernel steps through keys in the dense kernel's 64-key
