@@ -536,10 +536,14 @@ hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
-    // dense and causal: 8 waves (256 query rows) share each K/V tile, one
-    // workgroup per CU, 2 (dense) or 3 (causal) tiles in flight (4 waves and
-    // 2 tiles on small grids, below).  Block-sparse: the workgroup is one query block, two workgroups
-    // per CU, 2 tiles in flight.
+    // dense, causal and key ranges: 8 waves (256 query rows) share each K/V
+    // tile, one workgroup per CU, 2 tiles in flight (4 waves on small grids,
+    // below).  Two stages keep the 64 KiB of K and V buffers within reach of
+    // the LDS offset field, so every fragment read is a register plus an
+    // immediate; three stages were slower on every shape measured (B1 H8
+    // N131072 d128 causal: 1126 -> 1239 TFLOP/s with two; four key ranges
+    // of B1 H32 N8192 d128: 848 -> 943).  Block-sparse: the workgroup is one
+    // query block, two workgroups per CU, 2 tiles in flight.
     // Fewer than 4 rounds of 256-row workgroups over the 256 CUs: 128-row
     // workgroups (two per CU, 2 tiles in flight) fill the chip better (B=4
     // H=16 N=2048 causal: 343 -> 410 TFLOP/s); larger grids keep 256 rows,
@@ -547,15 +551,12 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     const bool small_grid = (int64_t)((a.N + 255) / 256) * a.BH < 1024;
     switch (mode) {
         case Mode::kDense:
-            // two stages: the 64 KiB of K and V buffers stay within reach of
-            // the LDS offset field (B1 H32 N8192 d128: +1% on N(0,1) inputs,
-            // +5% on all-zero inputs, where the clock is not power-limited)
             if (small_grid) return launch_v<D, 4, 2, (int)Mode::kDense>(a, stream);
             return launch_v<D, 8, 2, (int)Mode::kDense>(a, stream);
         case Mode::kCausal:
             if (small_grid) return launch_v<D, 4, 2, (int)Mode::kCausal>(a, stream);
-            return launch_v<D, 8, 3, (int)Mode::kCausal>(a, stream);
-        case Mode::kRange: return launch_v<D, 8, 3, (int)Mode::kRange>(a, stream);
+            return launch_v<D, 8, 2, (int)Mode::kCausal>(a, stream);
+        case Mode::kRange: return launch_v<D, 8, 2, (int)Mode::kRange>(a, stream);
         case Mode::kSparse:
             if (a.block == 128) return launch_v<D, 4, 2, (int)Mode::kSparse>(a, stream);
             // 64-key blocks at d = 128: 32-key tile steps, so a workgroup's two
