@@ -303,19 +303,22 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         auto scores = [&](const TileDesc& t, const unsigned char* bK) {
             // ---- S^T: lane (l32, hi) gets, in s[c][v], the score of query l32
             // and key kb0 + 32c + 8(v>>2) + 4hi + (v&3) ----
-            constexpr int NF = (BN / 32) * (D / 16);   // fragment f: 32-key block f / (D/16), chunk f % (D/16)
+            // fragment f: 32-key block c = f % NC, chunk f / NC -- the blocks'
+            // accumulation chains alternate, so consecutive MFMAs are independent
+            // (each chain still adds its chunks in order)
+            constexpr int NC = BN / 32, NF = NC * (D / 16);
             auto kfrag = [&](int f) {
-                return *reinterpret_cast<const bf16x8*>(bK + koff[f % (D / 16)] + 32 * (f / (D / 16)) * (2 * D));
+                return *reinterpret_cast<const bf16x8*>(bK + koff[f / NC] + 32 * (f % NC) * (2 * D));
             };
             bf16x8 kfr[NF];
 #pragma unroll
             for (int f = 0; f < kKAhead; ++f) kfr[f] = kfrag(f);
 #pragma unroll
-            for (int c = 0; c < BN / 32; ++c) s[c] = f32x16{};
+            for (int c = 0; c < NC; ++c) s[c] = f32x16{};
 #pragma unroll
             for (int f = 0; f < NF; ++f) {
                 if (f + kKAhead < NF) kfr[f + kKAhead] = kfrag(f + kKAhead);
-                s[f / (D / 16)] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[f], qf[f % (D / 16)], s[f / (D / 16)], 0, 0, 0);
+                s[f % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[f], qf[f / NC], s[f % NC], 0, 0, 0);
             }
             // keep the reads kKAhead MFMAs ahead (DS reads: 0x100, MFMA: 0x008)
             __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
