@@ -175,7 +175,8 @@ def oracle_check(cfg, q, k, v, o, lse, rows_per_head: int = CHECK_ROWS, mask_lis
             live = np.isfinite(rl)
             if np.isnan(go).any() or np.isnan(gl).any():
                 ok = False
-            if not np.array_equal(np.isfinite(gl), live) or not np.all(go[~live] == 0):
+            if not np.array_equal(np.isfinite(gl), live) or not np.all(go[~live] == 0) \
+                    or not np.all(gl[~live] == -np.inf):
                 ok = False
             if live.any():
                 worst_o = max(worst_o, float(np.abs(go[live] - ro[live]).max()))

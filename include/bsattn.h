@@ -248,6 +248,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *   overlap on one GPU (different streams, host threads) race and must be
  *   ordered by the caller.  Nothing in the array needs clearing between calls
  *   (the first kernel of a call writes every statistic the later ones read).
+ *   The array is the current HIP device's (hipGetDevice); the stream and the
+ *   tensors must be on that device.  The first call on a device looks up the
+ *   array's address there (hipGetSymbolAddress, no allocation); a caller that
+ *   captures graphs can make that first call before capturing.
  *   Errors: as for attn_bwd; ATTN_EHIP also when the array's device address
  *   cannot be obtained.
  */

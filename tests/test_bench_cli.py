@@ -123,3 +123,26 @@ def test_executed_tiles_of_causal_runs():
     assert bench.executed_tiles_128(c2) == 8704        # 64 heads x 16 * 17 / 2
     c5 = workloads.CONFIGS["causal-h8-n131072-d128"]
     assert bench.executed_tiles_128(c5) == 4198400
+
+
+def test_oracle_check_holds_empty_rows_to_zero_and_minus_inf():
+    import dataclasses
+    import numpy as np
+    import oracle
+    cfg = dataclasses.replace(workloads.CONFIGS["sparse-causal-h16-n16300-d128"], H=1, N=640)
+    nqb = cfg.N // cfg.block
+    rows = [[qb] if qb != 2 else [] for qb in range(nqb)]     # query block 2 lists nothing
+    rp, col = workloads.lists_to_csr(rows)
+    q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
+    o_ref, lse_ref = oracle.attn_fwd_blocksparse(q, k, v, cfg.scale, True, cfg.block, rp, col, 1)
+    assert np.isinf(lse_ref[0, 0, 256:384]).all()
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(lse_ref).float()
+    check = lambda o_, l_: bench.oracle_check(cfg, q, k, v, o_, l_, rows_per_head=640, mask_lists=(rp, col))["ok"]
+    assert check(o, lse)
+    bad_l = lse.clone()
+    bad_l[0, 0, 300] = float("inf")          # an empty row must give -inf, not +inf
+    assert not check(o, bad_l)
+    bad_o = o.clone()
+    bad_o[0, 0, 300, 7] = 1e-3               # and O exactly 0
+    assert not check(bad_o, lse)
