@@ -6,10 +6,12 @@ rounded to fp32 from the forward ORACLE; the reference is the oracle's
 gradient rebuilt from those same O and LSE, and the allowed error per element
 is the bound of ``parity_utils.bwd_bounds_head`` (bf16 rounding of P and dS,
 fp32 accumulation, bf16 outputs).  Small shapes are compared on every head.
-The full-size workloads are compared on one or two heads; heads are
-independent, so the other heads take their O and LSE from the GPU forward
-(their gradients are not compared).
+The full-size workloads are compared on every head (c2, c3) or on 8 of the
+16 heads (c4); heads are independent, so the other heads take their O and LSE
+from the GPU forward (their gradients are not compared).  The per-head oracle work runs on a thread pool (numpy's
+BLAS and elementwise loops release the GIL).
 """
+from concurrent.futures import ThreadPoolExecutor
 import math
 
 import numpy as np
@@ -32,7 +34,7 @@ def lib():
     return m
 
 
-def _setup(B, H, N, d, seed, fwd, heads=None, gpu_fwd=None):
+def _setup(B, H, N, d, seed, fwd, heads=None, gpu_fwd=None, workers=8):
     """Seeded bf16 Q, K, V, dO and the backward's O (bf16) and LSE (fp32) inputs:
     the forward oracle's on every head in ``heads`` (all heads when None),
     the GPU forward's (``gpu_fwd``) on the others."""
@@ -43,27 +45,33 @@ def _setup(B, H, N, d, seed, fwd, heads=None, gpu_fwd=None):
         return q, k, v, do, torch.from_numpy(o_ex).to(torch.bfloat16), torch.from_numpy(lse_ex).to(torch.float32)
     o_g, lse_g = gpu_fwd(q.cuda(), k.cuda(), v.cuda())
     o_in, lse_in = o_g.cpu(), lse_g.cpu()
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(h, h + 1))
-        o_ex, lse_ex = fwd(q[sl], k[sl], v[sl])
+    sls = [(slice(b, b + 1), slice(h, h + 1)) for b, h in heads]
+    with ThreadPoolExecutor(workers) as ex:
+        outs = list(ex.map(lambda sl: fwd(q[sl], k[sl], v[sl]), sls))
+    for sl, (o_ex, lse_ex) in zip(sls, outs):
         o_in[sl] = torch.from_numpy(o_ex).to(torch.bfloat16)
         lse_in[sl] = torch.from_numpy(lse_ex).to(torch.float32)
     return q, k, v, do, o_in, lse_in
 
 
-def _check_heads(grads, q, k, v, do, o_in, lse_in, scale, heads, allowed_for_head, ref_bwd, label):
+def _check_heads(grads, q, k, v, do, o_in, lse_in, scale, heads, allowed_for_head, ref_bwd, label, workers=8):
     """Compare GPU (dQ, dK, dV) with the oracle on the listed (b, h) heads."""
     gq, gk, gv = (to64(g) for g in grads)
     q64, k64, v64, do64, o64, l64 = (to64(t) for t in (q, k, v, do, o_in, lse_in))
-    worst = 0.0
-    for b, h in heads:
+
+    def one(bh):
+        b, h = bh
         rq, rk, rv = ref_bwd(b, h, q64[b, h], k64[b, h], v64[b, h], do64[b, h], o64[b, h], l64[b, h])
         bq, bk, bv = bwd_bounds_head(q64[b, h], k64[b, h], v64[b, h], do64[b, h], scale, allowed_for_head(b, h),
                                      o64[b, h], l64[b, h])
+        worst = 0.0
         for name, got, ref, bd in (("dQ", gq, rq, bq), ("dK", gk, rk, bk), ("dV", gv, rv, bv)):
             _, r = compare_grad(got[b, h], ref, bd, f"{label} ({b},{h}) {name}")
             worst = max(worst, r)
-    return worst
+        return worst
+
+    with ThreadPoolExecutor(workers) as ex:
+        return max(ex.map(one, heads))
 
 
 def _dense_ref(N, causal, scale):
@@ -73,17 +81,17 @@ def _dense_ref(N, causal, scale):
     return ref
 
 
-def _dense_case(lib, B, H, N, d, causal, seed, heads=None):
+def _dense_case(lib, B, H, N, d, causal, seed, heads=None, workers=8):
     scale = float(np.float32(1.0 / math.sqrt(d)))
     fwd = lambda q, k, v: oracle.attn_fwd(q, k, v, scale, causal)
     gpu_fwd = lambda q, k, v: lib.attn_fwd(q, k, v, scale=scale, causal=causal)
-    q, k, v, do, o_in, lse_in = _setup(B, H, N, d, seed, fwd, heads, gpu_fwd)
+    q, k, v, do, o_in, lse_in = _setup(B, H, N, d, seed, fwd, heads, gpu_fwd, workers)
     grads = lib.attn_bwd(*(t.cuda() for t in (q, k, v, o_in, lse_in, do)), scale=scale, causal=causal)
     torch.cuda.synchronize()
     heads = heads or [(b, h) for b in range(B) for h in range(H)]
     allowed = lambda b, h: (lambda rows: A.token_mask_dense(N, causal, rows))
     return _check_heads(grads, q, k, v, do, o_in, lse_in, scale, heads, allowed, _dense_ref(N, causal, scale),
-                        f"bwd dense B{B} H{H} N{N} d{d} causal={causal}")
+                        f"bwd dense B{B} H{H} N{N} d{d} causal={causal}", workers)
 
 
 SMALL = [(1, 1, 1, 64), (1, 2, 33, 128), (2, 1, 64, 64), (1, 2, 200, 128), (1, 1, 256, 64),
@@ -98,7 +106,7 @@ def test_bwd_dense_small(lib, shape, causal):
     _dense_case(lib, B, H, N, d, causal, seed=2000 + N + d + causal)
 
 
-def _sparse_case(lib, B, H, N, d, block, causal, lists, meta_heads, seed, heads=None):
+def _sparse_case(lib, B, H, N, d, block, causal, lists, meta_heads, seed, heads=None, workers=8):
     scale = float(np.float32(1.0 / math.sqrt(d)))
     rp, col = workloads.lists_to_csr(lists)
     fwd = lambda q, k, v: oracle.attn_fwd_blocksparse(q, k, v, scale, causal, block, rp, col, meta_heads)
@@ -106,7 +114,7 @@ def _sparse_case(lib, B, H, N, d, block, causal, lists, meta_heads, seed, heads=
     gpu_fwd = lambda q, k, v: lib.attn_fwd_blocksparse(q, k, v, mask, scale=scale)
     if heads is not None:
         assert meta_heads == 1, "per-head patterns are compared on every head"
-    q, k, v, do, o_in, lse_in = _setup(B, H, N, d, seed, fwd, heads, gpu_fwd)
+    q, k, v, do, o_in, lse_in = _setup(B, H, N, d, seed, fwd, heads, gpu_fwd, workers)
     grads = lib.attn_bwd_blocksparse(*(t.cuda() for t in (q, k, v, o_in, lse_in, do)), mask, scale=scale)
     torch.cuda.synchronize()
     heads = heads or [(b, h) for b in range(B) for h in range(H)]
@@ -119,7 +127,7 @@ def _sparse_case(lib, B, H, N, d, block, causal, lists, meta_heads, seed, heads=
         return oracle.attention_head_bwd(q_, k_, v_, do_, scale, allowed(b, h), o=o_, lse=l_)
 
     worst = _check_heads(grads, q, k, v, do, o_in, lse_in, scale, heads, allowed, ref,
-                         f"bwd sparse N{N} d{d} b{block} causal={causal} mh={meta_heads}")
+                         f"bwd sparse N{N} d{d} b{block} causal={causal} mh={meta_heads}", workers)
     return grads, worst
 
 
@@ -202,18 +210,21 @@ def test_bwd_workspace_too_small_is_rejected(lib):
         lib.attn_bwd(q, k, v, o, lse, q, workspace=torch.empty(64, dtype=torch.uint8, device="cuda"))
 
 
-# ---- full-size workloads, compared on one or two heads ----
+# ---- full-size workloads ----
 
 def test_bwd_causal_b4_h16_n2048_d64(lib):
+    # every head
     cfg = workloads.CONFIGS["causal-b4-h16-n2048-d64"]
-    print("case bwd causal-b4-h16-n2048-d64", flush=True)
-    _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, True, cfg.seed, heads=[(0, 0), (3, 15)])
+    print("case bwd causal-b4-h16-n2048-d64 (all heads)", flush=True)
+    _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, True, cfg.seed,
+                heads=[(b, h) for b in range(cfg.B) for h in range(cfg.H)])
 
 
 def test_bwd_dense_b1_h32_n8192_d128(lib):
+    # every head
     cfg = workloads.CONFIGS["dense-h32-n8192-d128"]
-    print("case bwd dense-h32-n8192-d128", flush=True)
-    _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, False, cfg.seed, heads=[(0, 5)])
+    print("case bwd dense-h32-n8192-d128 (all heads)", flush=True)
+    _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, False, cfg.seed, heads=[(0, h) for h in range(cfg.H)])
 
 
 def _global_column_lists(nb):
@@ -254,4 +265,6 @@ def test_bwd_block_sparse_b1_h16_n16300_d128(lib):
     cfg = workloads.CONFIGS["sparse-causal-h16-n16300-d128"]
     print("case bwd sparse-causal-h16-n16300-d128", flush=True)
     lists = workloads.local_global_random_lists(cfg.N, cfg.block, cfg.seed)
-    _sparse_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.block, True, lists, 1, cfg.seed, heads=[(0, 9)])
+    # 8 of the 16 heads, the first and the last included (~28 s of host work per head)
+    _sparse_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.block, True, lists, 1, cfg.seed,
+                 heads=[(0, h) for h in (0, 2, 5, 7, 9, 11, 13, 15)])
