@@ -221,6 +221,50 @@ def copy_calibration(nbytes: int = 1 << 30):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "dispatches": 3}))
 
 
+def algorithmic_bytes(cfg, mask=None) -> int:
+    """Bytes the method itself must move per launch: Q read once, O written
+    once, 4 B of LSE per row, and K and V read once -- for a block-sparse
+    pattern only the key blocks its lists reference (one pattern for every
+    head here)."""
+    elem = 2 if cfg.dtype == "bf16" else 4
+    rows = cfg.B * cfg.H * cfg.N
+    qo = 2 * rows * cfg.d * elem + 4 * rows
+    if mask is None:
+        return qo + 2 * rows * cfg.d * elem
+    keys = 0
+    for kb in sorted(set(int(c) for c in mask.col)):
+        keys += min(cfg.N, (kb + 1) * cfg.block) - kb * cfg.block
+    return qo + 2 * cfg.B * cfg.H * keys * cfg.d * elem
+
+
+def device_info(dev):
+    """The GPU's compute-unit count and maximum clock (rocminfo, when it runs;
+    the CU count also from the runtime), and the bf16 matrix peak they give."""
+    import subprocess
+    import torch
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cus_runtime": props.multi_processor_count, "cus_rocminfo": None, "max_clock_mhz_rocminfo": None}
+    try:
+        out = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        for agent in out.split("*******")[1:]:
+            fields = {}
+            for line in agent.splitlines():
+                if ":" in line:
+                    key, _, val = line.partition(":")
+                    fields.setdefault(key.strip(), val.strip())
+            if fields.get("Name", "").startswith("gfx"):
+                info["cus_rocminfo"] = int(fields["Compute Unit"])
+                info["max_clock_mhz_rocminfo"] = int(fields["Max Clock Freq. (MHz)"])
+                break
+    except (OSError, subprocess.SubprocessError, KeyError, ValueError):
+        pass
+    cus = info["cus_rocminfo"] or info["cus_runtime"]
+    if cus and info["max_clock_mhz_rocminfo"]:
+        info["bf16_peak_tflops_from_units"] = round(cus * 4096 * info["max_clock_mhz_rocminfo"] * 1e6 / 1e12, 1)
+    return info
+
+
 def executed_tiles_128(cfg, mask=None) -> int:
     """Executed work of a causal or block-sparse run in b x b tiles (b = 128;
     the sparse pattern's own block): diagonal tiles count whole."""
@@ -255,6 +299,7 @@ def bench_fwd(args, cfg, dev, gemm=None):
         build_ms = (time.perf_counter() - t0) * 1e3
         pairs = int(mask.allowed_pairs[0]) * cfg.B * cfg.H
         executed = executed_tiles_128(cfg, mask) * cfg.block * cfg.block
+        alg_bytes = algorithmic_bytes(cfg, mask)
         mask.to_device(dev)
         fused = lambda: attn.attn_fwd_blocksparse(q, k, v, mask, scale=cfg.scale, causal=cfg.causal,
                                                   out=o, lse=lse)
@@ -262,6 +307,7 @@ def bench_fwd(args, cfg, dev, gemm=None):
         build_ms = None
         pairs = allowed_pairs_dense(cfg)
         executed = executed_tiles_128(cfg) * 128 * 128 if cfg.causal else None
+        alg_bytes = algorithmic_bytes(cfg)
         fused = lambda: attn.attn_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
     flops = 4 * cfg.d * pairs
 
@@ -320,8 +366,13 @@ def bench_fwd(args, cfg, dev, gemm=None):
             "traffic": read_traffic(cfg.name) if cfg.dtype == "bf16" else None,
             "kernel": "fwd_bf16_kernel" if cfg.dtype == "bf16" else "fwd_f32_kernel",
             "mean_launch_ms": round(mean_launch_ms, 5),
+            # HBM rates per launch: the method's own bytes, and the counted bytes when known
+            "algorithmic_bytes": alg_bytes,
+            "hbm_gbps_algorithmic": round(alg_bytes / (mean_launch_ms * 1e-3) / 1e9, 1),
         },
     }
+    if rec["roofline"]["traffic"] is not None:
+        rec["roofline"]["hbm_gbps_counted"] = round(rec["roofline"]["traffic"] / (mean_launch_ms * 1e-3) / 1e9, 1)
     if cfg.dtype != "bf16":
         rec["roofline"]["note"] = ("fp32 workload of 16.8 MFLOP: one small launch, latency-bound; "
                                    "its time is reported for context, against the fp32 matrix peak")
@@ -387,9 +438,11 @@ def main():
         bench_select(args, cfg, dev)
         return
     gemm = None if args.no_gemm_ceiling else gemm_ceiling()
+    device = device_info(dev)
     failed = False
     for c in (workloads.CONFIGS.values() if args.all else [cfg]):
         rec = bench_fwd(args, c, dev, gemm)
+        rec["device"] = device
         failed = failed or not rec["check"]["ok"]
         print(json.dumps(rec), flush=True)
     if failed:

@@ -146,3 +146,19 @@ def test_oracle_check_holds_empty_rows_to_zero_and_minus_inf():
     bad_o = o.clone()
     bad_o[0, 0, 300, 7] = 1e-3               # and O exactly 0
     assert not check(bad_o, lse)
+
+
+def test_algorithmic_bytes():
+    # dense: Q, K, V read and O written once (bf16), 4 B of LSE per row
+    c3 = workloads.CONFIGS["dense-h32-n8192-d128"]
+    assert bench.algorithmic_bytes(c3) == 4 * 32 * 8192 * 128 * 2 + 32 * 8192 * 4
+    c1 = workloads.CONFIGS["dense-f32-h1-n256-d64"]
+    assert bench.algorithmic_bytes(c1) == 4 * 256 * 64 * 4 + 256 * 4
+    # block-sparse: K and V only for the referenced key blocks (the last one partial)
+    import dataclasses
+    import block_sparse_softmax_attn_amd as m
+    cfg = dataclasses.replace(workloads.CONFIGS["sparse-causal-h16-n16300-d128"], H=2, N=300)
+    rp, col = workloads.lists_to_csr([[0], [0], [2, 0]])        # block 1 never referenced
+    mask = m.blockmask_build(rp, col, 1, 300, 128, True)
+    keys = 128 + (300 - 256)
+    assert bench.algorithmic_bytes(cfg, mask) == 2 * 2 * 300 * 128 * 2 + 2 * 300 * 4 + 2 * 2 * keys * 128 * 2
