@@ -128,7 +128,34 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
     // (a few blocks each): head by head, which keeps one head's K/V hot in L2.
     int64_t rest;
     int qt;
-    if (MODE == (int)Mode::kCausal || (RANGE && a.causal)) {
+    // folded causal schedule: jobs (head, query tile) of this workgroup
+    int njobs = 1;
+    int64_t jhead[2] = {0, 0};
+    int jqt[2] = {0, 0};
+    const bool FOLD = MODE == (int)Mode::kCausal && a.fold_slots > 0;
+    if (FOLD) {
+        // per XCD: Tx tiles ranked heavy first (rank-major, head-minor), Sx
+        // slots; the Tx - Sx lightest ranks ride with the heaviest, the
+        // singles alternate heavy and light halves so each CU's three
+        // workgroups add up to the same work
+        const int x = blockIdx.x % 8, l = blockIdx.x / 8;
+        const int Tx = (int)(total / 8), Sx = a.fold_slots / 8, Px = Tx - Sx;
+        const int hx = Tx / nqt;
+        auto job_of = [&](int r, int k) {
+            jhead[k] = (int64_t)x * hx + r % hx;
+            jqt[k] = nqt - 1 - r / hx;
+        };
+        if (l < Px) {
+            job_of(l, 0);
+            job_of(Tx - 1 - l, 1);
+            njobs = 2;
+        } else {
+            const int i = l - Px, nsing = Tx - 2 * Px, h = (nsing + 1) / 2;
+            job_of(i < h ? Px + i : Tx - Px - 1 - (i - h), 0);
+        }
+        rest = jhead[0];
+        qt = jqt[0];
+    } else if (MODE == (int)Mode::kCausal || (RANGE && a.causal)) {
         rank_major_order(blockIdx.x, total, nqt, rest, qt);
         qt = nqt - 1 - qt;
     } else {
@@ -136,6 +163,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
         rest = ord / nqt;
         qt = (int)(ord % nqt);
         if (MODE == (int)Mode::kSparse) qt = nqt - 1 - qt;
+    }
+    // The workgroup's query tiles, one after the other (two only in a folded
+    // causal launch); the loop body keeps the indentation of the kernel.
+    for (int job = 0; job < njobs; ++job) {
+    if (FOLD) {
+        rest = jhead[job];
+        qt = jqt[job];
+        if (job > 0) barrier();   // every wave is done with the stage buffers
     }
     const int split = (int)(rest % nsplit);
     const int64_t bh = rest / nsplit;
@@ -466,7 +501,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
                 }
             if (hi == 0) a.lse_part[row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
         }
-        return;
+        continue;
     }
     if (qi < N) {
         __bf16* Oh = static_cast<__bf16*>(a.o) + bh * (int64_t)N * D + (int64_t)qi * D;
@@ -483,6 +518,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd_bf16_kernel(FwdArgs a) {
             a.lse[bh * (int64_t)N + qi] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
         }
     }
+    }   // query tiles of the workgroup
 }
 
 // V [BH][N][D] -> V^T [BH][D][npad].  Inside each 16-key group, slot 8h + w of
@@ -524,7 +560,8 @@ template <int D, int NW, int NS, int MODE, int VSRC, int BN = kBN>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
     using G = Geo<D, NW, NS, VSRC, BN>;
     const int64_t nqt = (a.N + G::BM - 1) / G::BM;
-    const int64_t grid = nqt * a.BH * (MODE == (int)Mode::kRange ? a.nsplit : 1);
+    const int64_t grid = (MODE == (int)Mode::kCausal && a.fold_slots > 0) ? a.fold_slots
+                         : nqt * a.BH * (MODE == (int)Mode::kRange ? a.nsplit : 1);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, NS, MODE, VSRC, BN>), dim3((unsigned)grid), dim3(G::NT), 0, stream,
                        a);
     return hipGetLastError();
@@ -535,6 +572,47 @@ template <int D, int NW, int NS, int MODE, int BN = kBN>
 hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
     if (a.vt != nullptr) return launch<D, NW, NS, MODE, kVsT, BN>(a, stream);
     return launch<D, NW, NS, MODE, kVsTr, BN>(a, stream);
+}
+
+// Workgroups of the 4-wave causal instance (head dimension D, V source vt)
+// that the current device holds at once: CUs x resident workgroups per CU,
+// asked once per device (-1 when the runtime cannot say).
+template <int D>
+int resident_slots(int vt) {
+    static int cached[2][64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+    int& c = cached[vt][dev];
+    if (c == 0) {
+        int cus = 0, per = 0;
+        hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = vt ? hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                         &per, fwd_bf16_kernel<D, 4, 2, (int)Mode::kCausal, kVsT>, 256, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                         &per, fwd_bf16_kernel<D, 4, 2, (int)Mode::kCausal, kVsTr>, 256, 0);
+        c = (e == hipSuccess && cus > 0 && per > 0) ? cus * per : -1;
+    }
+    return c;
+}
+
+// Causal launches whose query tiles number more than one resident round of
+// workgroups but at most two: the dispatcher would start the lightest tiles
+// only when the first slots free up, and they would run into a tail.  Folded,
+// the grid is exactly the resident slots S: on each XCD the Tx - Sx lightest
+// tiles ride in the workgroups of the heaviest (two tiles in a row), and the
+// remaining single tiles are ordered heavy, then light in reverse, so the
+// three workgroups a CU receives add up to the same work.  Needs the tiles in
+// whole heads per XCD (B*H a multiple of 8); returns S, or 0 for the plain
+// one-tile-per-workgroup grid.
+template <int D, int NW>
+int fold_slots(const FwdArgs& a) {
+    const int64_t nqt = (a.N + 32 * NW - 1) / (32 * NW);
+    const int64_t T = nqt * a.BH;
+    const int S = resident_slots<D>(a.vt != nullptr ? 1 : 0);
+    if (S <= 0 || S % 8 != 0 || a.BH % 8 != 0) return 0;
+    if (T <= S || T > 2 * (int64_t)S) return 0;
+    return S;
 }
 
 template <int D>
@@ -557,7 +635,11 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
             if (small_grid) return launch_v<D, 4, 2, (int)Mode::kDense>(a, stream);
             return launch_v<D, 8, 2, (int)Mode::kDense>(a, stream);
         case Mode::kCausal:
-            if (small_grid) return launch_v<D, 4, 2, (int)Mode::kCausal>(a, stream);
+            if (small_grid) {
+                FwdArgs f = a;
+                f.fold_slots = fold_slots<D, 4>(a);
+                return launch_v<D, 4, 2, (int)Mode::kCausal>(f, stream);
+            }
             return launch_v<D, 8, 2, (int)Mode::kCausal>(a, stream);
         case Mode::kRange: return launch_v<D, 8, 2, (int)Mode::kRange>(a, stream);
         case Mode::kSparse:

@@ -40,6 +40,7 @@ struct FwdArgs {
     int nsplit;
     float* o_part;       // [nsplit][BH][N][d]
     float* lse_part;     // [nsplit][BH][N]
+    int fold_slots;      // causal: grid of this many resident workgroups (0: one per query tile)
 };
 
 enum class Mode : int { kDense = 0, kCausal = 1, kSparse = 2, kRange = 3 };
