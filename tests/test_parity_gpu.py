@@ -64,6 +64,23 @@ def test_causal_b4_h16_n2048_d64_full(lib):
     _dense_case(lib, cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.causal, cfg.seed, cfg.scale)
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 8, 12400), (2, 8, 6400)])
+def test_causal_folded_schedule_every_row(lib, B, H, N):
+    # d = 64 causal launches of 4-wave workgroups with between one and two
+    # resident rounds of query tiles (776 and 800 tiles against 768 slots on a
+    # 256-CU part) run two query tiles in some workgroups; per XCD the single
+    # tiles number 95 (odd) and 92 (even), and N = 12400 leaves a ragged last tile
+    d = 64
+    print(f"case causal folded B{B} H{H} N{N} d{d}", flush=True)
+    q, k, v = inputs(B, H, N, d, "bf16", 4242 + N)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = lib.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = per_head(lambda q1, k1, v1, b, h: oracle.attn_fwd(q1, k1, v1, scale, True), q, k, v)
+    do, dl = compare(to64(o), to64(lse), o_ref, lse_ref, "bf16", f"causal folded B{B} H{H} N{N}")
+    print(f"max|dO| {do:.3e} max|dLSE| {dl:.3e}", flush=True)
+
+
 def _sampled_dense(lib, cfg, rows_per_head=None):
     q, k, v = workloads.make_qkv(cfg.B, cfg.H, cfg.N, cfg.d, cfg.dtype, cfg.seed)
     o, lse = lib.attn_fwd(q.cuda(), k.cuda(), v.cuda(), scale=cfg.scale, causal=cfg.causal)
