@@ -280,6 +280,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         hi_ = (int)min<int64_t>(max(hi_, lo), a.t_nnz);
     };
     int ntiles = 0;
+    int lo_u = 0;   // first entry of a list every query head of the group shares
     if (MODE != (int)Mode::kSparse) {
         ntiles = per * group;
     } else if (uniform) {
@@ -287,6 +288,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         list_of(0, lo, hi_);
         per = (hi_ - lo) * subs;
         ntiles = per * group;
+        lo_u = lo;
     } else {
         for (int gi = 0; gi < group; ++gi) {
             int lo, hi_;
@@ -324,8 +326,9 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         if (MODE != (int)Mode::kSparse) {
             t.q0 = (first + loc) * BT;
         } else {
-            int lo, hi_;
-            list_of(gi, lo, hi_);
+            // a shared list's start is known; per-head lists look theirs up
+            int lo = lo_u, hi_;
+            if (!uniform) list_of(gi, lo, hi_);
             const int qb = ld_meta(a.t_col, lo + loc / subs);
             t.q0 = (qb >= 0 && qb < nqb_meta) ? qb * a.block + (loc % subs) * BT : -1;
         }
