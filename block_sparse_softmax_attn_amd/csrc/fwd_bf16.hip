@@ -46,6 +46,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "fwd_common.h"
 #include "gfx950_util.h"
 
@@ -576,7 +579,8 @@ hipError_t launch_v(const FwdArgs& a, hipStream_t stream) {
 
 // Workgroups of the 4-wave causal instance (head dimension D, V source vt)
 // that the current device holds at once: CUs x resident workgroups per CU,
-// asked once per device (-1 when the runtime cannot say).
+// asked once per device (-1, and asked again on the next call, when the
+// runtime cannot say).
 template <int D>
 int resident_slots(int vt) {
     static int cached[2][64] = {};
@@ -591,7 +595,8 @@ int resident_slots(int vt) {
                          &per, fwd_bf16_kernel<D, 4, 2, (int)Mode::kCausal, kVsT>, 256, 0)
                    : hipOccupancyMaxActiveBlocksPerMultiprocessor(
                          &per, fwd_bf16_kernel<D, 4, 2, (int)Mode::kCausal, kVsTr>, 256, 0);
-        c = (e == hipSuccess && cus > 0 && per > 0) ? cus * per : -1;
+        if (e != hipSuccess || cus <= 0 || per <= 0) return -1;   // not cached: asked again next time
+        c = cus * per;
     }
     return c;
 }
@@ -615,6 +620,22 @@ int fold_slots(const FwdArgs& a) {
     return S;
 }
 
+// Tuning override of the dense and causal workgroup shape, read once per
+// process from the environment variable ATTN_TILE: "128" (4 waves, 128 query
+// rows per workgroup) or "256" (8 waves, 256 rows); unset or any other value
+// keeps the automatic choice.  The outputs do not depend on it: a wave's 32
+// rows, the key tiles it visits and their order are the same in both shapes.
+int tile_rows_override() {
+    static const int rows = [] {
+        const char* e = std::getenv("ATTN_TILE");
+        if (e == nullptr) return 0;
+        if (std::strcmp(e, "128") == 0) return 128;
+        if (std::strcmp(e, "256") == 0) return 256;
+        return 0;
+    }();
+    return rows;
+}
+
 template <int D>
 hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     // dense, causal and key ranges: 8 waves (256 query rows) share each K/V
@@ -629,7 +650,8 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     // workgroups (two per CU, 2 tiles in flight) fill the chip better (B=4
     // H=16 N=2048 causal: 343 -> 410 TFLOP/s); larger grids keep 256 rows,
     // which halves the K/V tile traffic per query.
-    const bool small_grid = (int64_t)((a.N + 255) / 256) * a.BH < 1024;
+    const int forced = tile_rows_override();
+    const bool small_grid = forced ? forced == 128 : (int64_t)((a.N + 255) / 256) * a.BH < 1024;
     switch (mode) {
         case Mode::kDense:
             if (small_grid) return launch_v<D, 4, 2, (int)Mode::kDense>(a, stream);

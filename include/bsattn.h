@@ -34,6 +34,11 @@
  *   - Status codes: every function returns ATTN_OK or a negative code, and
  *     validates all arguments before any launch (nothing is launched on
  *     error).  No C++ exception crosses this interface.
+ *   - Tuning override (not part of the interface contract): the environment
+ *     variable ATTN_TILE, read once per process, forces the workgroup shape of
+ *     the bf16 dense and causal forwards to "128" or "256" query rows; any
+ *     other value, or none, keeps the automatic choice.  The results are the
+ *     same in both shapes.
  */
 #ifndef BSATTN_H
 #define BSATTN_H
