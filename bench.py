@@ -62,6 +62,12 @@ import workloads  # noqa: E402  (seeded input recipes: shapes, seeds, block list
 
 PEAK_BF16_TFLOPS = 2516.6    # 256 CU x 4096 bf16 FLOP/clk/CU x 2.4 GHz, dense
 PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 matrix peak, dense
+# The softmax's vector work per executed score in the bf16 kernel: one FMA (scale
+# and reference value), one v_exp_f32 (two issue slots on gfx950), one add to
+# the fp32 denominator and half a bf16 pack: 4.5 wave64 instructions of 4 cycles
+# per 64 scores on a 16-lane SIMD.
+VALU_CYCLES_PER_SCORE = 4.5 * 4 / 64
+SIMDS, CLOCK_GHZ = 256 * 4, 2.4
 TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-5, 1e-5)}   # max|dO|, max|dLSE| against the oracle
 CHECK_ROWS = 64              # seeded query rows per head the bench output is checked on
 # the forward kernel's source and the headers it includes: the recorded counters stay valid
@@ -265,6 +271,16 @@ def device_info(dev):
     return info
 
 
+def vector_floor(executed_scores: int, mean_launch_ms: float) -> dict:
+    """Time floors of a launch at 2.4 GHz on all 1024 SIMDs: the softmax's
+    vector work (VALU_CYCLES_PER_SCORE per executed score) and the matrix work
+    (4 d flops per score at the bf16 peak are given by the caller's roofline);
+    the launch's time against the vector floor."""
+    floor_ms = executed_scores * VALU_CYCLES_PER_SCORE / (SIMDS * CLOCK_GHZ * 1e9) * 1e3
+    return {"cycles_per_score": VALU_CYCLES_PER_SCORE, "floor_ms": round(floor_ms, 5),
+            "frac": round(floor_ms / mean_launch_ms, 4)}
+
+
 def executed_tiles_128(cfg, mask=None) -> int:
     """Executed work of a causal or block-sparse run in b x b tiles (b = 128;
     the sparse pattern's own block): diagonal tiles count whole."""
@@ -373,6 +389,15 @@ def bench_fwd(args, cfg, dev, gemm=None):
     }
     if rec["roofline"]["traffic"] is not None:
         rec["roofline"]["hbm_gbps_counted"] = round(rec["roofline"]["traffic"] / (mean_launch_ms * 1e-3) / 1e9, 1)
+    if cfg.dtype == "bf16":
+        # secondary bound: the softmax's vector work on the executed scores
+        # (whole tiles for causal and block-sparse runs); at d = 64 it exceeds
+        # the matrix work's time at peak
+        scores = executed if executed is not None else pairs
+        vf = vector_floor(scores, mean_launch_ms)
+        vf["mfma_floor_ms"] = round(4 * cfg.d * scores / (PEAK_BF16_TFLOPS * 1e12) * 1e3, 5)
+        vf["binding"] = "valu" if vf["floor_ms"] > vf["mfma_floor_ms"] else "mfma"
+        rec["roofline"]["vector_floor"] = vf
     if cfg.dtype != "bf16":
         rec["roofline"]["note"] = ("fp32 workload of 16.8 MFLOP: one small launch, latency-bound; "
                                    "its time is reported for context, against the fp32 matrix peak")

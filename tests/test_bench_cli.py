@@ -162,3 +162,11 @@ def test_algorithmic_bytes():
     mask = m.blockmask_build(rp, col, 1, 300, 128, True)
     keys = 128 + (300 - 256)
     assert bench.algorithmic_bytes(cfg, mask) == 2 * 2 * 300 * 128 * 2 + 2 * 300 * 4 + 2 * 2 * keys * 128 * 2
+
+
+def test_vector_floor_closed_form():
+    # one millisecond of the softmax's vector work on every SIMD at 2.4 GHz
+    scores = round(1024 * 2.4e9 * 1e-3 / bench.VALU_CYCLES_PER_SCORE)
+    vf = bench.vector_floor(scores, 2.0)
+    assert abs(vf["floor_ms"] - 1.0) < 1e-4 and abs(vf["frac"] - 0.5) < 1e-4
+    assert bench.VALU_CYCLES_PER_SCORE == 4.5 * 4 / 64
