@@ -14,7 +14,9 @@ fp32 one included):
            query-key pair: the QK^T and PV contractions), wall clock between
            two device synchronisations;
   timing   the fused kernel's duration per launch (HIP events on the launch
-           stream): mean, median and min over the timed steps;
+           stream around every EVENT_STRIDE-th timed launch: an event pair
+           around every launch adds about 6 us to a 45 us step): mean, median
+           and min over those launches;
   roofline the fused kernel against the MFMA peak of its dtype: achieved =
            flops per launch / mean launch duration; traffic = HBM bytes per
            launch from rocprofv3 FETCH_SIZE and WRITE_SIZE counters
@@ -67,6 +69,10 @@ PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 matrix peak, dense
 # the fp32 denominator and half a bf16 pack: 4.5 wave64 instructions of 4 cycles
 # per 64 scores on a 16-lane SIMD.
 VALU_CYCLES_PER_SCORE = 4.5 * 4 / 64
+# Timed steps whose launch is bracketed by a HIP event pair (the first and then
+# every EVENT_STRIDE-th): enough samples for the kernel's mean duration, few
+# enough event records that they hardly add to the steps' wall clock.
+EVENT_STRIDE = 8
 SIMDS, CLOCK_GHZ = 256 * 4, 2.4
 TOL = {"bf16": (1e-2, 1e-3), "f32": (1e-5, 1e-5)}   # max|dO|, max|dLSE| against the oracle
 CHECK_ROWS = 64              # seeded query rows per head the bench output is checked on
@@ -332,13 +338,16 @@ def bench_fwd(args, cfg, dev, gemm=None):
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(0, args.steps, EVENT_STRIDE)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        fused()
-        ev[i][1].record(stream)
+        if i % EVENT_STRIDE == 0:
+            ev[i // EVENT_STRIDE][0].record(stream)
+            fused()
+            ev[i // EVENT_STRIDE][1].record(stream)
+        else:
+            fused()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch = sorted(e[0].elapsed_time(e[1]) for e in ev)
@@ -372,7 +381,8 @@ def bench_fwd(args, cfg, dev, gemm=None):
             "parallelism": "single GPU",
         },
         "timing": {"launch_ms_mean": round(mean_launch_ms, 5), "launch_ms_median": round(median_launch_ms, 5),
-                   "launch_ms_min": round(launch[0], 5), "launches": len(launch)},
+                   "launch_ms_min": round(launch[0], 5), "launches": len(launch),
+                   "launches_timed_of": args.steps, "event_stride": EVENT_STRIDE},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 3),
