@@ -19,7 +19,9 @@
 //   * dK/dV computes S = Q K^T and dP = dO V^T with the keys as the MFMA
 //     columns: a lane holds 16 queries of ONE key, and those registers (P and
 //     dS rounded to bf16) are directly the B operand of dV^T += dO^T P and
-//     dK^T += Q^T dS.  The A operands dO^T and Q^T come from the same
+//     dK^T += Q^T dS.  The dP product runs on -V and starts from D (read from
+//     LDS straight into the accumulator), so it yields D - dP and dS costs one
+//     multiply per element; the wave accumulates -dK, negated in the epilogue.  The A operands dO^T and Q^T come from the same
 //     row-major dO and Q tiles through the transposing LDS load
 //     (ds_read_b64_tr_b16), in the query order the P and dS registers hold.
 //   * dQ computes S^T = K Q^T and dP^T = V dO^T (a lane holds keys of ONE query,
@@ -214,6 +216,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
     unsigned char* const sO1 = sQO + 3 * G::TB;
     __shared__ __attribute__((aligned(1024))) float sS0[256], sS1[256];
     __shared__ __attribute__((aligned(16))) bf16x8 sP[PAIRED ? G::PAIRS : 1][2][2][64];   // [pair][block][step][lane]
+    __shared__ __attribute__((aligned(16))) float sZ[64];   // zeros: the P wave's accumulator start
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -395,6 +398,15 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         const __bf16* src = (role == 0 ? Kh : Vh) + (int64_t)row * D + 8 * hi;
 #pragma unroll
         for (int k = 0; k < D / 16; ++k) kvf[k] = *reinterpret_cast<const bf16x8*>(src + 16 * k);
+        // the dS wave holds -V, so its product started from D gives D - dP
+        const unsigned flip = role == 0 ? 0u : 0x80008000u;
+#pragma unroll
+        for (int k = 0; k < D / 16; ++k) {
+            u32x4 x = __builtin_bit_cast(u32x4, kvf[k]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] ^= flip;
+            kvf[k] = __builtin_bit_cast(bf16x8, x);
+        }
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) acc[i] = f32x16{};
     } else {
@@ -404,6 +416,11 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         for (int k = 0; k < D / 16; ++k) {
             kf[k] = *reinterpret_cast<const bf16x8*>(Kh + (int64_t)row * D + 16 * k + 8 * hi);
             vf[k] = *reinterpret_cast<const bf16x8*>(Vh + (int64_t)row * D + 16 * k + 8 * hi);
+            // -V: the product started from D gives D - dP
+            u32x4 x = __builtin_bit_cast(u32x4, vf[k]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[j] ^= 0x80008000u;
+            vf[k] = __builtin_bit_cast(bf16x8, x);
         }
 #pragma unroll
         for (int i = 0; i < D / 32; ++i) {
@@ -411,6 +428,7 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
             dvacc[i] = f32x16{};
         }
     }
+    if (tid < 64) sZ[tid] = 0.f;
     wait_vmcnt<0>();
     const float sl2 = a.scale_log2;
 
@@ -441,10 +459,22 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
         // q0 + 32qc + 8(v>>2) + 4hi + (v&3) of key kj in element v ----
         f32x16 pr[2];
         bf16x8 pb[2][2];
+        // accumulators start at 0 (P wave: S) or at D_q (dS wave: D - dP, the
+        // wave's V rows being negated); lane (l32, hi) element 4 g4 + e is query
+        // 32 qc + 8 g4 + 4 hi + e
+        const float* ib = role == 0 ? sZ : st + 64;
 #pragma unroll
         for (int qc = 0; qc < 2; ++qc) {
             pr[qc] = f32x16{};
             if (!live[qc]) continue;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 d4 = *reinterpret_cast<const float4*>(ib + 32 * qc * role + 8 * g4 + 4 * hi);
+                pr[qc][4 * g4 + 0] = d4.x;
+                pr[qc][4 * g4 + 1] = d4.y;
+                pr[qc][4 * g4 + 2] = d4.z;
+                pr[qc][4 * g4 + 3] = d4.w;
+            }
             bf16x8 fa[D / 16];
 #pragma unroll
             for (int k = 0; k < D / 16; ++k)
@@ -490,18 +520,13 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
                 op[0] = pb[qc][0];
                 op[1] = pb[qc][1];
             } else {
-                // dS = P (dP - D) from the rounded P, rounded to bf16
+                // -dS = P (D - dP) from the rounded P, rounded to bf16 (the
+                // epilogue negates dK)
                 const bf16x8 p0 = sP[pw][qc][0][lane], p1 = sP[pw][qc][1][lane];
 #pragma unroll
-                for (int g4 = 0; g4 < 4; ++g4) {
-                    const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 32 * qc + 8 * g4 + 4 * hi);
-                    const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int v = 4 * g4 + e;
-                        const float p = (float)((v >> 3) ? p1[v & 7] : p0[v & 7]);
-                        op[v >> 3][v & 7] = (__bf16)(p * (pr[qc][v] - dv[e]));
-                    }
+                for (int v = 0; v < 16; ++v) {
+                    const float p = (float)((v >> 3) ? p1[v & 7] : p0[v & 7]);
+                    op[v >> 3][v & 7] = (__bf16)(p * pr[qc][v]);
                 }
             }
             // dV^T += dO^T P (P wave) or dK^T += Q^T dS (dS wave) over two 16-query steps
@@ -540,7 +565,16 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
                 fa[k] = *reinterpret_cast<const bf16x8*>(bQ + off);
                 fb[k] = *reinterpret_cast<const bf16x8*>(bO + off);
             }
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // dp starts at D (its B operand is -V): D - dP
+            f32x16 s = f32x16{}, dp;
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 32 * qc + 8 * g4 + 4 * hi);
+                dp[4 * g4 + 0] = d4.x;
+                dp[4 * g4 + 1] = d4.y;
+                dp[4 * g4 + 2] = d4.z;
+                dp[4 * g4 + 3] = d4.w;
+            }
             __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
             for (int k = 0; k < D / 16; ++k) {
@@ -568,16 +602,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
                 const float4 l4 = *reinterpret_cast<const float4*>(st + 32 * qc + 8 * g4 + 4 * hi);
-                const float4 d4 = *reinterpret_cast<const float4*>(st + 64 + 32 * qc + 8 * g4 + 4 * hi);
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-                const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int v = 4 * g4 + e;
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[v], sl2, -lv[e]));
                     const __bf16 pr = (__bf16)p;
                     pb[v >> 3][v & 7] = pr;
-                    dsb[v >> 3][v & 7] = (__bf16)((float)pr * (dp[v] - dv[e]));
+                    dsb[v >> 3][v & 7] = (__bf16)((float)pr * dp[v]);   // -dS
                 }
             }
             // ---- dV^T += dO^T P, dK^T += Q^T dS over the two 16-query steps ----
@@ -651,14 +683,14 @@ __global__ __launch_bounds__(64 * NW, 2) void bwd_dkdv_kernel(BwdArgs a) {
                 const int c = 32 * db + 8 * j + 4 * hi;
                 bf16x4 kv, vv;
                 if constexpr (PAIRED) {
-                    const float f = role == 0 ? 1.0f : a.scale;
+                    const float f = role == 0 ? 1.0f : -a.scale;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) kv[i] = (__bf16)(acc[db][4 * j + i] * f);
                     *reinterpret_cast<bf16x4*>((role == 0 ? dVr : dKr) + c) = kv;
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        kv[i] = (__bf16)(dkacc[db][4 * j + i] * a.scale);
+                        kv[i] = (__bf16)(dkacc[db][4 * j + i] * -a.scale);
                         vv[i] = (__bf16)dvacc[db][4 * j + i];
                     }
                     *reinterpret_cast<bf16x4*>(dKr + c) = kv;
@@ -955,7 +987,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a, int nkt) {
         const int r = is_k ? e : e - BKV * D;
         const int key = r / D, c = r % D;
         if (kb0 + key >= a.N) continue;
-        const float m = is_k ? a.scale : 1.f;
+        const float m = is_k ? -a.scale : 1.f;   // the partial dK sums hold -dK / scale
         const bf16x4 out = {(__bf16)(sum.x * m), (__bf16)(sum.y * m), (__bf16)(sum.z * m), (__bf16)(sum.w * m)};
         __bf16* dst = static_cast<__bf16*>(is_k ? a.dk : a.dv);
         *reinterpret_cast<bf16x4*>(dst + (kvbh * a.N + kb0 + key) * (int64_t)D + c) = out;
