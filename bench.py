@@ -79,8 +79,21 @@ CHECK_ROWS = 64              # seeded query rows per head the bench output is ch
 # the forward kernel's source and the headers it includes: the recorded counters stay valid
 # only while none of them changes
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_softmax_attn_amd", "csrc", f)
-                  for f in ("fwd_bf16.hip", "fwd_common.h", "gfx950_util.h")]
+                  for f in ("fwd_bf16.hip", "fwd_bf16_w64.hip", "fwd_common.h", "gfx950_util.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_{workload}_traffic.json")
+
+
+def fwd_kernel_name(cfg) -> str:
+    """The forward kernel the library launches for a workload (its dispatch
+    rule: bf16 dense d = 128 launches of at least 1024 256-row query tiles
+    with N a multiple of 64 use the 64-row kernel unless ATTN_W64=0)."""
+    if cfg.dtype != "bf16":
+        return "fwd_f32_kernel"
+    large = (cfg.N + 255) // 256 * cfg.B * cfg.H >= 1024 or os.environ.get("ATTN_TILE") == "256"
+    if (not cfg.causal and not cfg.sparse and cfg.d == 128 and cfg.N >= 128 and cfg.N % 64 == 0 and large
+            and os.environ.get("ATTN_TILE") != "128" and os.environ.get("ATTN_W64") != "0"):
+        return "fwd_w64_kernel"
+    return "fwd_bf16_kernel"
 
 
 def kernel_source_hash() -> str:
@@ -390,7 +403,7 @@ def bench_fwd(args, cfg, dev, gemm=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": read_traffic(cfg.name) if cfg.dtype == "bf16" else None,
-            "kernel": "fwd_bf16_kernel" if cfg.dtype == "bf16" else "fwd_f32_kernel",
+            "kernel": fwd_kernel_name(cfg),
             "mean_launch_ms": round(mean_launch_ms, 5),
             # HBM rates per launch: the method's own bytes, and the counted bytes when known
             "algorithmic_bytes": alg_bytes,

@@ -27,6 +27,12 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",
           "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source flags.  The 64-row forward keeps its O accumulators in AGPRs by
+# writing those products as inline assembly; this makes the compiler keep its
+# own (score) products in the VGPR form, whose results the softmax reads.
+EXTRA = {"fwd_bf16_w64.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = shutil.which("hipcc") or os.path.join(rocm, "bin", "hipcc")
@@ -52,7 +58,7 @@ SANITIZED_LIB = os.path.join(BUILD, "asan", "libbsattn.so")
 
 def _compile(src: str, obj_dir: str = BUILD, extra=()) -> str:
     obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
