@@ -396,25 +396,39 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
 
     // ---- epilogue: O = A / l, LSE = (m + log2 l) ln 2 ----
+    // O goes through LDS (the tile buffers are idle now): each wave writes
+    // its 64 x 128 bf16 rows there, 16-byte chunks XOR-swizzled by the row,
+    // and reads them back four whole rows per instruction, so every global
+    // store writes 1 KiB of consecutive bytes.
     settle_acc(oacc);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's last fragment reads have returned
+    barrier();                            // ... and every other wave's
+    unsigned char* const stg = (w < 2 ? sK : sV) + (w & 1) * (kRows * kD * 2);
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const int qi = q0 + 32 * r + l32;
+        const int row = 32 * r + l32;   // of the wave's 64
         const float l_tot = xor32_sum(ell[r]);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-        if (qi < N) {
-            __bf16* Oh = static_cast<__bf16*>(a.o) + bh * (int64_t)N * kD + (int64_t)qi * kD;
 #pragma unroll
-            for (int db = 0; db < kD / 32; ++db)
+        for (int db = 0; db < kD / 32; ++db)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 ov;
+            for (int j = 0; j < 4; ++j) {
+                bf16x4 ov;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[r][db][4 * j + i] * inv);
-                    *reinterpret_cast<bf16x4*>(Oh + 32 * db + 8 * j + 4 * hi) = ov;
-                }
-            if (hi == 0) a.lse[bh * (int64_t)N + qi] = l_tot > 0.f ? (m_run[r] + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-        }
+                for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[r][db][4 * j + i] * inv);
+                const int chunk = (4 * db + j) ^ (row & 15);   // dims 32 db + 8 j .. + 7
+                *reinterpret_cast<bf16x4*>(stg + row * (2 * kD) + chunk * 16 + 8 * hi) = ov;
+            }
+        const int qi = q0 + row;
+        if (hi == 0 && qi < N)
+            a.lse[bh * (int64_t)N + qi] = l_tot > 0.f ? (m_run[r] + __log2f(l_tot)) * kLn2 : -__builtin_inff();
+    }
+    __bf16* const Oh = static_cast<__bf16*>(a.o) + bh * (int64_t)N * kD;
+#pragma unroll
+    for (int s4 = 0; s4 < kRows / 4; ++s4) {
+        const int row = 4 * s4 + (lane >> 4), c = lane & 15;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * (2 * kD) + (c ^ (row & 15)) * 16);
+        if (q0 + row < N) *reinterpret_cast<u32x4*>(Oh + (int64_t)(q0 + row) * kD + 8 * c) = val;
     }
 }
 
