@@ -28,10 +28,12 @@
 //
 // The online softmax is the one of fwd_bf16.hip: the exponentials of sub-tile
 // k are taken against each row's current reference value m and folded in as is
-// when every lane's sum is finite and at most 2^64; otherwise (and on a row's
-// first sub-tile) m is raised to the sub-tile's row max, the state rescaled and
-// the exponentials recomputed.  The PV products of sub-tile k-1, issued in the
-// same stage, used P relative to the old m, so rescaling A after them is exact.
+// when every lane's sum is finite and at most 2^64; otherwise m is raised to the
+// sub-tile's row max, the state rescaled and the exponentials recomputed.  The
+// PV products of sub-tile k-1, issued in the same stage, used P relative to the
+// old m, so rescaling A after them is exact.  A row's first sub-tile takes m
+// from its own row max before its exponentials (its scores are complete when
+// its stage begins), so it needs no check.
 //
 // Tiles: K and V tiles of 64 keys go straight into LDS (global_load_lds_dwordx4),
 // two buffers each.  Stage 2t+1 needs K of tile t+1 (its first half) and V of
@@ -206,6 +208,7 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         fNK = 32,       // read the next stage's first K fragments
         fNV = 64,       // read the next stage's first V fragments
         fCold = 256,    // no fragments were read ahead for this stage
+        fFirst = 1024,  // sub-tile 0: m from its row max first, no check
     };
     f32x16 sE[2], sO[2];          // scores of even / odd sub-tiles
     bf16x8 pE[2][2], pO[2][2];    // P of even / odd sub-tiles
@@ -248,6 +251,18 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
             sout[0] = f32x16{};
             sout[1] = f32x16{};
         }
+        if constexpr ((F & fFirst) != 0) {
+            // every row's first sub-tile: its scores are complete, so m starts
+            // at their row max and no exponential can exceed 1 (whole tiles
+            // and no masks here, so the max is finite)
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                float mx = sin[r][0];
+#pragma unroll
+                for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sin[r][v]);
+                m_run[r] = xor32_max(mx) * sl2;
+            }
+        }
         if constexpr ((F & fCold) != 0) {
             read(0);
             read(1);
@@ -284,8 +299,7 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 if (i == SPAN + LAG) {
                     tsum[0] = (ts[0][0] + ts[0][1]) + (ts[0][2] + ts[0][3]);
                     tsum[1] = (ts[1][0] + ts[1][1]) + (ts[1][2] + ts[1][3]);
-                    bad = m_run[0] == -__builtin_inff() || m_run[1] == -__builtin_inff() || !(tsum[0] <= kSumMax) ||
-                          !(tsum[1] <= kSumMax);
+                    bad = !(tsum[0] <= kSumMax) || !(tsum[1] <= kSumMax);
                 }
             }
         };
@@ -336,7 +350,10 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (SM) {
+        if constexpr (SM && (F & fFirst) != 0) {
+            ell[0] = tsum[0];
+            ell[1] = tsum[1];
+        } else if constexpr (SM) {
             // P complete before the check (which may recompute it)
             asm volatile("" : "+v"(pout[0][0]), "+v"(pout[0][1]), "+v"(pout[1][0]), "+v"(pout[1][1]));
             settle(sin, pout, tsum, bad);
@@ -354,8 +371,8 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     wait_vmcnt<2 * kPerW>();
     barrier();
     stage(std::integral_constant<int, fS | fCold | fNK>{}, sO, pO, sE, sK, pE, sV, 0, sK + kHalf, sV, 0, 0, 0, 0, 0);
-    stage(std::integral_constant<int, fS | fSM | fBar | fNK | fNV>{}, sE, pE, sO, sK + kHalf, pO, sV, 0, sK1, sV, 0,
-          0, 0, 0, 0);
+    stage(std::integral_constant<int, fS | fSM | fFirst | fBar | fNK | fNV>{}, sE, pE, sO, sK + kHalf, pO, sV, 0, sK1,
+          sV, 0, 0, 0, 0, 0);
 
     // Tile t+1 for t <= T-3: stage 2t+1 (S(2t+2) <- K(t+1) half 0, PV(2t) <-
     // V(t) half 0, SM(2t+1); loads of K(t+2) and V(t+1) into the buffers of
