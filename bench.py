@@ -80,7 +80,7 @@ CHECK_ROWS = 64              # seeded query rows per head the bench output is ch
 # only while none of them changes
 KERNEL_SOURCES = [os.path.join(ROOT, "block_sparse_softmax_attn_amd", "csrc", f)
                   for f in ("fwd_bf16.hip", "fwd_bf16_w64.hip", "fwd_common.h", "gfx950_util.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_bf16_{workload}_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "{kernel}_{workload}_traffic.json")
 
 
 def fwd_kernel_name(cfg) -> str:
@@ -109,8 +109,8 @@ def allowed_pairs_dense(cfg) -> int:
     return cfg.B * cfg.H * per_head
 
 
-def read_traffic(workload: str):
-    path = TRAFFIC_FILE.format(workload=workload)
+def read_traffic(workload: str, kernel: str = "fwd_bf16"):
+    path = TRAFFIC_FILE.format(workload=workload, kernel=kernel)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -402,7 +402,8 @@ def bench_fwd(args, cfg, dev, gemm=None):
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": read_traffic(cfg.name) if cfg.dtype == "bf16" else None,
+            "traffic": (read_traffic(cfg.name, fwd_kernel_name(cfg).replace("_kernel", "")) if cfg.dtype == "bf16"
+                        else None),
             "kernel": fwd_kernel_name(cfg),
             "mean_launch_ms": round(mean_launch_ms, 5),
             # HBM rates per launch: the method's own bytes, and the counted bytes when known
