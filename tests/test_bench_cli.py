@@ -67,13 +67,21 @@ def test_stored_traffic_is_used_only_for_the_same_kernel_source(tmp_path, monkey
 
 
 def test_committed_traffic_records_name_their_workloads():
+    # profiles/<kernel>_<workload>_traffic.json, <kernel> the one bench.py names for the workload
     prof = os.path.join(ROOT, "profiles")
+    seen = 0
     for name in os.listdir(prof):
         if name.endswith("_traffic.json"):
             rec = json.load(open(os.path.join(prof, name)))
-            w = name[len("fwd_bf16_"):-len("_traffic.json")]
-            assert w in workloads.CONFIGS, name
+            stem = name[:-len("_traffic.json")]
+            found = [w for w in workloads.CONFIGS if stem.endswith("_" + w)]
+            assert len(found) == 1, name
+            cfg = workloads.CONFIGS[found[0]]
+            assert stem == bench.fwd_kernel_name(cfg).replace("_kernel", "") + "_" + cfg.name, name
+            assert rec["workload"] == cfg.description, name
             assert rec["traffic_bytes_per_launch"] > 0 and len(rec["kernel_source_sha256"]) == 64
+            seen += 1
+    assert seen >= 4
 
 
 def test_cpu_baseline_reports_host_cores_and_blas_threads_separately():
