@@ -238,8 +238,10 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         // compiler would otherwise sink them all to the end of the stage)
         auto fold = [&](int e) __attribute__((always_inline)) {
             const int r = e / 16, v = e % 16;
-            ts[r][v & 3] = v < 4 ? ex[e] : ts[r][v & 3] + ex[e];
-            asm volatile("" : "+v"(ts[r][v & 3]));
+            if (v >= 4) {
+                ts[r][v & 3] = v < 8 ? ex[e - 4] + ex[e] : ts[r][v & 3] + ex[e];
+                asm volatile("" : "+v"(ts[r][v & 3]));
+            }
             if (v & 1) {
                 bf16x2 pr = {(__bf16)ex[e - 1], (__bf16)ex[e]};
                 asm volatile("" : "+v"(pr));
