@@ -281,7 +281,7 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         // One slot per MFMA, fenced so that the compiler keeps the order: the
         // MFMA, one exponential (two in 16-slot stages), the sum and packing of
         // an element exponentiated LAG slots earlier, and at most one fragment
-        // read.  Slot order per fragment j: S r0, PV r0, S r1, PV r1.
+        // read.  Slot order per fragment j: S r0, S r1, PV r0, PV r1.
         constexpr int NSL = (DS ? 16 : 0) + (DP ? 16 : 0);
         // element e is exponentiated in slot (e * SPAN) / 32 and folded LAG
         // slots later; the slot after the last fold computes the check's
@@ -320,8 +320,8 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
             }
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
-                const bool isS = (q4 & 1) == 0;
-                const int r = q4 >> 1;
+                const bool isS = q4 < 2;
+                const int r = q4 & 1;
                 if (isS && !DS) continue;
                 if (!isS && !DP) continue;
                 __builtin_amdgcn_sched_barrier(0);
@@ -337,7 +337,7 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 }
                 // reads: first slot of the group reads fragment j+2 (or the
                 // next stage's first fragments in groups 6 and 7)
-                if (q4 == (DS ? 0 : 1)) {
+                if (q4 == (DS ? 0 : 2)) {   // the group's first slot
                     if (j + 2 < 8) read(j + 2);
                     else if ((F & fBar) == 0 || j == 7) {
                         if constexpr ((F & fBar) != 0) {
