@@ -85,12 +85,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "{kernel}_{workload}_traffic.json"
 
 def fwd_kernel_name(cfg) -> str:
     """The forward kernel the library launches for a workload (its dispatch
-    rule: bf16 dense d = 128 launches of at least 1024 256-row query tiles
-    with N a multiple of 64 use the 64-row kernel unless ATTN_W64=0)."""
+    rule: bf16 dense and causal d = 128 launches of at least 1024 256-row
+    query tiles with N a multiple of 64 use the 64-row kernel unless
+    ATTN_W64=0)."""
     if cfg.dtype != "bf16":
         return "fwd_f32_kernel"
     large = (cfg.N + 255) // 256 * cfg.B * cfg.H >= 1024 or os.environ.get("ATTN_TILE") == "256"
-    if (not cfg.causal and not cfg.sparse and cfg.d == 128 and cfg.N >= 128 and cfg.N % 64 == 0 and large
+    if (not cfg.sparse and cfg.d == 128 and cfg.N >= 128 and cfg.N % 64 == 0 and large
             and os.environ.get("ATTN_TILE") != "128" and os.environ.get("ATTN_W64") != "0"):
         return "fwd_w64_kernel"
     return "fwd_bf16_kernel"

@@ -636,10 +636,10 @@ int tile_rows_override() {
     return rows;
 }
 
-// The dense d = 128 forward with 64 query rows per wave (fwd_bf16_w64.hip)
-// takes V in place and whole 64-key tiles (N a multiple of 64, at least two
-// tiles); ATTN_W64=0 in the environment (read once per process) keeps the
-// 32-row kernel instead.
+// The d = 128 forward with 64 query rows per wave (fwd_bf16_w64.hip, dense or
+// causal, large grids) takes V in place and whole 64-key tiles (N a multiple
+// of 64, at least two tiles); ATTN_W64=0 in the environment (read once per
+// process) keeps the 32-row kernel instead.
 bool w64_eligible(const FwdArgs& a) {
     static const bool off = [] {
         const char* e = std::getenv("ATTN_W64");
@@ -661,16 +661,19 @@ hipError_t launch_d(const FwdArgs& a, Mode mode, hipStream_t stream) {
     // Fewer than 4 rounds of 256-row workgroups over the 256 CUs: 128-row
     // workgroups (two per CU, 2 tiles in flight) fill the chip better (B=4
     // H=16 N=2048 causal: 343 -> 410 TFLOP/s); larger grids keep 256 rows,
-    // which halves the K/V tile traffic per query.  Large dense d = 128 grids
-    // of whole 64-key tiles use the 64-row kernel (w64_eligible).
+    // which halves the K/V tile traffic per query.  Large dense and causal
+    // d = 128 grids of whole 64-key tiles use the 64-row kernel (w64_eligible);
+    // at d = 64 its one-wave softmax made the causal B=4 H=16 N=2048 launch
+    // slower (52.3 against 50.7 us).
     const int forced = tile_rows_override();
     const bool small_grid = forced ? forced == 128 : (int64_t)((a.N + 255) / 256) * a.BH < 1024;
     switch (mode) {
         case Mode::kDense:
             if (small_grid) return launch_v<D, 4, 2, (int)Mode::kDense>(a, stream);
-            if (D == 128 && w64_eligible(a)) return launch_fwd_w64(a, stream);
+            if (D == 128 && w64_eligible(a)) return launch_fwd_w64(a, false, stream);
             return launch_v<D, 8, 2, (int)Mode::kDense>(a, stream);
         case Mode::kCausal:
+            if (D == 128 && !small_grid && w64_eligible(a)) return launch_fwd_w64(a, true, stream);
             if (small_grid) {
                 FwdArgs f = a;
                 f.fold_slots = fold_slots<D, 4>(a);

@@ -1,6 +1,6 @@
-// Fused attention forward, bf16, d = 128, dense: one wave per SIMD holding 64
-// query rows, with the softmax of one 32-key sub-tile overlapped with the matrix
-// products of its neighbours.
+// Fused attention forward, bf16, d = 128, dense or causal: one wave per SIMD
+// holding 64 query rows, with the softmax of one 32-key sub-tile overlapped with
+// the matrix products of its neighbours.
 //
 // The method is the one of fwd_bf16.hip ("Exact Blocks, Rings, and Sparsity",
 // section 2, "What the forward kernel keeps on chip"; FlashAttention notes,
@@ -52,13 +52,10 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kD = 128;
 constexpr int kNW = 4;                       // waves per workgroup
 constexpr int kRows = 64;                    // query rows per wave
 constexpr int kBM = kNW * kRows;             // query rows per workgroup
 constexpr int kBN = 64;                      // keys per tile
-constexpr int kTileBytes = kBN * kD * 2;     // one K or V tile
-constexpr int kPerW = kTileBytes / 1024 / kNW;   // 1 KiB direct-to-LDS loads per wave per tile
 constexpr float kSumMax = 0x1p64f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -78,7 +75,13 @@ static __device__ __forceinline__ void settle_acc(f32x16 (&o)[2][4]) {
                    "+a"(o[1][2]), "+a"(o[1][3]));
 }
 
+template <bool CAUSAL>
 __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_w64_kernel(FwdArgs a) {
+    constexpr int kD = 128;
+    constexpr int kTileBytes = kBN * kD * 2;         // one K or V tile
+    constexpr int kPerW = kTileBytes / 1024 / kNW;   // 1 KiB direct-to-LDS loads per wave per tile
+    constexpr int NF = kD / 16;                      // K chunks (and V^T fragments) per 32-key half
+    constexpr int NDB = kD / 32;                     // 32-dimension blocks of O
     // two K tiles, then two V tiles
     __shared__ __attribute__((aligned(1024))) unsigned char sK[2 * kTileBytes], sV[2 * kTileBytes];
     const unsigned kl = lds_addr(sK), vl = lds_addr(sV);
@@ -88,15 +91,23 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const int l32 = lane & 31, hi = lane >> 5;
     const TrLane<kD> trl = tr_lane<kD>(lane);
     // K fragment of chunk c (dims 16c..16c+15), row l32 of a 32-key half
-    int koff[kD / 16];
+    int koff[NF];
 #pragma unroll
-    for (int c = 0; c < kD / 16; ++c) koff[c] = l32 * (2 * kD) + rt_swz<kD>(l32, 2 * c + hi) * 16;
+    for (int c = 0; c < NF; ++c) koff[c] = l32 * (2 * kD) + rt_swz<kD>(l32, 2 * c + hi) * 16;
 
     const int N = a.N;
     const int nqt = (N + kBM - 1) / kBM;
-    const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nqt * a.BH);
-    const int64_t bh = ord / nqt;
-    const int q0 = (int)(ord % nqt) * kBM + kRows * w;   // this wave's first row
+    int64_t bh;
+    int qt;
+    if constexpr (CAUSAL) {   // the costliest query tiles of the XCD's heads first
+        rank_major_order(blockIdx.x, (int64_t)nqt * a.BH, nqt, bh, qt);
+        qt = nqt - 1 - qt;
+    } else {
+        const int64_t ord = xcd_tile_order(blockIdx.x, (int64_t)nqt * a.BH);
+        bh = ord / nqt;
+        qt = (int)(ord % nqt);
+    }
+    const int q0 = qt * kBM + kRows * w;   // this wave's first row
 
     const int64_t kvh = kv_head_of(bh, a.H, a.Hkv);
     const __bf16* Qh = static_cast<const __bf16*>(a.q) + bh * (int64_t)N * kD;
@@ -104,12 +115,12 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     const __bf16* Vh = static_cast<const __bf16*>(a.v) + kvh * (int64_t)N * kD;
 
     // Q fragments (B operand of S^T = K Q^T) of rows q0 + 32r + l32
-    bf16x8 qf[2][kD / 16];
+    bf16x8 qf[2][NF];
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int qrow = min(q0 + 32 * r + l32, N - 1);
 #pragma unroll
-        for (int c = 0; c < kD / 16; ++c)
+        for (int c = 0; c < NF; ++c)
             qf[r][c] = *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qrow * kD + 16 * c + 8 * hi);
     }
 
@@ -133,16 +144,17 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         for (int i = 0; i < kPerW; ++i) issue_one(base, kb0, lds, i);
     };
 
-    f32x16 oacc[2][kD / 32];
+    f32x16 oacc[2][NDB];
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
-        for (int i = 0; i < kD / 32; ++i) oacc[r][i] = f32x16{};
+        for (int i = 0; i < NDB; ++i) oacc[r][i] = f32x16{};
     settle_acc(oacc);
     float m_run[2] = {-__builtin_inff(), -__builtin_inff()};
     float ell[2] = {0.f, 0.f};
     const float sl2 = a.scale_log2;
-    const int T = (N + kBN - 1) / kBN;   // tiles; sub-tiles 0 .. 2T-1
+    // tiles; sub-tiles 0 .. 2T-1 (causal: keys up to the workgroup's last row)
+    const int T = CAUSAL ? min(N, qt * kBM + kBM) / kBN : N / kBN;
 
     // exponentials of s against m_run into p; per-row-block lane sums
     auto exps = [&](const f32x16 (&s)[2], bf16x8 (&p)[2][2], float (&tsum)[2], int r, float mu) __attribute__((always_inline)) {
@@ -156,6 +168,16 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 p[r][g][i] = (__bf16)e;
             }
         tsum[r] = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+    };
+    // causal: key j of the sub-tile starting at kb is masked for row i when
+    // j > i; s[r][v] holds key kb + 8(v>>2) + 4hi + (v&3) of row q0 + 32r + l32
+    auto mask = [&](f32x16 (&s)[2], int kb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int rlim = q0 + 32 * r + l32 - kb - 4 * hi;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) s[r][v] = 8 * (v >> 2) + (v & 3) > rlim ? -__builtin_inff() : s[r][v];
+        }
     };
     // the check after the exponentials of a sub-tile (see the file comment)
     auto settle = [&](const f32x16 (&s)[2], bf16x8 (&p)[2][2], float (&tsum)[2], bool bad) __attribute__((always_inline)) {
@@ -174,7 +196,7 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
                     ell[r] *= alpha;
                     settle_acc(oacc);
 #pragma unroll
-                    for (int i = 0; i < kD / 32; ++i) oacc[r][i] *= alpha;
+                    for (int i = 0; i < NDB; ++i) oacc[r][i] *= alpha;
                     settle_acc(oacc);
                 }
                 exps(s, p, tsum, r, m_run[r] == -__builtin_inff() ? 0.f : m_run[r]);
@@ -216,17 +238,22 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     auto stage = [&](auto flags, f32x16 (&sin)[2], bf16x8 (&pout)[2][2], f32x16 (&sout)[2],
                      const unsigned char* bK, const bf16x8 (&pin)[2][2], const unsigned char* bV, int vhalf,
                      const unsigned char* bKn, const unsigned char* bVn, int vhalf_n, int k_load, unsigned k_lds,
-                     int v_load, unsigned v_lds) __attribute__((always_inline)) {
+                     int v_load, unsigned v_lds, int kb_in) __attribute__((always_inline)) {
         constexpr int F = decltype(flags)::value;
         constexpr bool DS = F & fS, DP = F & fP, SM = F & fSM;
-        bf16x8 kf[8], vf[8];
+        // causal: the element mask on a sub-tile that reaches past this wave's
+        // first row (sub-tiles wholly past its rows are computed and masked)
+        if constexpr (CAUSAL && SM) {
+            if (kb_in + 31 > q0) mask(sin, kb_in);
+        }
+        bf16x8 kf[NF], vf[NF];
         auto read = [&](int j) __attribute__((always_inline)) {
             if constexpr (DS) kf[j] = *reinterpret_cast<const bf16x8*>(bK + koff[j]);
-            if constexpr (DP) vf[j] = tr_operand<kD>(bV, trl, 2 * vhalf + j / 4, j % 4);
+            if constexpr (DP) vf[j] = tr_operand<kD>(bV, trl, 2 * vhalf + j / NDB, j % NDB);
         };
         auto read_next = [&](int j) __attribute__((always_inline)) {
             if constexpr ((F & fNK) != 0) kN[j] = *reinterpret_cast<const bf16x8*>(bKn + koff[j]);
-            if constexpr ((F & fNV) != 0) vN[j] = tr_operand<kD>(bVn, trl, 2 * vhalf_n + j / 4, j % 4);
+            if constexpr ((F & fNV) != 0) vN[j] = tr_operand<kD>(bVn, trl, 2 * vhalf_n + j / NDB, j % NDB);
         };
         // softmax element e: row block e / 16, register e % 16
         float ex[32], ts[2][4];
@@ -282,11 +309,11 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         // MFMA, one exponential (two in 16-slot stages), the sum and packing of
         // an element exponentiated LAG slots earlier, and at most one fragment
         // read.  Slot order per fragment j: S r0, S r1, PV r0, PV r1.
-        constexpr int NSL = (DS ? 16 : 0) + (DP ? 16 : 0);
+        constexpr int NSL = (DS ? 2 * NF : 0) + (DP ? 2 * NF : 0);
         // element e is exponentiated in slot (e * SPAN) / 32 and folded LAG
         // slots later; the slot after the last fold computes the check's
         // inputs, so that only the ballot and the branch follow the last MFMA
-        constexpr int SPAN = NSL * 3 / 4, LAG = NSL == 32 ? 4 : 2;
+        constexpr int SPAN = NSL * 3 / 4, LAG = NSL / 8;
         float tsum[2];
         bool bad = false;
         int slot = 0;
@@ -306,11 +333,11 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
             }
         };
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NF; ++j) {
             // fragment reads issued in the slots of group j: fragment j + 2,
-            // then (groups 6 and 7) the next stage's fragments 0 and 1
+            // then (the last two groups) the next stage's fragments 0 and 1
             if constexpr ((F & fBar) != 0) {
-                if (j == 7) {
+                if (j == NF - 1) {
                     __builtin_amdgcn_sched_barrier(0);
                     // this wave's reads of the retiring tiles have returned;
                     // every wave's loads of the next tiles have landed
@@ -326,7 +353,7 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 if (!isS && !DP) continue;
                 __builtin_amdgcn_sched_barrier(0);
                 if (isS) sout[r] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[r][j], sout[r], 0, 0, 0);
-                else mfma_acc(oacc[r][j % 4], vf[j], pin[r][j / 4]);
+                else mfma_acc(oacc[r][j % NDB], vf[j], pin[r][j / NDB]);
                 work(slot);
                 // tile loads (into buffers freed by the last barrier), one per slot
                 if constexpr ((F & fLoad) != 0) {   // every fourth slot
@@ -338,13 +365,13 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
                 // reads: first slot of the group reads fragment j+2 (or the
                 // next stage's first fragments in groups 6 and 7)
                 if (q4 == (DS ? 0 : 2)) {   // the group's first slot
-                    if (j + 2 < 8) read(j + 2);
-                    else if ((F & fBar) == 0 || j == 7) {
+                    if (j + 2 < NF) read(j + 2);
+                    else if ((F & fBar) == 0 || j == NF - 1) {
                         if constexpr ((F & fBar) != 0) {
                             read_next(0);
                             read_next(1);
                         } else {
-                            read_next(j - 6);
+                            read_next(j - (NF - 2));
                         }
                     }
                 }
@@ -372,9 +399,10 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     issue(Kh, kBN, kl + kTileBytes);
     wait_vmcnt<2 * kPerW>();
     barrier();
-    stage(std::integral_constant<int, fS | fCold | fNK>{}, sO, pO, sE, sK, pE, sV, 0, sK + kHalf, sV, 0, 0, 0, 0, 0);
+    stage(std::integral_constant<int, fS | fCold | fNK>{}, sO, pO, sE, sK, pE, sV, 0, sK + kHalf, sV, 0, 0, 0, 0, 0,
+          0);
     stage(std::integral_constant<int, fS | fSM | fFirst | fBar | fNK | fNV>{}, sE, pE, sO, sK + kHalf, pO, sV, 0, sK1,
-          sV, 0, 0, 0, 0, 0);
+          sV, 0, 0, 0, 0, 0, 0);
 
     // Tile t+1 for t <= T-3: stage 2t+1 (S(2t+2) <- K(t+1) half 0, PV(2t) <-
     // V(t) half 0, SM(2t+1); loads of K(t+2) and V(t+1) into the buffers of
@@ -388,9 +416,9 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const unsigned char* const bKn = P ? sK1 : sK;   // K(t+2)
         const unsigned char* const bVn = P ? sV : sV1;   // V(t+1)
         stage(std::integral_constant<int, fS | fP | fSM | fLoad | fNK | fNV>{}, sO, pO, sE, bK, pE, bV, 0, bK + kHalf,
-              bV, 1, (t + 2) * kBN, kl + P * kTileBytes, (t + 1) * kBN, vl + (1 - P) * kTileBytes);
+              bV, 1, (t + 2) * kBN, kl + P * kTileBytes, (t + 1) * kBN, vl + (1 - P) * kTileBytes, t * kBN + 32);
         stage(std::integral_constant<int, fS | fP | fSM | fBar | fNK | fNV>{}, sE, pE, sO, bK + kHalf, pO, bV, 1, bKn,
-              bVn, 0, 0, 0, 0, 0);
+              bVn, 0, 0, 0, 0, 0, (t + 1) * kBN);
     };
     int t = 0;
     for (; t + 3 < T; t += 2) {   // t, t+1 <= T-3
@@ -404,14 +432,15 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const unsigned char* bV = (tl & 1) ? sV1 : sV;
         const unsigned char* bVn = (tl & 1) ? sV : sV1;
         stage(std::integral_constant<int, fS | fP | fSM | fLoadV | fNK | fNV>{}, sO, pO, sE, bK, pE, bV, 0,
-              bK + kHalf, bV, 1, 0, 0, (tl + 1) * kBN, vl + ((tl + 1) & 1) * kTileBytes);
+              bK + kHalf, bV, 1, 0, 0, (tl + 1) * kBN, vl + ((tl + 1) & 1) * kTileBytes, tl * kBN + 32);
         stage(std::integral_constant<int, fS | fP | fSM | fBar | fNV>{}, sE, pE, sO, bK + kHalf, pO, bV, 1, nullptr,
-              bVn, 0, 0, 0, 0, 0);
+              bVn, 0, 0, 0, 0, 0, (tl + 1) * kBN);
         // stage 2T-1: PV(2T-2) <- V(T-1) half 0, SM(2T-1)
         stage(std::integral_constant<int, fP | fSM | fNV>{}, sO, pO, sE, nullptr, pE, bVn, 0, nullptr, bVn, 1, 0, 0,
-              0, 0);
+              0, 0, (tl + 1) * kBN + 32);
         // PV(2T-1) <- V(T-1) half 1
-        stage(std::integral_constant<int, fP>{}, sE, pE, sO, nullptr, pO, bVn, 1, nullptr, nullptr, 0, 0, 0, 0, 0);
+        stage(std::integral_constant<int, fP>{}, sE, pE, sO, nullptr, pO, bVn, 1, nullptr, nullptr, 0, 0, 0, 0, 0,
+              0);
     }
 
     // ---- epilogue: O = A / l, LSE = (m + log2 l) ln 2 ----
@@ -423,19 +452,21 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's last fragment reads have returned
     barrier();                            // ... and every other wave's
     unsigned char* const stg = (w < 2 ? sK : sV) + (w & 1) * (kRows * kD * 2);
+    constexpr int CPR = kD / 8;     // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;   // rows per 1 KiB read
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int row = 32 * r + l32;   // of the wave's 64
         const float l_tot = xor32_sum(ell[r]);
         const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
-        for (int db = 0; db < kD / 32; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 bf16x4 ov;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ov[i] = (__bf16)(oacc[r][db][4 * j + i] * inv);
-                const int chunk = (4 * db + j) ^ (row & 15);   // dims 32 db + 8 j .. + 7
+                const int chunk = (4 * db + j) ^ (row & (CPR - 1));   // dims 32 db + 8 j .. + 7
                 *reinterpret_cast<bf16x4*>(stg + row * (2 * kD) + chunk * 16 + 8 * hi) = ov;
             }
         const int qi = q0 + row;
@@ -444,18 +475,19 @@ __global__ __launch_bounds__(64 * kNW, 1) __attribute__((amdgpu_waves_per_eu(1, 
     }
     __bf16* const Oh = static_cast<__bf16*>(a.o) + bh * (int64_t)N * kD;
 #pragma unroll
-    for (int s4 = 0; s4 < kRows / 4; ++s4) {
-        const int row = 4 * s4 + (lane >> 4), c = lane & 15;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * (2 * kD) + (c ^ (row & 15)) * 16);
+    for (int s4 = 0; s4 < kRows / RPI; ++s4) {
+        const int row = RPI * s4 + lane / CPR, c = lane % CPR;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(stg + row * (2 * kD) + (c ^ (row & (CPR - 1))) * 16);
         if (q0 + row < N) *reinterpret_cast<u32x4*>(Oh + (int64_t)(q0 + row) * kD + 8 * c) = val;
     }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_w64(const FwdArgs& a, hipStream_t stream) {
-    const int64_t grid = (int64_t)((a.N + kBM - 1) / kBM) * a.BH;
-    hipLaunchKernelGGL(fwd_w64_kernel, dim3((unsigned)grid), dim3(64 * kNW), 0, stream, a);
+hipError_t launch_fwd_w64(const FwdArgs& a, bool causal, hipStream_t stream) {
+    const dim3 grid((unsigned)((int64_t)((a.N + kBM - 1) / kBM) * a.BH)), block(64 * kNW);
+    if (causal) hipLaunchKernelGGL(fwd_w64_kernel<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(fwd_w64_kernel<false>, grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

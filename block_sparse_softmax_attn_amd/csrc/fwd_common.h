@@ -151,8 +151,9 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, Mode mode, hipStream_t stream);
 // Launchers: return hipSuccess or the launch error.
 hipError_t launch_fwd_bf16(const FwdArgs& a, Mode mode, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, Mode mode, hipStream_t stream);
-// Dense d = 128 forward with 64 query rows per wave (V read in place).
-hipError_t launch_fwd_w64(const FwdArgs& a, hipStream_t stream);
+// Forward with 64 query rows per wave (d = 128, V read in place, N a multiple
+// of 64 and at least 128): dense or causal.
+hipError_t launch_fwd_w64(const FwdArgs& a, bool causal, hipStream_t stream);
 // Fill a.vt from a.v (bf16 path): V^T with the key order the forward kernel reads.
 hipError_t launch_v_transpose(const FwdArgs& a, hipStream_t stream);
 // Keys per head of the V^T workspace: N rounded up to 128.

@@ -1,10 +1,13 @@
-"""GPU parity of the dense d = 128 forward with 64 query rows per wave (the
-kernel the library launches for large bf16 dense grids of whole 64-key tiles),
+"""GPU parity of the d = 128 forward with 64 query rows per wave (the kernel the
+library launches for large bf16 dense and causal grids of whole 64-key tiles),
 through the C ABI, against the float64 oracle on every row.
 
 The kernel is chosen for grids of at least 1024 256-row query tiles; these
 shapes are smaller, so each case runs in a child process with ATTN_TILE=256
 (read once per process), which makes the dispatcher treat every grid as large.
+Causal cases cover the element mask on the sub-tiles that cross a wave's rows,
+sub-tiles wholly past them (computed and masked), and workgroups whose key
+range ends at their own last row.
 Tile counts 2 to 5 cover the pipeline's prologue, its two-tile loop body, the
 single leftover tile and the last two tiles; 16 and 17 tiles cover many trips
 of the loop with an even and an odd count; GQA shares K/V heads; growing
@@ -30,9 +33,11 @@ pytestmark = pytest.mark.gpu
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-# (B, H, Hkv, N, seed): N a multiple of 64 (2 to 17 tiles of 64 keys)
-CASES = [(1, 2, 2, 128, 1), (1, 2, 2, 192, 2), (1, 3, 3, 256, 3), (2, 2, 2, 320, 4), (1, 2, 2, 1024, 5),
-         (1, 1, 1, 1088, 6), (1, 4, 2, 512, 7)]
+# (B, H, Hkv, N, causal, seed): N a multiple of 64 (2 to 17 tiles of 64 keys)
+CASES = [(1, 2, 2, 128, False, 1), (1, 2, 2, 192, False, 2), (1, 3, 3, 256, False, 3), (2, 2, 2, 320, False, 4),
+         (1, 2, 2, 1024, False, 5), (1, 1, 1, 1088, False, 6), (1, 4, 2, 512, False, 7),
+         (1, 2, 2, 128, True, 11), (1, 2, 2, 320, True, 12), (2, 2, 2, 576, True, 13), (1, 4, 2, 1088, True, 14),
+         (1, 3, 3, 704, True, 15)]
 
 CHILD = r"""
 import sys, numpy as np, torch
@@ -40,15 +45,15 @@ sys.path.insert(0, {root!r})
 import block_sparse_softmax_attn_amd as m
 import workloads
 out = {{}}
-for (B, H, Hkv, N, seed) in {cases!r}:
+for (B, H, Hkv, N, causal, seed) in {cases!r}:
     g = torch.Generator().manual_seed(1000 + seed)
     q = torch.randn((B, H, N, 128), generator=g).to(torch.bfloat16)
     k = torch.randn((B, Hkv, N, 128), generator=g).to(torch.bfloat16)
     v = torch.randn((B, Hkv, N, 128), generator=g).to(torch.bfloat16)
-    print("case", B, H, Hkv, N, flush=True)
-    o, lse = m.attn_fwd(q.cuda(), k.cuda(), v.cuda())
+    print("case", B, H, Hkv, N, causal, flush=True)
+    o, lse = m.attn_fwd(q.cuda(), k.cuda(), v.cuda(), causal=causal)
     torch.cuda.synchronize()
-    key = f"{{B}}_{{H}}_{{Hkv}}_{{N}}"
+    key = f"{{B}}_{{H}}_{{Hkv}}_{{N}}_{{int(causal)}}"
     out["o_" + key] = o.float().cpu().numpy()
     out["lse_" + key] = lse.cpu().numpy()
 # growing logits: key j = (j + 1) k0, so most sub-tiles raise the row's reference value
@@ -91,20 +96,21 @@ def outputs(tmp_path_factory):
     return _run(tmp, None), _run(tmp, "0")
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}Hkv{c[2]}N{c[3]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}Hkv{c[2]}N{c[3]}{'causal' if c[4] else 'dense'}"
+                                              for c in CASES])
 def test_w64_matches_oracle(outputs, case):
     got, _ = outputs
-    B, H, Hkv, N, seed = case
+    B, H, Hkv, N, causal, seed = case
     g = torch.Generator().manual_seed(1000 + seed)
     q = torch.randn((B, H, N, 128), generator=g).to(torch.bfloat16)
     k = torch.randn((B, Hkv, N, 128), generator=g).to(torch.bfloat16)
     v = torch.randn((B, Hkv, N, 128), generator=g).to(torch.bfloat16)
     scale = 1.0 / math.sqrt(128)
     if Hkv == H:
-        o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, False)
+        o_ref, lse_ref = oracle.attn_fwd(q, k, v, scale, causal)
     else:
-        o_ref, lse_ref = oracle.attn_fwd_gqa(q, k, v, scale, False)
-    key = f"{B}_{H}_{Hkv}_{N}"
+        o_ref, lse_ref = oracle.attn_fwd_gqa(q, k, v, scale, causal)
+    key = f"{B}_{H}_{Hkv}_{N}_{int(causal)}"
     do, dl = compare(got["o_" + key].astype(np.float64), got["lse_" + key].astype(np.float64), o_ref, lse_ref,
                      "bf16", f"w64 {key}")
     print(f"w64 {key}: max|dO| {do:.3e} max|dLSE| {dl:.3e}", flush=True)
