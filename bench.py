@@ -69,6 +69,11 @@ PEAK_F32_MFMA_TFLOPS = 157.3  # MI355X fp32 matrix peak, dense
 # the fp32 denominator and half a bf16 pack: 4.5 wave64 instructions of 4 cycles
 # per 64 scores on a 16-lane SIMD.
 VALU_CYCLES_PER_SCORE = 4.5 * 4 / 64
+# Issue cycles a 32x32x16 bf16 MFMA takes from its wave's instruction stream
+# (a register-only probe, one wave per SIMD: 16 MFMAs take 512 cycles alone, 576
+# with 96 FMAs between them, 688 with 128, 940 with 192).  A 32 x 32 score block
+# needs d / 8 of them (d / 16 for the scores, d / 16 for its share of P V).
+MFMA_ISSUE_CYCLES = 11
 # Timed steps whose launch is bracketed by a HIP event pair (the first and then
 # every EVENT_STRIDE-th): enough samples for the kernel's mean duration, few
 # enough event records that they hardly add to the steps' wall clock.
@@ -291,14 +296,23 @@ def device_info(dev):
     return info
 
 
-def vector_floor(executed_scores: int, mean_launch_ms: float) -> dict:
+def vector_floor(executed_scores: int, mean_launch_ms: float, d: int = 0) -> dict:
     """Time floors of a launch at 2.4 GHz on all 1024 SIMDs: the softmax's
-    vector work (VALU_CYCLES_PER_SCORE per executed score) and the matrix work
-    (4 d flops per score at the bf16 peak are given by the caller's roofline);
-    the launch's time against the vector floor."""
-    floor_ms = executed_scores * VALU_CYCLES_PER_SCORE / (SIMDS * CLOCK_GHZ * 1e9) * 1e3
-    return {"cycles_per_score": VALU_CYCLES_PER_SCORE, "floor_ms": round(floor_ms, 5),
-            "frac": round(floor_ms / mean_launch_ms, 4)}
+    vector work (VALU_CYCLES_PER_SCORE per executed score), and with the head
+    dimension d the issue floor of one wave's instruction stream (that vector
+    work plus MFMA_ISSUE_CYCLES for each of the d / 8 MFMAs of a 32 x 32 score
+    block); the launch's time against each.  The matrix work's floor (4 d flops
+    per score at the bf16 peak) is added by the caller."""
+    unit = SIMDS * CLOCK_GHZ * 1e9
+    floor_ms = executed_scores * VALU_CYCLES_PER_SCORE / unit * 1e3
+    rec = {"cycles_per_score": VALU_CYCLES_PER_SCORE, "floor_ms": round(floor_ms, 5),
+           "frac": round(floor_ms / mean_launch_ms, 4)}
+    if d:
+        issue = VALU_CYCLES_PER_SCORE + MFMA_ISSUE_CYCLES * (d / 8) / 1024
+        issue_ms = executed_scores * issue / unit * 1e3
+        rec.update({"issue_cycles_per_score": round(issue, 5), "issue_floor_ms": round(issue_ms, 5),
+                    "issue_frac": round(issue_ms / mean_launch_ms, 4)})
+    return rec
 
 
 def executed_tiles_128(cfg, mask=None) -> int:
@@ -419,9 +433,10 @@ def bench_fwd(args, cfg, dev, gemm=None):
         # (whole tiles for causal and block-sparse runs); at d = 64 it exceeds
         # the matrix work's time at peak
         scores = executed if executed is not None else pairs
-        vf = vector_floor(scores, mean_launch_ms)
+        vf = vector_floor(scores, mean_launch_ms, cfg.d)
         vf["mfma_floor_ms"] = round(4 * cfg.d * scores / (PEAK_BF16_TFLOPS * 1e12) * 1e3, 5)
         vf["binding"] = "valu" if vf["floor_ms"] > vf["mfma_floor_ms"] else "mfma"
+        vf["binding_with_issue"] = "issue" if vf["issue_floor_ms"] > vf["mfma_floor_ms"] else "mfma"
         rec["roofline"]["vector_floor"] = vf
     if cfg.dtype != "bf16":
         rec["roofline"]["note"] = ("fp32 workload of 16.8 MFLOP: one small launch, latency-bound; "

@@ -178,3 +178,17 @@ def test_vector_floor_closed_form():
     vf = bench.vector_floor(scores, 2.0)
     assert abs(vf["floor_ms"] - 1.0) < 1e-4 and abs(vf["frac"] - 0.5) < 1e-4
     assert bench.VALU_CYCLES_PER_SCORE == 4.5 * 4 / 64
+    assert "issue_floor_ms" not in vf
+
+
+def test_issue_floor_closed_form():
+    # d = 64: 16 MFMAs per 32 x 64 tile of scores, 11 issue cycles each, on top of
+    # the vector work; d = 128 twice the MFMAs
+    for d, mfma_per_2048 in ((64, 16), (128, 32)):
+        per_score = bench.VALU_CYCLES_PER_SCORE + mfma_per_2048 * bench.MFMA_ISSUE_CYCLES / 2048
+        scores = round(1024 * 2.4e9 * 1e-3 / per_score)
+        vf = bench.vector_floor(scores, 4.0, d)
+        assert abs(vf["issue_cycles_per_score"] - per_score) < 1e-5
+        assert abs(vf["issue_floor_ms"] - 1.0) < 1e-4 and abs(vf["issue_frac"] - 0.25) < 1e-4
+    # the issue floor binds above the matrix work at d = 64, not at d = 128
+    assert 0.28125 + 16 * 11 / 2048 > 64 / 256 and 0.28125 + 32 * 11 / 2048 < 128 / 256
