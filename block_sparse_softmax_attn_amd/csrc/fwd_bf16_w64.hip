@@ -9,15 +9,19 @@
 // Only the schedule differs.
 //
 // Why this shape on gfx950.  Ordinary vector instructions issued between
-// independent MFMAs of the same wave execute in the MFMA's shadow (a register-
-// only measurement: 16 32x32x16 MFMAs take 512 cycles alone and 520 with 64
-// FMAs interleaved); the softmax of a tile, though, depends on that tile's
+// independent MFMAs of the same wave execute in the MFMA's shadow, up to about
+// four FMAs per MFMA (a register-only measurement: 16 32x32x16 MFMAs take 512
+// cycles alone, 520 with 64 FMAs interleaved, 688 with 128: each MFMA holds
+// the wave's issue for ~11 of its 32 cycles, and an exponential there costs
+// ~12 cycles of issue).  The softmax of a tile, though, depends on that tile's
 // score products and feeds its PV products, so in the one-tile-at-a-time loop
 // it runs between them and the matrix core idles.  Here a wave splits each
 // 64-key tile into two 32-key sub-tiles k and runs a three-stage pipeline: in
 // stage k it issues the score MFMAs of sub-tile k+1 and the PV MFMAs of
 // sub-tile k-1, and between them the exponentials of sub-tile k.  The two
-// products and the vector work of a stage are independent of each other.
+// products and the vector work of a stage are independent of each other; a
+// stage (32 MFMAs, 32 exponentials, ~90 other vector instructions, 24 LDS
+// reads) needs about as many issue cycles as its matrix work takes.
 //
 // Each wave holds 64 query rows (two 32-row blocks r) instead of 32, so every
 // K or V fragment read from LDS feeds two MFMAs: half the LDS reads per flop.
